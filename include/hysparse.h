@@ -1,0 +1,183 @@
+/*
+ * hysparse.h - C ABI of the HySparse hybrid-block attention library for one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (pages: the HySparse abstract; the intelliparadigm HySparse
+ * article sections 2.1, 2.2 and 3.1; the Baidu article "Sparse Evolution of
+ * Hybrid Attention Architectures", section "Fine-Grained Sparse Attention:
+ * Indexer + Top-K"):
+ *
+ *   full layer    O[b,i,h]   = sum_j softmax_j(tau * q.k_j, j <= pos(i)) v_j
+ *                 S[b,g,n,j] = sum over heads h of KV group g and queries i of
+ *                              score block n of P[b,h,i,j]   (importance score)
+ *   top-K         idx[b,g,n] = the K largest S[b,g,n,j] over j <= last(n)
+ *   sparse layer  out = sigmoid(w_h) * o_global + (1 - sigmoid(w_h)) * o_local
+ *                 o_global: softmax attention over {j in idx[b,g,n] : j <= pos(i)}
+ *                 o_local:  softmax attention over the W keys [pos(i)-W+1, pos(i)]
+ *                 both on the full layer's K and V (the cache is shared, read only)
+ *
+ * Conventions shared by every entry point
+ *   - pos(i) = kv_len - q_len + i; tau = 1/sqrt(head_dim) unless desc.scale > 0;
+ *     query head h uses KV head h / (n_q_heads / n_kv_heads).
+ *   - Score blocks: n = i / score_block, NB = ceil(q_len / score_block),
+ *     last(n) = pos(min((n+1)*score_block, q_len) - 1).  score_block is 1 or 64.
+ *   - Top-K order: the float32 bit pattern u is mapped to a key that is
+ *     u ^ 0xFFFFFFFF for negative values and u ^ 0x80000000 otherwise; larger
+ *     key first, lower index first among equal keys.  Index rows are sorted
+ *     ascending and padded with -1 when fewer than K candidates exist.
+ *   - Memory: every pointer argument except host arrays explicitly marked
+ *     "host" is device memory owned by the caller.  The library allocates
+ *     nothing and keeps no state between calls; all scratch comes from the
+ *     caller's workspace, sized by hysparse_workspace_bytes /
+ *     hysparse_topk_workspace_bytes.  A workspace must not be shared by calls
+ *     that may run concurrently.
+ *   - Layout: q, k, v are strided by desc (elements; the head_dim axis is
+ *     contiguous).  Outputs are dense: out [B, Tq, Hq, D] in desc.dtype,
+ *     lse [B, Hq, Tq] float32 (natural log), scores [B, Hkv, NB, Tkv] float32,
+ *     idx [B, Hkv, NB, K] int32.  Base pointers must be 16-byte aligned and
+ *     the batch/token/head strides multiples of 16 bytes.
+ *   - Errors: every argument is checked on the host before anything is
+ *     enqueued; on error nothing is launched and a status != 0 is returned
+ *     (hysparse_last_error() gives the detail).  After launching, a HIP launch
+ *     error maps to HYS_ERR_HIP.  Device-side faults surface at the caller's
+ *     next synchronisation.  Nothing throws across this interface.
+ *   - Asynchrony: all work is enqueued on `stream` (0 = the null stream); the
+ *     call returns without waiting.
+ *   - Supported shapes: head_dim 64 or 128; n_q_heads % n_kv_heads == 0 with
+ *     1 <= n_q_heads / n_kv_heads <= 16; 1 <= q_len <= kv_len; dtype bf16 or
+ *     float32.  NaN or Inf in q, k or v is outside the contract.
+ */
+#ifndef HYSPARSE_H
+#define HYSPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t hys_status;
+
+enum {
+  HYS_OK = 0,
+  HYS_ERR_NULL_PTR = 1,     /* a required pointer is NULL                     */
+  HYS_ERR_BAD_SHAPE = 2,    /* inconsistent or out-of-range sizes             */
+  HYS_ERR_UNSUPPORTED = 3,  /* valid but not implemented (head_dim, dtype ...) */
+  HYS_ERR_ALIGN = 4,        /* a pointer or stride is not 16-byte aligned     */
+  HYS_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required     */
+  HYS_ERR_HIP = 6           /* the HIP runtime reported an error              */
+};
+
+typedef enum { HYS_F32 = 0, HYS_BF16 = 1 } hys_dtype;
+
+/* Attention problem shared by the entry points.  Strides are in elements for
+ * the (batch, token, head) axes of q ([B, Tq, Hq, D]) and of k and v
+ * ([B, Tkv, Hkv, D]; k and v share strides). */
+typedef struct {
+  int32_t batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim;
+  int32_t dtype;          /* hys_dtype of q, k, v and of the attention outputs */
+  float scale;            /* softmax scale; <= 0 selects 1/sqrt(head_dim)      */
+  int64_t q_stride[3];
+  int64_t kv_stride[3];
+} hys_attn_desc;
+
+/* Operation ids for hysparse_workspace_bytes. */
+enum { HYS_OP_FULL = 0, HYS_OP_TOPK = 1, HYS_OP_SPARSE = 2, HYS_OP_HYBRID = 3 };
+
+/*
+ * Full-attention layer with importance-score emission (HySparse abstract: the
+ * full layer is the oracle that selects tokens; intelliparadigm article 3.1:
+ * its importance scores are reused by the following sparse layers).
+ *
+ *   q, k, v      inputs laid out by desc.
+ *   score_block  1 (one score row per query) or 64 (one per 64-query block).
+ *   out          [B, Tq, Hq, D] desc.dtype, written.
+ *   lse          [B, Hq, Tq] float32 log-sum-exp of the scaled logits, or NULL.
+ *   scores       [B, Hkv, NB, Tkv] float32, written in full (0 past last(n)).
+ *   ws/ws_bytes  workspace of at least hysparse_workspace_bytes(HYS_OP_FULL, ...).
+ */
+hys_status hysparse_full_attn_scores(const hys_attn_desc* desc, const void* q, const void* k,
+                                     const void* v, int32_t score_block, void* out, float* lse,
+                                     float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Top-K select over score rows (Baidu article, "Fine-Grained Sparse Attention:
+ * Indexer + Top-K": keep the K best positions per query; intelliparadigm
+ * article 2.2: TopK indices of the preceding full layer).
+ *
+ *   scores       float32 rows; row r starts at scores + r * row_stride.
+ *   n_rows       number of rows (>= 0); row_len = columns per row (>= 1).
+ *   row_stride   elements between rows, >= row_len, multiple of 4.
+ *   valid_len    int32 [n_rows] candidates per row (clamped to [0, row_len]),
+ *                or NULL for row_len everywhere.
+ *   k            K >= 1.
+ *   idx          int32 [n_rows, k], written: ascending indices, -1 padded.
+ *   ws/ws_bytes  at least hysparse_topk_workspace_bytes(n_rows, row_len, k).
+ * Results are bit-exact functions of the input bits (no atomics-order effects).
+ */
+hys_status hysparse_topk(const float* scores, int64_t n_rows, int32_t row_len, int64_t row_stride,
+                         const int32_t* valid_len, int32_t k, int32_t* idx, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Sparse layer (intelliparadigm article 2.2: global branch on the shared KV at
+ * the TopK indices, 128-token sliding-window branch, sigmoid-gated sum;
+ * Baidu article pseudocode: gather k_cache[idx], v_cache[idx], then softmax
+ * attention).  k and v are the full layer's cache and are only read.
+ *
+ *   q            this layer's queries, laid out by desc.
+ *   idx          int32 [B, Hkv, NB, k_top]; entries < 0 are skipped, entries
+ *                > pos(i) are masked per query, duplicates are not allowed.
+ *   window       W >= 1 keys ending at each query's own position.
+ *   gate_logits  float32 [Hq] (device); +-inf give gate 1 / 0 exactly.
+ *   out          [B, Tq, Hq, D] desc.dtype, written.
+ */
+hys_status hysparse_sparse_attn(const hys_attn_desc* desc, const void* q, const void* k,
+                                const void* v, const int32_t* idx, int32_t k_top,
+                                int32_t score_block, int32_t window, const float* gate_logits,
+                                void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * One hybrid block (intelliparadigm article 2.1 and 3.1): the full layer on
+ * q_full, top-K over its scores, then n_sparse sparse layers that reuse its
+ * k, v and indices, each with its own queries and gate logits.
+ *
+ *   q_sparse     host array of n_sparse device pointers, each laid out by desc.
+ *   gate_logits  float32 [n_sparse, Hq] (device).
+ *   out_full     [B, Tq, Hq, D]; out_sparse: host array of n_sparse device
+ *                pointers to [B, Tq, Hq, D] outputs.
+ *   lse, scores, idx  optional outputs (NULL: kept in the workspace only).
+ */
+hys_status hysparse_hybrid_block(const hys_attn_desc* desc, const void* q_full, const void* k,
+                                 const void* v, int32_t n_sparse, const void* const* q_sparse,
+                                 const float* gate_logits, int32_t k_top, int32_t score_block,
+                                 int32_t window, void* out_full, void* const* out_sparse,
+                                 float* lse, float* scores, int32_t* idx, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for op (HYS_OP_*) on desc; k_top and window are ignored
+ * where they do not apply.  For HYS_OP_HYBRID the figure covers scores and
+ * idx kept in the workspace (the NULL-output case) and any n_sparse.
+ * Returns 0 for invalid arguments. */
+size_t hysparse_workspace_bytes(int32_t op, const hys_attn_desc* desc, int32_t score_block,
+                                int32_t k_top, int32_t window);
+
+/* Workspace bytes for hysparse_topk. */
+size_t hysparse_topk_workspace_bytes(int64_t n_rows, int32_t row_len, int32_t k);
+
+/* Static description of a status code. */
+const char* hysparse_status_string(hys_status status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* hysparse_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t hysparse_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYSPARSE_H */

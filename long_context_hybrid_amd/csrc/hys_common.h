@@ -1,0 +1,127 @@
+// Device-side building blocks shared by the gfx950 kernels of libhysparse.
+//
+// Element traits pair a storage type with one 16x16 MFMA "k-step" of 32
+// products per output element:
+//   BF16: one v_mfma_f32_16x16x32_bf16 (8 bf16 per lane per operand)
+//   F32 : eight v_mfma_f32_16x16x4_f32 (8 floats per lane per operand; the
+//         lane's e-th element feeds the e-th instruction)
+// In both, lane l holds operand row/column (l % 16) and eight k-values owned
+// by lane group (l / 16).  Which k a (group, element) slot stands for is the
+// caller's choice, as long as the A and B operands agree: the contraction sums
+// over all 32 slots.  Accumulators follow the 16x16 layout: lane l holds
+// rows 4*(l/16) + r (r = 0..3) of column l % 16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hys {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+struct BF16 {
+  using storage = uint16_t;
+  using frag = bf16x8_t;
+  static constexpr int kBytes = 2;
+  // 8 consecutive elements from 16-byte aligned memory
+  __device__ static __forceinline__ frag load8(const storage* p) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    return __builtin_bit_cast(frag, u);
+  }
+  __device__ static __forceinline__ frag zero8() { return __builtin_bit_cast(frag, make_uint4(0, 0, 0, 0)); }
+  __device__ static __forceinline__ void mma(f32x4_t& acc, const frag& a, const frag& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  }
+  __device__ static __forceinline__ storage from_float(float x) { return f32_to_bf16_rne(x); }
+  __device__ static __forceinline__ float to_float(storage x) { return bf16_to_f32(x); }
+  // pack two groups of four floats (RNE) into one fragment
+  __device__ static __forceinline__ frag pack(const float* lo4, const float* hi4) {
+    uint4 u;
+    u.x = (uint32_t)f32_to_bf16_rne(lo4[0]) | ((uint32_t)f32_to_bf16_rne(lo4[1]) << 16);
+    u.y = (uint32_t)f32_to_bf16_rne(lo4[2]) | ((uint32_t)f32_to_bf16_rne(lo4[3]) << 16);
+    u.z = (uint32_t)f32_to_bf16_rne(hi4[0]) | ((uint32_t)f32_to_bf16_rne(hi4[1]) << 16);
+    u.w = (uint32_t)f32_to_bf16_rne(hi4[2]) | ((uint32_t)f32_to_bf16_rne(hi4[3]) << 16);
+    return __builtin_bit_cast(frag, u);
+  }
+  // four consecutive elements (8 bytes, 8-byte aligned) as a raw vector
+  typedef uint2 quad_t;
+  __device__ static __forceinline__ frag join(quad_t lo, quad_t hi) {
+    return __builtin_bit_cast(frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
+  }
+};
+
+struct F32 {
+  using storage = float;
+  using frag = f32x8_t;
+  static constexpr int kBytes = 4;
+  __device__ static __forceinline__ frag load8(const storage* p) {
+    float4 a = reinterpret_cast<const float4*>(p)[0];
+    float4 b = reinterpret_cast<const float4*>(p)[1];
+    frag f;
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    return f;
+  }
+  __device__ static __forceinline__ frag zero8() {
+    frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = 0.f;
+    return f;
+  }
+  __device__ static __forceinline__ void mma(f32x4_t& acc, const frag& a, const frag& b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+  }
+  __device__ static __forceinline__ storage from_float(float x) { return x; }
+  __device__ static __forceinline__ float to_float(storage x) { return x; }
+  __device__ static __forceinline__ frag pack(const float* lo4, const float* hi4) {
+    frag f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f[e] = lo4[e]; f[4 + e] = hi4[e]; }
+    return f;
+  }
+  typedef float4 quad_t;
+  __device__ static __forceinline__ frag join(quad_t lo, quad_t hi) {
+    frag f;
+    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+    f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+    return f;
+  }
+};
+
+// Order-preserving key of a float32 bit pattern (larger float -> larger key).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u ^ 0x80000000u);
+}
+
+// Compiler barrier plus wait for this wave's outstanding LDS operations, used
+// between lanes of one wave exchanging data through a wave-private LDS region.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ float wave_max16x4(float x) {
+  // max over the four lanes l, l^16, l^32, l^48 that share (l % 16)
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float wave_sum16x4(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+}  // namespace hys

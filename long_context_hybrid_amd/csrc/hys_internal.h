@@ -1,0 +1,93 @@
+// Host-side interface between the C ABI (hysparse_api.cpp) and the kernel
+// translation units.  Plain structs passed by value to the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hys {
+
+// Problem geometry after validation (strides in elements).
+struct Geom {
+  int B, Tq, Tkv, Hq, Hkv, G, D;
+  int dtype;  // 0 f32, 1 bf16
+  float scale;
+  int64_t qs_b, qs_t, qs_h;
+  int64_t ks_b, ks_t, ks_h;
+};
+
+// Row -> candidate count for top-K rows.  Either an explicit device array
+// (clamped to row_len), or the causal rule of the hybrid block
+// (row = ((b * Hkv + g) * NB + n): candidates = Tkv - Tq + min((n+1)*Sb, Tq)),
+// or row_len everywhere.
+struct ValidLen {
+  const int32_t* ptr;
+  int32_t row_len;
+  int32_t causal;  // 1: use (nb, sb, tq, tkv)
+  int32_t nb, sb, tq, tkv;
+};
+
+__host__ __device__ inline int32_t valid_len_of(const ValidLen& v, int64_t row) {
+  int32_t n;
+  if (v.ptr) {
+    n = v.ptr[row];
+    n = n < 0 ? 0 : (n > v.row_len ? v.row_len : n);
+  } else if (v.causal) {
+    int32_t blk = (int32_t)(row % v.nb);
+    int32_t i1 = (blk + 1) * v.sb;
+    if (i1 > v.tq) i1 = v.tq;
+    n = v.tkv - v.tq + i1;
+    if (n > v.row_len) n = v.row_len;
+  } else {
+    n = v.row_len;
+  }
+  return n;
+}
+
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- decode path
+// Split-K attention of one query row per (batch, KV group) unit against a key
+// list (the whole cache for the full layer; idx + window for a sparse layer).
+struct DecodePlan {
+  int units;     // full: B*Hkv ; sparse: B*Hkv*Tq
+  int chunk;     // keys per split
+  int nsplit;    // splits per unit
+  int nsg;       // sparse: global splits (the remaining ones cover the window)
+};
+DecodePlan plan_full_decode(const Geom& g);
+DecodePlan plan_sparse_rows(const Geom& g, int k_top, int window);
+
+struct DecodeWs {
+  float* part_o;   // [units, nsplit, G, D]
+  float* part_ml;  // [units, nsplit, G, 2]
+  float* logits;   // full only: [B, Hq, Tkv] base-2 scaled logits
+  float* lse2;     // full only: [B, Hq] base-2 log-sum-exp
+};
+size_t decode_full_ws_bytes(const Geom& g);
+size_t decode_sparse_ws_bytes(const Geom& g, int k_top, int window);
+DecodeWs carve_decode_ws(const Geom& g, const DecodePlan& p, void* ws, bool full);
+
+hipError_t launch_full_decode(const Geom& g, const void* q, const void* k, const void* v, void* out,
+                              float* lse, float* scores, void* ws, hipStream_t st);
+hipError_t launch_sparse_rows(const Geom& g, const void* q, const void* k, const void* v,
+                              const int32_t* idx, int k_top, int score_block, int window,
+                              const float* gate, void* out, void* ws, hipStream_t st);
+
+// --------------------------------------------------------------- prefill path
+size_t prefill_full_ws_bytes(const Geom& g, int score_block);
+hipError_t launch_full_prefill(const Geom& g, const void* q, const void* k, const void* v,
+                               int score_block, void* out, float* lse, float* scores, void* ws,
+                               hipStream_t st);
+size_t sparse_block_ws_bytes(const Geom& g, int k_top, int window);
+hipError_t launch_sparse_block(const Geom& g, const void* q, const void* k, const void* v,
+                               const int32_t* idx, int k_top, int score_block, int window,
+                               const float* gate, void* out, void* ws, hipStream_t st);
+
+// ---------------------------------------------------------------------- top-K
+size_t topk_ws_bytes(int64_t n_rows, int32_t row_len, int32_t k);
+hipError_t launch_topk(const float* scores, int64_t n_rows, int32_t row_len, int64_t row_stride,
+                       const ValidLen& vl, int32_t k, int32_t* idx, void* ws, hipStream_t st);
+
+}  // namespace hys

@@ -1,0 +1,283 @@
+// C ABI of libhysparse: argument validation, workspace carving and launch
+// sequencing.  No allocation, no global mutable state besides the calling
+// thread's last-error text.
+#include "hysparse.h"
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "hys_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+hys_status fail(hys_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+hys_status ok() {
+  g_err.clear();
+  return HYS_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+hys_status check_desc(const hys_attn_desc* d, hys::Geom* g) {
+  if (!d) return fail(HYS_ERR_NULL_PTR, "desc is NULL");
+  if (d->batch < 1 || d->q_len < 1 || d->kv_len < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1)
+    return fail(HYS_ERR_BAD_SHAPE, "batch, q_len, kv_len, head counts and head_dim must be >= 1");
+  if (d->q_len > d->kv_len) return fail(HYS_ERR_BAD_SHAPE, "q_len must not exceed kv_len");
+  if (d->n_q_heads % d->n_kv_heads != 0) return fail(HYS_ERR_BAD_SHAPE, "n_q_heads must be a multiple of n_kv_heads");
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (G > 16) return fail(HYS_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(HYS_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (d->dtype != HYS_F32 && d->dtype != HYS_BF16) return fail(HYS_ERR_UNSUPPORTED, "dtype must be HYS_F32 or HYS_BF16");
+  if (!(d->scale == d->scale) || std::isinf(d->scale)) return fail(HYS_ERR_BAD_SHAPE, "scale is not finite");
+  const int64_t esz = d->dtype == HYS_BF16 ? 2 : 4;
+  for (int x = 0; x < 3; ++x) {
+    if (d->q_stride[x] < 0 || d->kv_stride[x] < 0) return fail(HYS_ERR_BAD_SHAPE, "negative stride");
+    if ((d->q_stride[x] * esz) % 16 != 0 || (d->kv_stride[x] * esz) % 16 != 0)
+      return fail(HYS_ERR_ALIGN, "batch/token/head strides must be multiples of 16 bytes");
+  }
+  if (d->q_stride[2] < d->head_dim && d->n_q_heads > 1) return fail(HYS_ERR_BAD_SHAPE, "q head stride < head_dim");
+  if (d->kv_stride[2] < d->head_dim && d->n_kv_heads > 1) return fail(HYS_ERR_BAD_SHAPE, "kv head stride < head_dim");
+  if (d->kv_stride[1] < 1 && d->kv_len > 1) return fail(HYS_ERR_BAD_SHAPE, "kv token stride must be >= 1");
+  if (d->q_stride[1] < 1 && d->q_len > 1) return fail(HYS_ERR_BAD_SHAPE, "q token stride must be >= 1");
+  g->B = d->batch;
+  g->Tq = d->q_len;
+  g->Tkv = d->kv_len;
+  g->Hq = d->n_q_heads;
+  g->Hkv = d->n_kv_heads;
+  g->G = G;
+  g->D = d->head_dim;
+  g->dtype = d->dtype;
+  g->scale = d->scale > 0.f ? d->scale : (float)(1.0 / std::sqrt((double)d->head_dim));
+  g->qs_b = d->q_stride[0];
+  g->qs_t = d->q_stride[1];
+  g->qs_h = d->q_stride[2];
+  g->ks_b = d->kv_stride[0];
+  g->ks_t = d->kv_stride[1];
+  g->ks_h = d->kv_stride[2];
+  return HYS_OK;
+}
+
+hys_status check_tensor(const void* p, const char* name, uintptr_t align) {
+  if (!p) return fail(HYS_ERR_NULL_PTR, std::string(name) + " is NULL");
+  if (!aligned(p, align)) return fail(HYS_ERR_ALIGN, std::string(name) + " is not " + std::to_string(align) + "-byte aligned");
+  return HYS_OK;
+}
+
+int n_blocks(const hys::Geom& g, int sb) { return (g.Tq + sb - 1) / sb; }
+
+hys_status check_sb(int sb) {
+  if (sb != 1 && sb != 64) return fail(HYS_ERR_UNSUPPORTED, "score_block must be 1 or 64");
+  return HYS_OK;
+}
+
+bool sparse_by_rows(const hys::Geom& g, int sb) { return sb == 1 || g.Tq == 1; }
+
+size_t full_ws(const hys::Geom& g, int sb) {
+  return g.Tq == 1 ? hys::decode_full_ws_bytes(g) : hys::prefill_full_ws_bytes(g, sb);
+}
+size_t topk_ws(const hys::Geom& g, int sb, int k) {
+  return hys::topk_ws_bytes((int64_t)g.B * g.Hkv * n_blocks(g, sb), g.Tkv, k);
+}
+size_t sparse_ws(const hys::Geom& g, int sb, int k, int w) {
+  return sparse_by_rows(g, sb) ? hys::decode_sparse_ws_bytes(g, k, w) : hys::sparse_block_ws_bytes(g, k, w);
+}
+size_t scores_bytes(const hys::Geom& g, int sb) {
+  return hys::align_up((size_t)g.B * g.Hkv * n_blocks(g, sb) * g.Tkv * sizeof(float));
+}
+size_t idx_bytes(const hys::Geom& g, int sb, int k) {
+  return hys::align_up((size_t)g.B * g.Hkv * n_blocks(g, sb) * (size_t)k * sizeof(int32_t));
+}
+
+hys_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return HYS_OK;
+  if (!ws) return fail(HYS_ERR_WORKSPACE, "workspace is NULL; " + std::to_string(need) + " bytes needed");
+  if (!aligned(ws, 16)) return fail(HYS_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(HYS_ERR_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes; " + std::to_string(need) + " needed");
+  return HYS_OK;
+}
+
+hys_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return ok();
+  if (e == hipErrorNotSupported) return fail(HYS_ERR_UNSUPPORTED, "this path is not available in this build");
+  return fail(HYS_ERR_HIP, std::string("HIP error: ") + hipGetErrorString(e));
+}
+
+hipError_t run_full(const hys::Geom& g, const void* q, const void* k, const void* v, int sb, void* out, float* lse,
+                    float* scores, void* ws, hipStream_t st) {
+  if (g.Tq == 1) return hys::launch_full_decode(g, q, k, v, out, lse, scores, ws, st);
+  return hys::launch_full_prefill(g, q, k, v, sb, out, lse, scores, ws, st);
+}
+
+hipError_t run_sparse(const hys::Geom& g, const void* q, const void* k, const void* v, const int32_t* idx, int kt,
+                      int sb, int w, const float* gate, void* out, void* ws, hipStream_t st) {
+  if (sparse_by_rows(g, sb)) return hys::launch_sparse_rows(g, q, k, v, idx, kt, sb, w, gate, out, ws, st);
+  return hys::launch_sparse_block(g, q, k, v, idx, kt, sb, w, gate, out, ws, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+hys_status hysparse_full_attn_scores(const hys_attn_desc* desc, const void* q, const void* k, const void* v,
+                                     int32_t score_block, void* out, float* lse, float* scores, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  hys::Geom g;
+  hys_status s;
+  if ((s = check_desc(desc, &g))) return s;
+  if ((s = check_sb(score_block))) return s;
+  if ((s = check_tensor(q, "q", 16)) || (s = check_tensor(k, "k", 16)) || (s = check_tensor(v, "v", 16)) ||
+      (s = check_tensor(out, "out", 16)) || (s = check_tensor(scores, "scores", 16)))
+    return s;
+  if (lse && !aligned(lse, 4)) return fail(HYS_ERR_ALIGN, "lse is not 4-byte aligned");
+  if ((s = check_ws(ws, ws_bytes, full_ws(g, score_block)))) return s;
+  return from_hip(run_full(g, q, k, v, score_block, out, lse, scores, ws, stream));
+}
+
+hys_status hysparse_topk(const float* scores, int64_t n_rows, int32_t row_len, int64_t row_stride,
+                         const int32_t* valid_len, int32_t k, int32_t* idx, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  if (n_rows < 0 || row_len < 1 || k < 1) return fail(HYS_ERR_BAD_SHAPE, "need n_rows >= 0, row_len >= 1, k >= 1");
+  if (row_stride < row_len) return fail(HYS_ERR_BAD_SHAPE, "row_stride < row_len");
+  if (row_stride % 4 != 0 && n_rows > 1) return fail(HYS_ERR_ALIGN, "row_stride must be a multiple of 4");
+  if (n_rows == 0) return ok();
+  hys_status s;
+  if ((s = check_tensor(scores, "scores", 16)) || (s = check_tensor(idx, "idx", 4))) return s;
+  if (valid_len && !aligned(valid_len, 4)) return fail(HYS_ERR_ALIGN, "valid_len is not 4-byte aligned");
+  if ((s = check_ws(ws, ws_bytes, hys::topk_ws_bytes(n_rows, row_len, k)))) return s;
+  hys::ValidLen vl{valid_len, row_len, 0, 1, 1, 1, 1};
+  return from_hip(hys::launch_topk(scores, n_rows, row_len, row_stride, vl, k, idx, ws, stream));
+}
+
+hys_status hysparse_sparse_attn(const hys_attn_desc* desc, const void* q, const void* k, const void* v,
+                                const int32_t* idx, int32_t k_top, int32_t score_block, int32_t window,
+                                const float* gate_logits, void* out, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  hys::Geom g;
+  hys_status s;
+  if ((s = check_desc(desc, &g))) return s;
+  if ((s = check_sb(score_block))) return s;
+  if (k_top < 1) return fail(HYS_ERR_BAD_SHAPE, "k_top must be >= 1");
+  if (window < 1) return fail(HYS_ERR_BAD_SHAPE, "window must be >= 1");
+  if ((s = check_tensor(q, "q", 16)) || (s = check_tensor(k, "k", 16)) || (s = check_tensor(v, "v", 16)) ||
+      (s = check_tensor(out, "out", 16)) || (s = check_tensor(idx, "idx", 4)) ||
+      (s = check_tensor(gate_logits, "gate_logits", 4)))
+    return s;
+  if ((s = check_ws(ws, ws_bytes, sparse_ws(g, score_block, k_top, window)))) return s;
+  return from_hip(run_sparse(g, q, k, v, idx, k_top, score_block, window, gate_logits, out, ws, stream));
+}
+
+hys_status hysparse_hybrid_block(const hys_attn_desc* desc, const void* q_full, const void* k, const void* v,
+                                 int32_t n_sparse, const void* const* q_sparse, const float* gate_logits,
+                                 int32_t k_top, int32_t score_block, int32_t window, void* out_full,
+                                 void* const* out_sparse, float* lse, float* scores, int32_t* idx, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  hys::Geom g;
+  hys_status s;
+  if ((s = check_desc(desc, &g))) return s;
+  if ((s = check_sb(score_block))) return s;
+  if (k_top < 1) return fail(HYS_ERR_BAD_SHAPE, "k_top must be >= 1");
+  if (window < 1) return fail(HYS_ERR_BAD_SHAPE, "window must be >= 1");
+  if (n_sparse < 0) return fail(HYS_ERR_BAD_SHAPE, "n_sparse must be >= 0");
+  if ((s = check_tensor(q_full, "q_full", 16)) || (s = check_tensor(k, "k", 16)) || (s = check_tensor(v, "v", 16)) ||
+      (s = check_tensor(out_full, "out_full", 16)))
+    return s;
+  if (n_sparse > 0) {
+    if (!q_sparse || !out_sparse) return fail(HYS_ERR_NULL_PTR, "q_sparse / out_sparse array is NULL");
+    if ((s = check_tensor(gate_logits, "gate_logits", 4))) return s;
+    for (int l = 0; l < n_sparse; ++l) {
+      if ((s = check_tensor(q_sparse[l], "q_sparse[l]", 16)) || (s = check_tensor(out_sparse[l], "out_sparse[l]", 16)))
+        return s;
+    }
+  }
+  if (lse && !aligned(lse, 4)) return fail(HYS_ERR_ALIGN, "lse is not 4-byte aligned");
+  if (scores && !aligned(scores, 16)) return fail(HYS_ERR_ALIGN, "scores is not 16-byte aligned");
+  if (idx && !aligned(idx, 4)) return fail(HYS_ERR_ALIGN, "idx is not 4-byte aligned");
+  const size_t s_b = scores ? 0 : scores_bytes(g, score_block);
+  const size_t i_b = idx ? 0 : idx_bytes(g, score_block, k_top);
+  size_t inner = full_ws(g, score_block);
+  const size_t tk = topk_ws(g, score_block, k_top);
+  const size_t sp = n_sparse > 0 ? sparse_ws(g, score_block, k_top, window) : 0;
+  if (tk > inner) inner = tk;
+  if (sp > inner) inner = sp;
+  if ((s = check_ws(ws, ws_bytes, s_b + i_b + inner))) return s;
+  unsigned char* c = static_cast<unsigned char*>(ws);
+  if (!scores) {
+    scores = reinterpret_cast<float*>(c);
+    c += s_b;
+  }
+  if (!idx) {
+    idx = reinterpret_cast<int32_t*>(c);
+    c += i_b;
+  }
+  void* inner_ws = c;
+  hipError_t e = run_full(g, q_full, k, v, score_block, out_full, lse, scores, inner_ws, stream);
+  if (e != hipSuccess) return from_hip(e);
+  const int NB = n_blocks(g, score_block);
+  hys::ValidLen vl{nullptr, g.Tkv, 1, NB, score_block, g.Tq, g.Tkv};
+  e = hys::launch_topk(scores, (int64_t)g.B * g.Hkv * NB, g.Tkv, g.Tkv, vl, k_top, idx, inner_ws, stream);
+  if (e != hipSuccess) return from_hip(e);
+  for (int l = 0; l < n_sparse; ++l) {
+    e = run_sparse(g, q_sparse[l], k, v, idx, k_top, score_block, window, gate_logits + (size_t)l * g.Hq,
+                   out_sparse[l], inner_ws, stream);
+    if (e != hipSuccess) return from_hip(e);
+  }
+  return ok();
+}
+
+size_t hysparse_workspace_bytes(int32_t op, const hys_attn_desc* desc, int32_t score_block, int32_t k_top,
+                                int32_t window) {
+  hys::Geom g;
+  if (check_desc(desc, &g) != HYS_OK) return 0;
+  if (score_block != 1 && score_block != 64) return 0;
+  if (k_top < 1) k_top = 1;
+  if (window < 1) window = 1;
+  switch (op) {
+    case HYS_OP_FULL:
+      return full_ws(g, score_block);
+    case HYS_OP_TOPK:
+      return topk_ws(g, score_block, k_top);
+    case HYS_OP_SPARSE:
+      return sparse_ws(g, score_block, k_top, window);
+    case HYS_OP_HYBRID: {
+      size_t inner = full_ws(g, score_block);
+      const size_t tk = topk_ws(g, score_block, k_top);
+      const size_t sp = sparse_ws(g, score_block, k_top, window);
+      if (tk > inner) inner = tk;
+      if (sp > inner) inner = sp;
+      return scores_bytes(g, score_block) + idx_bytes(g, score_block, k_top) + inner;
+    }
+    default:
+      return 0;
+  }
+}
+
+size_t hysparse_topk_workspace_bytes(int64_t n_rows, int32_t row_len, int32_t k) {
+  if (n_rows < 0 || row_len < 1 || k < 1) return 0;
+  return hys::topk_ws_bytes(n_rows, row_len, k);
+}
+
+const char* hysparse_status_string(hys_status status) {
+  switch (status) {
+    case HYS_OK: return "ok";
+    case HYS_ERR_NULL_PTR: return "null pointer";
+    case HYS_ERR_BAD_SHAPE: return "bad shape";
+    case HYS_ERR_UNSUPPORTED: return "unsupported";
+    case HYS_ERR_ALIGN: return "misaligned pointer or stride";
+    case HYS_ERR_WORKSPACE: return "workspace too small";
+    case HYS_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* hysparse_last_error(void) { return g_err.c_str(); }
+
+int32_t hysparse_version(void) { return 100; }
+
+}  // extern "C"

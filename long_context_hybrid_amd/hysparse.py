@@ -1,0 +1,229 @@
+"""ctypes binding of libhysparse (the HIP C ABI declared in include/hysparse.h).
+
+Argument marshalling only: every step of the computation runs in the
+library's HIP kernels.  PyTorch provides device memory and the current
+stream.  There is no fallback: if the library is missing or a call fails,
+an exception is raised.
+
+Functions keep the C names:
+``hysparse_full_attn_scores``, ``hysparse_topk``, ``hysparse_sparse_attn``,
+``hysparse_hybrid_block``, ``hysparse_workspace_bytes``,
+``hysparse_topk_workspace_bytes``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhysparse.so")
+
+HYS_F32, HYS_BF16 = 0, 1
+HYS_OP_FULL, HYS_OP_TOPK, HYS_OP_SPARSE, HYS_OP_HYBRID = 0, 1, 2, 3
+STATUS = {0: "HYS_OK", 1: "HYS_ERR_NULL_PTR", 2: "HYS_ERR_BAD_SHAPE", 3: "HYS_ERR_UNSUPPORTED",
+          4: "HYS_ERR_ALIGN", 5: "HYS_ERR_WORKSPACE", 6: "HYS_ERR_HIP"}
+
+EXPORTS = ("hysparse_full_attn_scores", "hysparse_topk", "hysparse_sparse_attn", "hysparse_hybrid_block",
+           "hysparse_workspace_bytes", "hysparse_topk_workspace_bytes", "hysparse_status_string",
+           "hysparse_last_error", "hysparse_version")
+
+
+class HysAttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("q_len", ctypes.c_int32), ("kv_len", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("q_stride", ctypes.c_int64 * 3), ("kv_stride", ctypes.c_int64 * 3)]
+
+
+class HysError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """Load libhysparse.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m long_context_hybrid_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    D = ctypes.POINTER(HysAttnDesc)
+    L.hysparse_full_attn_scores.argtypes = [D, _P, _P, _P, i32, _P, _P, _P, _P, sz, _P]
+    L.hysparse_topk.argtypes = [_P, i64, i32, i64, _P, i32, _P, _P, sz, _P]
+    L.hysparse_sparse_attn.argtypes = [D, _P, _P, _P, _P, i32, i32, i32, _P, _P, _P, sz, _P]
+    L.hysparse_hybrid_block.argtypes = [D, _P, _P, _P, i32, ctypes.POINTER(_P), _P, i32, i32, i32, _P,
+                                        ctypes.POINTER(_P), _P, _P, _P, _P, sz, _P]
+    for f in ("hysparse_full_attn_scores", "hysparse_topk", "hysparse_sparse_attn", "hysparse_hybrid_block"):
+        getattr(L, f).restype = i32
+    L.hysparse_workspace_bytes.argtypes = [i32, D, i32, i32, i32]
+    L.hysparse_workspace_bytes.restype = sz
+    L.hysparse_topk_workspace_bytes.argtypes = [i64, i32, i32]
+    L.hysparse_topk_workspace_bytes.restype = sz
+    L.hysparse_status_string.argtypes = [i32]
+    L.hysparse_status_string.restype = ctypes.c_char_p
+    L.hysparse_last_error.argtypes = []
+    L.hysparse_last_error.restype = ctypes.c_char_p
+    L.hysparse_version.restype = i32
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise HysError(status, lib().hysparse_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return HYS_BF16
+    if dt == torch.float32:
+        return HYS_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def make_desc(q: torch.Tensor, k: torch.Tensor, scale: float = 0.0) -> HysAttnDesc:
+    """Descriptor for q [B, Tq, Hq, D] and k/v [B, Tkv, Hkv, D] (head_dim contiguous)."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be 4-D [B, T, H, D]")
+    if q.stride(3) != 1 or k.stride(3) != 1:
+        raise ValueError("head_dim must be the contiguous axis")
+    B, Tq, Hq, D = q.shape
+    d = HysAttnDesc()
+    d.batch, d.q_len, d.kv_len = B, Tq, k.shape[1]
+    d.n_q_heads, d.n_kv_heads, d.head_dim = Hq, k.shape[2], D
+    d.dtype = _dtype_code(q.dtype)
+    d.scale = float(scale)
+    for x in range(3):
+        d.q_stride[x] = q.stride(x)
+        d.kv_stride[x] = k.stride(x)
+    return d
+
+
+def hysparse_workspace_bytes(op: int, desc: HysAttnDesc, score_block: int, k_top: int = 1, window: int = 1) -> int:
+    return int(lib().hysparse_workspace_bytes(op, ctypes.byref(desc), score_block, k_top, window))
+
+
+def hysparse_topk_workspace_bytes(n_rows: int, row_len: int, k: int) -> int:
+    return int(lib().hysparse_topk_workspace_bytes(n_rows, row_len, k))
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if ws is not None:
+        return ws
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _same_device(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if t is not None and t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    return dev
+
+
+def hysparse_full_attn_scores(q, k, v, score_block: int, out=None, lse=None, scores=None, want_lse: bool = True,
+                              workspace=None, scale: float = 0.0):
+    """Full-attention layer; returns (out, lse or None, scores)."""
+    dev = _same_device(q, k, v)
+    if k.stride() != v.stride():
+        raise ValueError("k and v must share strides")
+    desc = make_desc(q, k, scale)
+    B, Tq, Hq, D = q.shape
+    Hkv, Tkv = k.shape[2], k.shape[1]
+    NB = -(-Tq // score_block)
+    out = torch.empty((B, Tq, Hq, D), dtype=q.dtype, device=dev) if out is None else out
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=dev)
+    scores = torch.empty((B, Hkv, NB, Tkv), dtype=torch.float32, device=dev) if scores is None else scores
+    ws = _workspace(hysparse_workspace_bytes(HYS_OP_FULL, desc, score_block), dev, workspace)
+    _check(lib().hysparse_full_attn_scores(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), score_block, _ptr(out),
+                                           _ptr(lse), _ptr(scores), _ptr(ws), 0 if ws is None else ws.numel(),
+                                           _stream(dev)))
+    return out, lse, scores
+
+
+def hysparse_topk(scores, k: int, valid_len=None, idx=None, workspace=None):
+    """Top-K of each row of a 2-D float32 tensor (last axis contiguous)."""
+    dev = _same_device(scores)
+    if scores.dim() != 2 or scores.stride(1) != 1 or scores.dtype != torch.float32:
+        raise ValueError("scores must be a 2-D float32 tensor with contiguous rows")
+    R, L = scores.shape
+    idx = torch.empty((R, k), dtype=torch.int32, device=dev) if idx is None else idx
+    if valid_len is not None and (valid_len.dtype != torch.int32 or valid_len.numel() != R):
+        raise ValueError("valid_len must be int32 [n_rows]")
+    ws = _workspace(hysparse_topk_workspace_bytes(R, L, k), dev, workspace)
+    _check(lib().hysparse_topk(_ptr(scores), R, L, scores.stride(0) if R > 1 else L, _ptr(valid_len), k, _ptr(idx),
+                               _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)))
+    return idx
+
+
+def hysparse_sparse_attn(q, k, v, idx, k_top: int, score_block: int, window: int, gate_logits, out=None,
+                         workspace=None, scale: float = 0.0):
+    """One sparse layer over the shared k, v at the given indices; returns out."""
+    dev = _same_device(q, k, v, idx, gate_logits)
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be contiguous int32 [B, Hkv, NB, k_top]")
+    if gate_logits.dtype != torch.float32 or not gate_logits.is_contiguous():
+        raise ValueError("gate_logits must be contiguous float32 [Hq]")
+    desc = make_desc(q, k, scale)
+    out = torch.empty(q.shape, dtype=q.dtype, device=dev) if out is None else out
+    ws = _workspace(hysparse_workspace_bytes(HYS_OP_SPARSE, desc, score_block, k_top, window), dev, workspace)
+    _check(lib().hysparse_sparse_attn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), k_top, score_block,
+                                      window, _ptr(gate_logits), _ptr(out), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(dev)))
+    return out
+
+
+def hysparse_hybrid_block(q_full, k, v, q_sparse: Sequence[torch.Tensor], gate_logits, k_top: int,
+                          score_block: int, window: int, out_full=None, out_sparse=None, lse=None, scores=None,
+                          idx=None, want_scores: bool = True, workspace=None, scale: float = 0.0):
+    """Full layer -> top-K -> len(q_sparse) sparse layers.  Returns a dict with
+    out_full, out (list), lse, scores, idx (the last three may be None)."""
+    dev = _same_device(q_full, k, v, *q_sparse)
+    desc = make_desc(q_full, k, scale)
+    B, Tq, Hq, D = q_full.shape
+    Hkv, Tkv = k.shape[2], k.shape[1]
+    NB = -(-Tq // score_block)
+    N = len(q_sparse)
+    for qs in q_sparse:
+        if qs.shape != q_full.shape or qs.stride() != q_full.stride() or qs.dtype != q_full.dtype:
+            raise ValueError("every q_sparse must match q_full in shape, strides and dtype")
+    if N:
+        if gate_logits.dtype != torch.float32 or not gate_logits.is_contiguous() or gate_logits.shape != (N, Hq):
+            raise ValueError("gate_logits must be contiguous float32 [n_sparse, Hq]")
+        _same_device(q_full, gate_logits)
+    out_full = torch.empty(q_full.shape, dtype=q_full.dtype, device=dev) if out_full is None else out_full
+    if out_sparse is None:
+        out_sparse = [torch.empty(q_full.shape, dtype=q_full.dtype, device=dev) for _ in range(N)]
+    if want_scores:
+        scores = torch.empty((B, Hkv, NB, Tkv), dtype=torch.float32, device=dev) if scores is None else scores
+        idx = torch.empty((B, Hkv, NB, k_top), dtype=torch.int32, device=dev) if idx is None else idx
+    ws = _workspace(hysparse_workspace_bytes(HYS_OP_HYBRID, desc, score_block, k_top, window), dev, workspace)
+    qs_arr = (_P * max(N, 1))(*[qs.data_ptr() for qs in q_sparse])
+    os_arr = (_P * max(N, 1))(*[o.data_ptr() for o in out_sparse])
+    _check(lib().hysparse_hybrid_block(ctypes.byref(desc), _ptr(q_full), _ptr(k), _ptr(v), N, qs_arr,
+                                       _ptr(gate_logits) if N else None, k_top, score_block, window, _ptr(out_full),
+                                       os_arr, _ptr(lse), _ptr(scores), _ptr(idx), _ptr(ws),
+                                       0 if ws is None else ws.numel(), _stream(dev)))
+    return {"out_full": out_full, "out": list(out_sparse), "lse": lse, "scores": scores, "idx": idx}

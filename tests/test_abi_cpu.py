@@ -1,0 +1,136 @@
+"""The C ABI library loads, exports what include/hysparse.h declares, and
+rejects bad arguments on the host before launching anything.
+
+These run without a GPU: every call here fails validation, which happens
+before any HIP call (pointers are fake, never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_hybrid_amd import hysparse as hy
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hysparse.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(hy.LIB_PATH), reason="libhysparse.so not built")
+
+FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p(0x10004)   # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(hysparse_\w+)\s*\(", text)))
+
+
+def test_exports_match_header():
+    L = hy.lib()
+    names = declared_functions()
+    assert set(names) == set(hy.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    L = hy.lib()
+    assert L.hysparse_status_string(0) == b"ok"
+    for s in range(1, 7):
+        assert L.hysparse_status_string(s) not in (b"ok", b"unknown status")
+    assert L.hysparse_status_string(99) == b"unknown status"
+    assert L.hysparse_version() >= 100
+
+
+def _desc(B=2, Tq=1, Tkv=256, Hq=8, Hkv=2, D=128, dtype=hy.HYS_BF16):
+    d = hy.HysAttnDesc()
+    d.batch, d.q_len, d.kv_len, d.n_q_heads, d.n_kv_heads, d.head_dim = B, Tq, Tkv, Hq, Hkv, D
+    d.dtype, d.scale = dtype, 0.0
+    for x, s in enumerate((Tq * Hq * D, Hq * D, D)):
+        d.q_stride[x] = s
+    for x, s in enumerate((Tkv * Hkv * D, Hkv * D, D)):
+        d.kv_stride[x] = s
+    return d
+
+
+def _full(d, sb=1, q=FAKE, out=FAKE, scores=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return hy.lib().hysparse_full_attn_scores(ctypes.byref(d), q, FAKE, FAKE, sb, out, None, scores, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda d: setattr(d, "q_len", 300), 2),          # q_len > kv_len
+    (lambda d: setattr(d, "n_kv_heads", 3), 2),       # Hq % Hkv != 0
+    (lambda d: setattr(d, "head_dim", 96), 3),        # unsupported head_dim
+    (lambda d: setattr(d, "dtype", 7), 3),            # unknown dtype
+    (lambda d: (setattr(d, "n_q_heads", 64), setattr(d, "n_kv_heads", 2)), 3),  # G = 32 > 16
+    (lambda d: setattr(d, "batch", 0), 2),
+    (lambda d: d.kv_stride.__setitem__(1, 100), 4),   # 200-byte token stride
+    (lambda d: d.q_stride.__setitem__(2, -128), 2),
+])
+def test_desc_validation(mutate, status):
+    d = _desc()
+    mutate(d)
+    assert _full(d) == status
+    assert hy.lib().hysparse_last_error() != b""
+
+
+def test_pointer_and_workspace_checks():
+    d = _desc()
+    L = hy.lib()
+    assert _full(d, q=None) == 1
+    assert _full(d, scores=FAKE_ODD) == 4
+    assert _full(d, sb=32) == 3
+    need = L.hysparse_workspace_bytes(hy.HYS_OP_FULL, ctypes.byref(d), 1, 1, 1)
+    assert need > 0
+    assert _full(d, ws=None, ws_bytes=0) == 5
+    assert _full(d, ws_bytes=need - 1) == 5
+    assert b"needed" in L.hysparse_last_error()
+
+
+def test_topk_validation():
+    L = hy.lib()
+    assert L.hysparse_topk(FAKE, 4, 100, 100, None, 0, FAKE, FAKE, 1 << 30, None) == 2   # k < 1
+    assert L.hysparse_topk(FAKE, 4, 100, 50, None, 8, FAKE, FAKE, 1 << 30, None) == 2    # stride < len
+    assert L.hysparse_topk(FAKE, 4, 100, 102, None, 8, FAKE, FAKE, 1 << 30, None) == 4   # stride % 4
+    assert L.hysparse_topk(None, 4, 100, 100, None, 8, FAKE, FAKE, 1 << 30, None) == 1
+    assert L.hysparse_topk(FAKE, 4, 100, 100, None, 8, FAKE, FAKE, 16, None) == 5       # workspace
+    assert L.hysparse_topk(FAKE, 0, 100, 100, None, 8, FAKE, None, 0, None) == 0        # empty: no-op
+    assert L.hysparse_topk_workspace_bytes(16, 131072, 2048) > 16 * 4096 * 4
+
+
+def test_sparse_and_hybrid_validation():
+    L = hy.lib()
+    d = _desc()
+    args = lambda kt, w: (ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, kt, 1, w, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert L.hysparse_sparse_attn(*args(0, 128)) == 2
+    assert L.hysparse_sparse_attn(*args(64, 0)) == 2
+    assert L.hysparse_sparse_attn(ctypes.byref(d), FAKE, FAKE, FAKE, None, 64, 1, 128, FAKE, FAKE, FAKE,
+                                  1 << 40, None) == 1
+    P = ctypes.c_void_p
+    arr = (P * 2)(FAKE.value, None)
+    outs = (P * 2)(FAKE.value, FAKE.value)
+    st = L.hysparse_hybrid_block(ctypes.byref(d), FAKE, FAKE, FAKE, 2, arr, FAKE, 64, 1, 128, FAKE, outs,
+                                 None, None, None, FAKE, 1 << 40, None)
+    assert st == 1 and b"q_sparse" in L.hysparse_last_error()
+    st = L.hysparse_hybrid_block(ctypes.byref(d), FAKE, FAKE, FAKE, -1, None, None, 64, 1, 128, FAKE, None,
+                                 None, None, None, FAKE, 1 << 40, None)
+    assert st == 2
+
+
+def test_workspace_query_grows_with_problem():
+    L = hy.lib()
+    small = L.hysparse_workspace_bytes(hy.HYS_OP_HYBRID, ctypes.byref(_desc(Tkv=1024)), 1, 64, 128)
+    large = L.hysparse_workspace_bytes(hy.HYS_OP_HYBRID, ctypes.byref(_desc(Tkv=8192)), 1, 64, 128)
+    assert 0 < small < large
+    bad = _desc()
+    bad.head_dim = 80
+    assert L.hysparse_workspace_bytes(hy.HYS_OP_FULL, ctypes.byref(bad), 1, 1, 1) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64)
+    k = torch.zeros(1, 8, 1, 64)
+    with pytest.raises(ValueError):
+        hy.hysparse_full_attn_scores(q, k, k, 1)

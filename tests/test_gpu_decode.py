@@ -1,0 +1,198 @@
+"""GPU parity of the decode path (one query row per sequence) and of top-K.
+
+Every case compares the HIP library, called through its C ABI, with the CPU
+oracle on the same seeded inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+from long_context_hybrid_amd import hysparse as hy
+from long_context_hybrid_amd import inputs as gen
+from oracle import hysparse_oracle as orc
+from tests.gpu_util import (assert_attn_close, assert_scores_close, dev_tensor, eps_valid, host, say)
+
+pytestmark = pytest.mark.gpu
+
+W = gen.WORKLOADS
+DECODE_CASES = {
+    # name: workload (reduced sizes span several splits and ragged tails)
+    "decode8k_small": W["decode8k"].replace(batch=2, kv_len=1000, k_top=100, n_sparse=2),
+    "decode128k_small": W["decode128k"].replace(batch=1, kv_len=5000, k_top=256, n_sparse=2, n_planted=16),
+    "tiny_decode_f32": W["tiny"].replace(batch=2, q_len=1, kv_len=300, k_top=32, n_sparse=2),
+    "mha_d64_bf16": W["decode8k"].replace(batch=1, kv_len=777, n_q_heads=3, n_kv_heads=3, head_dim=64,
+                                          k_top=64, window=40, n_sparse=1),
+    "g16_window300": W["decode128k"].replace(batch=1, kv_len=2000, k_top=300, window=300, n_sparse=1,
+                                             n_planted=8),
+    "short_ctx": W["decode8k"].replace(batch=1, kv_len=20, k_top=64, window=128, n_sparse=1),
+}
+
+
+def _inputs(wl):
+    return gen.make_inputs(wl)
+
+
+def _dev(inp):
+    dt = inp.wl.dtype
+    return (dev_tensor(inp.q_full, dt), dev_tensor(inp.k, dt), dev_tensor(inp.v, dt),
+            [dev_tensor(q, dt) for q in inp.q_sparse], torch.from_numpy(inp.gate_logits).cuda())
+
+
+@pytest.fixture(autouse=True)
+def _lib():
+    hy.lib()
+
+
+# ---------------------------------------------------------------------- top-K
+
+@pytest.mark.parametrize("kind", ["probs", "ties", "signed"])
+@pytest.mark.parametrize("k", [1, 7, 1024, 2048])
+def test_topk_bit_exact(kind, k):
+    say(f"topk kind={kind} k={k}")
+    R, L = 24, 9000
+    S = gen.random_scores(11 + k, R, L, kind)
+    vl = np.random.default_rng(k).integers(0, L + 1, size=R).astype(np.int32)
+    vl[0], vl[1], vl[2] = 0, L, min(k, L)
+    ref = orc.topk_rows(S, vl, k)
+    got = hy.hysparse_topk(torch.from_numpy(S).cuda(), k, valid_len=torch.from_numpy(vl).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(got), ref)
+
+
+def test_topk_long_rows_decode128k_shape():
+    """16 rows of 131072 scores, K = 2048: the decode-time selection shape."""
+    say("topk 16x131072 k=2048")
+    S = gen.random_scores(5, 16, 131072, "probs")
+    ref = orc.topk_rows(S, 131072, 2048)
+    got = hy.hysparse_topk(torch.from_numpy(S).cuda(), 2048)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(got), ref)
+
+
+def test_topk_row_stride_and_all_equal():
+    say("topk strided rows, all-equal rows")
+    base = np.full((5, 4100), 0.5, np.float32)
+    base[3, 17] = 0.75
+    t = torch.from_numpy(base).cuda()[:, :4096]
+    got = host(hy.hysparse_topk(t, 10))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got[0], np.arange(10))
+    np.testing.assert_array_equal(got[3], np.array([0, 1, 2, 3, 4, 5, 6, 7, 8, 17]))
+
+
+# --------------------------------------------------------------- full decode
+
+@pytest.mark.parametrize("name", list(DECODE_CASES))
+def test_full_decode_matches_oracle(name):
+    wl = DECODE_CASES[name]
+    say(f"full decode {name}")
+    inp = _inputs(wl)
+    qf, k, v, _, _ = _dev(inp)
+    out, lse, S = hy.hysparse_full_attn_scores(qf, k, v, wl.score_block)
+    torch.cuda.synchronize()
+    O_ref, LSE_ref, S_ref = orc.full_layer(inp.q_full, inp.k, inp.v, wl.score_block)
+    assert_attn_close(out, O_ref, wl.dtype, "O_full")
+    np.testing.assert_allclose(host(lse), LSE_ref, rtol=0, atol=2e-5 if wl.dtype == "bf16" else 1e-5)
+    assert_scores_close(S, S_ref)
+
+
+# -------------------------------------------------------------- sparse decode
+
+@pytest.mark.parametrize("name", list(DECODE_CASES))
+def test_sparse_decode_on_oracle_indices(name):
+    wl = DECODE_CASES[name]
+    say(f"sparse decode {name}")
+    inp = _inputs(wl)
+    _, k, v, qs, gates = _dev(inp)
+    _, _, S_ref = orc.full_layer(inp.q_full, inp.k, inp.v, wl.score_block)
+    idx = orc.select_indices(S_ref, wl.q_len, wl.kv_len, wl.score_block, wl.k_top)
+    g = gates[0].clone()
+    g[0] = float("inf")      # pure global branch
+    g[-1] = float("-inf")    # pure window branch
+    out = hy.hysparse_sparse_attn(qs[0], k, v, torch.from_numpy(idx).cuda(), wl.k_top, wl.score_block,
+                                  wl.window, g)
+    torch.cuda.synchronize()
+    ref = orc.sparse_layer(inp.q_sparse[0], inp.k, inp.v, idx, wl.score_block, wl.window, host(g))
+    assert_attn_close(out, ref, wl.dtype, "sparse out")
+
+
+# ----------------------------------------------------------- hybrid block e2e
+
+def check_hybrid(wl, inp, res, n_check_layers=None):
+    """End-to-end criteria: GPU scores within tolerance of the oracle's; GPU
+    indices equal the oracle's top-K of the GPU scores (bit-exact) and are
+    eps-valid against the oracle's scores; sparse outputs match the oracle
+    evaluated on the GPU's indices."""
+    O_ref, LSE_ref, S_ref = orc.full_layer(inp.q_full, inp.k, inp.v, wl.score_block)
+    assert_attn_close(res["out_full"], O_ref, wl.dtype, "O_full")
+    assert_scores_close(res["scores"], S_ref)
+    S_gpu = host(res["scores"]).astype(np.float32)
+    idx_gpu = host(res["idx"])
+    idx_from_gpu_S = orc.select_indices(S_gpu, wl.q_len, wl.kv_len, wl.score_block, wl.k_top)
+    np.testing.assert_array_equal(idx_gpu, idx_from_gpu_S)
+    idx_ref = orc.select_indices(S_ref, wl.q_len, wl.kv_len, wl.score_block, wl.k_top)
+    B, Hkv, NB, _ = S_ref.shape
+    differ = 0
+    for b in range(B):
+        for g in range(Hkv):
+            for n in range(NB):
+                c = orc.candidate_count(n, wl.q_len, wl.kv_len, wl.score_block)
+                assert eps_valid(idx_gpu[b, g, n], S_ref[b, g, n], c)
+                differ += int(not np.array_equal(idx_gpu[b, g, n], idx_ref[b, g, n]))
+    say(f"  index rows differing from the oracle's own selection: {differ}/{B * Hkv * NB}")
+    layers = range(len(inp.q_sparse)) if n_check_layers is None else range(n_check_layers)
+    for l in layers:
+        ref = orc.sparse_layer(inp.q_sparse[l], inp.k, inp.v, idx_gpu, wl.score_block, wl.window,
+                               inp.gate_logits[l])
+        assert_attn_close(res["out"][l], ref, wl.dtype, f"sparse layer {l}")
+    return S_ref, idx_gpu
+
+
+@pytest.mark.parametrize("name", list(DECODE_CASES))
+def test_hybrid_block_decode(name):
+    wl = DECODE_CASES[name]
+    say(f"hybrid decode {name}")
+    inp = _inputs(wl)
+    qf, k, v, qs, gates = _dev(inp)
+    res = hy.hysparse_hybrid_block(qf, k, v, qs, gates, wl.k_top, wl.score_block, wl.window)
+    torch.cuda.synchronize()
+    _, idx_gpu = check_hybrid(wl, inp, res)
+    if inp.planted is not None:
+        for b in range(wl.batch):
+            for g in range(wl.n_kv_heads):
+                assert set(inp.planted[b].tolist()) <= set(idx_gpu[b, g, 0].tolist())
+
+
+def test_hybrid_block_deterministic():
+    wl = DECODE_CASES["decode8k_small"]
+    say("determinism decode8k_small x5")
+    inp = _inputs(wl)
+    qf, k, v, qs, gates = _dev(inp)
+    first = None
+    for _ in range(5):
+        res = hy.hysparse_hybrid_block(qf, k, v, qs, gates, wl.k_top, wl.score_block, wl.window)
+        torch.cuda.synchronize()
+        cur = [res["out_full"].clone(), res["scores"].clone(), res["idx"].clone()] + [o.clone() for o in res["out"]]
+        if first is None:
+            first = cur
+        else:
+            for a, b in zip(first, cur):
+                assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------- full sizes
+
+@pytest.mark.parametrize("name", ["decode8k", "decode128k"])
+def test_hybrid_block_full_size(name):
+    """The real decode workloads (two of their sparse layers checked)."""
+    wl = W[name].replace(n_sparse=2)
+    say(f"hybrid decode full size {name}")
+    inp = _inputs(wl)
+    qf, k, v, qs, gates = _dev(inp)
+    res = hy.hysparse_hybrid_block(qf, k, v, qs, gates, wl.k_top, wl.score_block, wl.window)
+    torch.cuda.synchronize()
+    _, idx_gpu = check_hybrid(wl, inp, res)
+    if inp.planted is not None:
+        for b in range(wl.batch):
+            for g in range(wl.n_kv_heads):
+                assert set(inp.planted[b].tolist()) <= set(idx_gpu[b, g, 0].tolist())
