@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark of the HySparse hybrid-block hot path on one MI355X.
+
+One step = one hybrid block over one batch of synthetic input: the full
+attention layer with score emission, the top-K select, then every sparse
+layer (all of them reading the full layer's K/V and indices).  Default
+workload: decode at 128K context (B 4, Hq 64 / Hkv 4, D 128, bf16, K 2048,
+window 128, 9 sparse layers); ``value`` is decoded tokens per second of the
+whole block, inputs resident in HBM.
+
+Prints one JSON line.  Per-kernel durations come from HIP events that the
+library records around each kernel on its launch stream (a second pass over
+the same steps, so the timed pass carries no extra events).  The
+``cpu_baseline`` leg times the CPU oracle on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "sparse-layer decode tokens/s + HBM GB/s (% roofline) at 128K ctx, K=2048"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode128k", choices=["decode128k", "decode8k", "prefill32k", "tiny"])
+    ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the oracle timing")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    return ap.parse_args()
+
+
+def sparse_layer_bytes(wl, idx_np):
+    """Algorithmic bytes of one sparse layer: the gathered K and V rows of both
+    branches (valid entries only), the layer's queries and outputs, the indices."""
+    e = 2 if wl.dtype == "bf16" else 4
+    row = wl.head_dim * e
+    B, Hkv, NB, K = idx_np.shape
+    Tq, Tkv, Sb, W = wl.q_len, wl.kv_len, wl.score_block, wl.window
+    rows = 0
+    for n in range(NB):
+        i0, i1 = n * Sb, min((n + 1) * Sb, Tq)
+        last = Tkv - Tq + i1 - 1
+        first = Tkv - Tq + i0
+        nsel = int((idx_np[:, :, n] >= 0).sum())
+        nwin = B * Hkv * (last + 1 - max(0, first - W + 1))
+        rows += nsel + nwin
+    q_out = 2 * wl.batch * Tq * wl.n_q_heads * wl.head_dim * e
+    return 2 * rows * row + q_out + idx_np.size * 4
+
+
+def full_split_bytes(wl):
+    e = 2 if wl.dtype == "bf16" else 4
+    return 2 * wl.batch * wl.kv_len * wl.n_kv_heads * wl.head_dim * e + wl.batch * wl.q_len * wl.n_q_heads * wl.head_dim * e
+
+
+def cpu_baseline(wl, inp, budget_s: float):
+    """Time the oracle on (b, g) units of the block until the budget is spent,
+    then scale to the whole block."""
+    from threadpoolctl import threadpool_info
+    from oracle import hysparse_oracle as orc
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    units = [(b, g) for b in range(wl.batch) for g in range(wl.n_kv_heads)]
+    NB = wl.n_blocks
+    done = 0
+    t0 = time.perf_counter()
+    for (b, g) in units:
+        for n in range(NB):
+            _, _, s = orc.full_layer_block(inp.q_full, inp.k, inp.v, b, g, n, wl.score_block)
+            c = orc.candidate_count(n, wl.q_len, wl.kv_len, wl.score_block)
+            idx = orc.topk_row(s.astype(np.float32), c, wl.k_top)
+            for l in range(wl.n_sparse):
+                orc.sparse_layer_block(inp.q_sparse[l], inp.k, inp.v, idx, b, g, n, wl.score_block, wl.window,
+                                       inp.gate_logits[l])
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    step_s = el * len(units) / done
+    return {"value": wl.batch * wl.q_len / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(units)} (batch, KV-group) units of one block (full layer, top-K, "
+                      f"{wl.n_sparse} sparse layers) in {el:.1f} s, scaled to the whole block"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU; multi-GPU runs are not part of it (use --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from long_context_hybrid_amd import hysparse as hy
+    from long_context_hybrid_amd import inputs as gen
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    hy.lib()
+    wl = gen.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    inp = gen.make_inputs(wl)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    to = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(tdt).to(dev)
+    qf, k, v = to(inp.q_full), to(inp.k), to(inp.v)
+    qs = [to(q) for q in inp.q_sparse]
+    gates = torch.from_numpy(inp.gate_logits).to(dev)
+    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    B, Tq, Hq, D = qf.shape
+    Hkv, Tkv = k.shape[2], k.shape[1]
+    NB = wl.n_blocks
+    out_full = torch.empty_like(qf)
+    outs = [torch.empty_like(qf) for _ in qs]
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=dev)
+    scores = torch.empty((B, Hkv, NB, Tkv), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, Hkv, NB, wl.k_top), dtype=torch.int32, device=dev)
+    desc = hy.make_desc(qf, k)
+    ws = torch.empty(hy.hysparse_workspace_bytes(hy.HYS_OP_HYBRID, desc, wl.score_block, wl.k_top, wl.window),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        hy.hysparse_hybrid_block(qf, k, v, qs, gates, wl.k_top, wl.score_block, wl.window, out_full=out_full,
+                                 out_sparse=outs, lse=lse, scores=scores, idx=idx, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+    tokens_per_step = B * Tq
+    value = tokens_per_step / (ms * 1e-3)
+    print(f"[bench] {args.steps} steps: {ms:.4f} ms/step (wall {1e3 * wall / args.steps:.4f})", file=sys.stderr,
+          flush=True)
+
+    # per-kernel durations: second pass with the library's event trace
+    trace = hy.KernelTrace(capacity_kernels=64 * (args.steps + 1))
+    trace.begin()
+    for _ in range(args.steps):
+        step()
+    rows = trace.end()
+    torch.cuda.synchronize()
+    per = {}
+    for name, t in rows:
+        per.setdefault(name, []).append(t)
+    kernels = {n: {"launches_per_step": len(t) / args.steps, "avg_us": 1e3 * float(np.mean(t)),
+                   "us_per_step": 1e3 * float(np.sum(t)) / args.steps} for n, t in per.items()}
+    traced_ms = float(sum(np.sum(t) for t in per.values())) / args.steps
+
+    idx_np = idx.cpu().numpy()
+    result = {"metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+              "config": {"workload": wl.name, "batch": B, "q_len": Tq, "context": Tkv, "q_heads": Hq,
+                         "kv_heads": Hkv, "head_dim": D, "k_top": wl.k_top, "window": wl.window,
+                         "n_sparse": len(qs), "score_block": wl.score_block,
+                         "step": "hybrid block: full layer + top-K + all sparse layers"}}
+
+    def roof(name, alg_bytes):
+        if name not in kernels:
+            return None
+        us = kernels[name]["avg_us"]
+        gbs = alg_bytes / (us * 1e-6) / 1e9
+        return {"kernel": name, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS, "traffic": None, "alg_bytes_per_launch": alg_bytes, "avg_us": us}
+
+    if Tq == 1:
+        dom = max(kernels, key=lambda n: kernels[n]["us_per_step"])
+        result["roofline"] = roof("full_decode_split", full_split_bytes(wl)) if dom == "full_decode_split" else None
+        sb = sparse_layer_bytes(wl, idx_np)
+        rs = roof("sparse_decode", sb)
+        result["roofline_sparse"] = rs
+        if rs:
+            result["sparse_layer"] = {"tokens_per_s": tokens_per_step / (rs["avg_us"] * 1e-6),
+                                      "us_per_layer": rs["avg_us"], "GB_per_s": rs["achieved"],
+                                      "frac_hbm": rs["frac"], "alg_bytes": sb}
+    result["kernels"] = kernels
+    result["traced_ms_per_step"] = traced_ms
+    result["input_sha256"] = inp.sha256()
+    if args.cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -114,7 +114,8 @@ hys_status hysparse_full_attn_scores(const hys_attn_desc* desc, const void* q, c
  *                or NULL for row_len everywhere.
  *   k            K >= 1.
  *   idx          int32 [n_rows, k], written: ascending indices, -1 padded.
- *   ws/ws_bytes  at least hysparse_topk_workspace_bytes(n_rows, row_len, k).
+ *   ws/ws_bytes  at least hysparse_topk_workspace_bytes(n_rows, row_len, k)
+ *                bytes (currently 0: ws may be NULL).
  * Results are bit-exact functions of the input bits (no atomics-order effects).
  */
 hys_status hysparse_topk(const float* scores, int64_t n_rows, int32_t row_len, int64_t row_stride,
@@ -175,6 +176,23 @@ const char* hysparse_last_error(void);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int32_t hysparse_version(void);
+
+/*
+ * Kernel-level timing hook for profilers (not part of the computation).
+ * While a trace is active on the calling thread, the library records, on the
+ * launch stream, events[2i] just before and events[2i+1] just after the i-th
+ * kernel it launches, for as long as 2i+1 < capacity.  `events` is a host
+ * array of events the caller created (hipEventCreate) and keeps alive until
+ * the recorded work has completed.  This is the library's only per-thread
+ * state besides the last-error text.
+ *   hysparse_trace_begin  starts (or restarts) the trace; events NULL stops it.
+ *   hysparse_trace_end    stops it and returns the number of kernels traced.
+ *   hysparse_trace_name   static name of the i-th traced kernel ("" if none);
+ *                         valid until the next hysparse_trace_begin.
+ */
+void hysparse_trace_begin(hipEvent_t* events, int32_t capacity);
+int32_t hysparse_trace_end(void);
+const char* hysparse_trace_name(int32_t i);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,226 @@
+// LDS-staged 64-key tiles and the per-wave MFMA attention step used by the
+// prefill kernels (full layer and block-sparse layer).
+//
+// A workgroup stages one tile of 64 key rows at a time: K row-major (A/B
+// fragments read 16 contiguous bytes per lane) and V transposed (Vt[d][key],
+// so the PV product's B fragments are 8-byte reads of four consecutive keys).
+// Key rows may come from any list (contiguous range, gathered indices,
+// window); a row whose list entry is invalid is loaded from key 0 and masked
+// with index -1, so every load stays in bounds.
+//
+// Rows: a "row tile" is 16 (query, head) rows of one KV group.  In the
+// S^T = K . Q^T product a lane owns row (l % 16) of the tile; in the O = P.V
+// accumulator it owns rows 4*(l/16) + r, r = 0..3 (16x16 MFMA layout).
+#pragma once
+
+#include "hys_common.h"
+
+namespace hys {
+
+constexpr int kTK = 64;  // keys per tile
+
+template <typename TR, int D>
+struct TileLayout {
+  static constexpr int EPC = 16 / TR::kBytes;          // elements per 16-byte chunk
+  static constexpr int CPR = D / EPC;                  // chunks per row
+  static constexpr int KP = D * TR::kBytes + 16;       // K row pitch, bytes
+  static constexpr int VPE = kTK + 16 / TR::kBytes;    // Vt row pitch, elements
+  static constexpr int kKBytes = kTK * KP;
+  static constexpr int kVBytes = D * VPE * TR::kBytes;
+  static constexpr int kBytes = kKBytes + kVBytes;
+};
+
+// Per-thread staging registers of one tile (global -> registers -> LDS), so
+// the next tile's loads can be in flight while the current tile is used.
+template <typename TR, int D, int NT, bool WITH_V>
+struct TileStage {
+  using ST = typename TR::storage;
+  using L = TileLayout<TR, D>;
+  static constexpr int NK = (kTK * L::CPR + NT - 1) / NT;
+  static constexpr int NV = WITH_V ? (16 * L::CPR + NT - 1) / NT : 0;
+  uint4 kr[NK];
+  uint4 vr[NV > 0 ? NV : 1][4];
+  int jk;
+
+  // key(t) -> key index of tile entry t, or -1 when the entry is invalid
+  template <class KeyFn>
+  __device__ __forceinline__ void load(const ST* kbase, const ST* vbase, int64_t ks_t, KeyFn key) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      const int x = tid + s * NT;
+      if (x < kTK * L::CPR) {
+        const int t = x / L::CPR, c = x - (x / L::CPR) * L::CPR;
+        const int j = key(t);
+        kr[s] = *reinterpret_cast<const uint4*>(kbase + (int64_t)(j >= 0 ? j : 0) * ks_t + c * L::EPC);
+      }
+    }
+    if constexpr (WITH_V) {
+#pragma unroll
+      for (int s = 0; s < NV; ++s) {
+        const int x = tid + s * NT;
+        if (x < 16 * L::CPR) {
+          const int kq = x / L::CPR, c = x - (x / L::CPR) * L::CPR;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = key(4 * kq + r);
+            vr[s][r] = *reinterpret_cast<const uint4*>(vbase + (int64_t)(j >= 0 ? j : 0) * ks_t + c * L::EPC);
+          }
+        }
+      }
+    }
+    jk = (tid < kTK) ? key(tid) : -1;
+  }
+
+  __device__ __forceinline__ void store(unsigned char* sm, int* kj) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      const int x = tid + s * NT;
+      if (x < kTK * L::CPR) {
+        const int t = x / L::CPR, c = x - (x / L::CPR) * L::CPR;
+        *reinterpret_cast<uint4*>(sm + t * L::KP + c * 16) = kr[s];
+      }
+    }
+    if constexpr (WITH_V) {
+      ST* vt = reinterpret_cast<ST*>(sm + L::kKBytes);
+#pragma unroll
+      for (int s = 0; s < NV; ++s) {
+        const int x = tid + s * NT;
+        if (x < 16 * L::CPR) {
+          const int kq = x / L::CPR, c = x - (x / L::CPR) * L::CPR;
+#pragma unroll
+          for (int e = 0; e < L::EPC; ++e) {
+            ST* dst = vt + (c * L::EPC + e) * L::VPE + 4 * kq;
+            if constexpr (TR::kBytes == 2) {
+              const int w = e >> 1, sh = 16 * (e & 1);
+              const uint32_t a0 = (reinterpret_cast<const uint32_t*>(&vr[s][0])[w] >> sh) & 0xFFFFu;
+              const uint32_t a1 = (reinterpret_cast<const uint32_t*>(&vr[s][1])[w] >> sh) & 0xFFFFu;
+              const uint32_t a2 = (reinterpret_cast<const uint32_t*>(&vr[s][2])[w] >> sh) & 0xFFFFu;
+              const uint32_t a3 = (reinterpret_cast<const uint32_t*>(&vr[s][3])[w] >> sh) & 0xFFFFu;
+              *reinterpret_cast<uint2*>(dst) = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+            } else {
+              *reinterpret_cast<float4*>(dst) =
+                  make_float4(reinterpret_cast<const float*>(&vr[s][0])[e], reinterpret_cast<const float*>(&vr[s][1])[e],
+                              reinterpret_cast<const float*>(&vr[s][2])[e], reinterpret_cast<const float*>(&vr[s][3])[e]);
+            }
+          }
+        }
+      }
+    }
+    if (tid < kTK) kj[tid] = jk;
+  }
+};
+
+// K fragment of key sub-tile kt (16 keys) for k-step c, from the staged tile:
+// lane (key = l % 16, group = l / 16) gets K[16*kt + key][32c + 8*group + e].
+template <typename TR, int D>
+__device__ __forceinline__ typename TR::frag lds_k_frag(const unsigned char* sm, int kt, int c, int col, int quad) {
+  using L = TileLayout<TR, D>;
+  return TR::load8(reinterpret_cast<const typename TR::storage*>(sm + (16 * kt + col) * L::KP) + 32 * c + 8 * quad);
+}
+
+// Vt fragment for the P.V product: lane (d = 16*dt + l % 16, group q) gets
+// keys {32kk + 4q + e} (e < 4) and {32kk + 16 + 4q + e - 4} (e >= 4).
+template <typename TR, int D>
+__device__ __forceinline__ typename TR::frag lds_v_frag(const unsigned char* sm, int dt, int kk, int col, int quad) {
+  using L = TileLayout<TR, D>;
+  using quad_t = typename TR::quad_t;
+  const typename TR::storage* row =
+      reinterpret_cast<const typename TR::storage*>(sm + L::kKBytes) + (16 * dt + col) * L::VPE + 32 * kk;
+  const quad_t lo = *reinterpret_cast<const quad_t*>(row + 4 * quad);
+  const quad_t hi = *reinterpret_cast<const quad_t*>(row + 16 + 4 * quad);
+  return TR::join(lo, hi);
+}
+
+// Online-softmax state of RTW row tiles of one wave.
+template <int RTW, int D>
+struct RowState {
+  f32x4_t o[RTW][D / 16];
+  float m[RTW];  // running max (base 2) of the lane's row (l % 16)
+  float l[RTW];  // lane-partial running sum of that row
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      m[rt] = kNegInf;
+      l[rt] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[rt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+};
+
+// One wave attends its RTW row tiles to the staged tile.  valid(rt, j) says
+// whether key j may be used by the lane's row (l % 16) of row tile rt;
+// j < 0 marks an invalid tile entry.
+template <typename TR, int D, int RTW, class Valid>
+__device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename TR::frag (&qf)[RTW][D / 32],
+                                            const unsigned char* sm, const int* kj, float sl2, Valid valid) {
+  using frag = typename TR::frag;
+  constexpr int KC = D / 32, DT = D / 16;
+  const int lane = threadIdx.x & 63, col = lane & 15, quad = lane >> 4;
+  f32x4_t sacc[RTW][4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    frag kf[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) kf[c] = lds_k_frag<TR, D>(sm, kt, c, col, quad);
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      sacc[rt][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) TR::mma(sacc[rt][kt], kf[c], qf[rt][c]);
+    }
+  }
+  int jj[4][4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) jj[kt][r] = kj[16 * kt + 4 * quad + r];
+  frag pa[RTW][2];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) {
+    float s[4][4];
+    float mt = kNegInf;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = jj[kt][r];
+        s[kt][r] = (j >= 0 && valid(rt, j)) ? sacc[rt][kt][r] * sl2 : kNegInf;
+        mt = fmaxf(mt, s[kt][r]);
+      }
+    mt = wave_max16x4(mt);
+    const float m_new = fmaxf(st.m[rt], mt);
+    const float mu = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = exp2f(st.m[rt] - mu);
+    float ls = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s[kt][r] = exp2f(s[kt][r] - mu);
+        ls += s[kt][r];
+      }
+    st.l[rt] = st.l[rt] * alpha + ls;
+    st.m[rt] = m_new;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __shfl(alpha, 4 * quad + r);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) st.o[rt][dt][r] *= ar;
+    }
+    pa[rt][0] = TR::pack(s[0], s[1]);
+    pa[rt][1] = TR::pack(s[2], s[3]);
+  }
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const frag vb = lds_v_frag<TR, D>(sm, dt, kk, col, quad);
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt) TR::mma(st.o[rt][dt], pa[rt][kk], vb);
+    }
+}
+
+}  // namespace hys

@@ -19,8 +19,13 @@
 //   O[16 heads x D] += P . V_sel                 (V rows staged transposed in a
 //                                                 wave-private LDS tile)
 // The four waves of the workgroup are merged through LDS and the workgroup
-// writes one partial state (m, l, O) per head; small reduce kernels combine
-// the splits (and for the sparse layer apply the sigmoid gate).
+// writes one partial state (m, l, O) per head.  Sparse layer: a small merge
+// kernel combines each unit's splits and applies the sigmoid gate.  Full
+// layer: a second kernel forms each head's log-sum-exp from the partial
+// states, then the output rows and the importance scores.  (Merging inside
+// the split kernel by its last-arriving workgroup would need a device-scope
+// fence per workgroup, which on this multi-die part writes back and
+// invalidates the die's L2 and costs far more than a second launch.)
 #include "hys_common.h"
 #include "hys_internal.h"
 
@@ -31,7 +36,8 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kStep = 32;  // keys per wave step
 constexpr int kVPad = 4;   // extra key slots per transposed-V row (bank spread)
-constexpr int kScoreChunk = 1024;
+constexpr int kScoreChunk = 4096;  // keys per score workgroup (multiple of 1024)
+
 
 struct DecodeArgs {
   const void* q;
@@ -42,18 +48,24 @@ struct DecodeArgs {
   float sl2;  // softmax scale * log2(e)
   const int32_t* idx;
   int k_top, score_block, NB, window;
-  int chunk, nsplit, nsg;
+  int chunk, wchunk, nsplit, nsg;
   float* logits;
   float* part_o;
   float* part_ml;
+  const float* gate;    // sparse: [Hq] gate logits
+  void* out;            // sparse: [B, Tq, Hq, D]
 };
+
+constexpr int kMaxSparseSplits = 64;
 
 template <typename TR, int D>
 struct DecodeSmem {
   static constexpr int kVP = kStep + kVPad;
   static constexpr size_t kVt = (size_t)kWaves * D * kVP * TR::kBytes;
   static constexpr size_t kObuf = (size_t)kWaves * 16 * D * sizeof(float);
-  static constexpr size_t kBytes = kVt > kObuf ? kVt : kObuf;
+  static constexpr size_t kMerge = 64 * 16 * 3 * sizeof(float);  // sparse merge: (m, l) + weights
+  static constexpr size_t kA = kVt > kObuf ? kVt : kObuf;
+  static constexpr size_t kBytes = kA > kMerge ? kA : kMerge;
 };
 
 template <typename TR, int D, bool FULL>
@@ -104,8 +116,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     idx_row = a.idx + ((int64_t)(b * a.Hkv + g) * a.NB + n) * a.k_top;
   } else {
     kind = 2;
-    t_begin = (split - a.nsg) * a.chunk;
-    t_end = min(t_begin + a.chunk, a.window);
+    t_begin = (split - a.nsg) * a.wchunk;
+    t_end = min(t_begin + a.wchunk, a.window);
     wbase = pos - a.window + 1;
   }
 
@@ -130,6 +142,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   int* kj = kj_s[wave];
   float* lg_row = nullptr;
   if (FULL && col < a.G) lg_row = a.logits + ((int64_t)b * a.Hq + g * a.G + col) * a.Tkv;
+  const bool lg_vec = (a.Tkv & 3) == 0;
 
   for (int t0 = t_begin + wave * kStep; t0 < t_end; t0 += kWaves * kStep) {
     wave_lds_sync();
@@ -175,13 +188,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     float mt = kNegInf;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
+      bool all_valid = true;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = kj[16 * kt + 4 * quad + r];
-        const float x = sacc[kt][r] * a.sl2;
-        s[kt][r] = (j >= 0) ? x : kNegInf;
-        if (FULL && lg_row != nullptr && j >= 0) lg_row[j] = x;
+        s[kt][r] = (j >= 0) ? sacc[kt][r] * a.sl2 : kNegInf;
+        all_valid = all_valid && (j >= 0);
         mt = fmaxf(mt, s[kt][r]);
+      }
+      if (FULL && lg_row != nullptr) {
+        // full layer: list entry t is key t, so the four keys are consecutive
+        const int j0 = t0 + 16 * kt + 4 * quad;
+        if (all_valid && lg_vec) {
+          *reinterpret_cast<float4*>(lg_row + j0) = make_float4(s[kt][0], s[kt][1], s[kt][2], s[kt][3]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (j0 + r < t_end) lg_row[j0 + r] = s[kt][r];
+        }
       }
     }
     mt = wave_max16x4(mt);
@@ -294,91 +318,151 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// Merge the partial states of splits [s0, s1) of one (unit, head): returns
-// the normalised output element d (0 when no key was valid) and the base-2
-// log-sum-exp.
-__device__ __forceinline__ float merge_splits(const float* po, const float* pml, int s0, int s1, int G,
-                                              int D, int h, int d, float* lse2_out) {
-  float M = kNegInf;
-  for (int s = s0; s < s1; ++s) M = fmaxf(M, pml[(s * G + h) * 2]);
-  const float mu = (M == kNegInf) ? 0.f : M;
-  float L = 0.f, acc = 0.f;
-  for (int s = s0; s < s1; ++s) {
-    const float w = exp2f(pml[(s * G + h) * 2] - mu);
-    L += pml[(s * G + h) * 2 + 1] * w;
-    acc += po[((int64_t)s * G + h) * D + d] * w;
-  }
-  if (lse2_out) *lse2_out = (L > 0.f) ? mu + log2f(L) : kNegInf;
-  return (L > 0.f) ? acc / L : 0.f;
-}
-
+// Sparse layer: merge the splits of one (unit, head) into its global and
+// window outputs and apply the sigmoid gate,
+//   out = g * o_global + (1 - g) * o_window,  g = 1 / (1 + exp(-w_h)).
+// One workgroup of D threads per (unit, head), one output element per thread.
 template <typename TR, int D>
-__global__ __launch_bounds__(D) void decode_full_reduce_kernel(const float* part_o, const float* part_ml, int nsplit,
-                                                               int G, int Hkv, void* out, float* lse,
-                                                               float* lse2) {
-  const int unit = blockIdx.x / G, h = blockIdx.x - (blockIdx.x / G) * G;
-  const int b = unit / Hkv, g = unit - b * Hkv;
-  const int Hq = Hkv * G, d = threadIdx.x;
-  const float* po = part_o + (int64_t)unit * nsplit * G * D;
-  const float* pml = part_ml + (int64_t)unit * nsplit * G * 2;
-  float l2;
-  const float o = merge_splits(po, pml, 0, nsplit, G, D, h, d, &l2);
-  const int hq = g * G + h;
-  reinterpret_cast<typename TR::storage*>(out)[((int64_t)b * Hq + hq) * D + d] = TR::from_float(o);
-  if (d == 0) {
-    lse2[(int64_t)b * Hq + hq] = l2;
-    if (lse) lse[(int64_t)b * Hq + hq] = l2 * kLn2;
+__global__ __launch_bounds__(D) void sparse_merge_kernel(DecodeArgs a) {
+  __shared__ float wts[kMaxSparseSplits];
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x / a.G, h = blockIdx.x - (blockIdx.x / a.G) * a.G;
+  const int i = unit % a.Tq, bg = unit / a.Tq;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const float* pml = a.part_ml + (int64_t)unit * a.nsplit * a.G * 2;
+  // weights: lanes 0..nsg-1 of wave 0 handle the global splits, the next
+  // lanes the window splits (nsplit <= 64)
+  if (tid < 64) {
+    const int sp = tid;
+    const bool in = sp < a.nsplit;
+    const bool win = sp >= a.nsg;
+    const float m = in ? pml[(sp * a.G + h) * 2] : kNegInf;
+    const float l = in ? pml[(sp * a.G + h) * 2 + 1] : 0.f;
+    // branch max and sum over the lanes of the same branch
+    float mg = (in && !win) ? m : kNegInf, mw = (in && win) ? m : kNegInf;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      mg = fmaxf(mg, __shfl_xor(mg, off));
+      mw = fmaxf(mw, __shfl_xor(mw, off));
+    }
+    const float mu = win ? (mw == kNegInf ? 0.f : mw) : (mg == kNegInf ? 0.f : mg);
+    const float w = in ? exp2f(m - mu) : 0.f;
+    float lg = (in && !win) ? l * w : 0.f, lw = (in && win) ? l * w : 0.f;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      lg += __shfl_xor(lg, off);
+      lw += __shfl_xor(lw, off);
+    }
+    const float gt = 1.f / (1.f + expf(-a.gate[g * a.G + h]));
+    const float L = win ? lw : lg;
+    const float scale = (L > 0.f) ? (win ? (1.f - gt) : gt) / L : 0.f;
+    if (in) wts[sp] = w * scale;
   }
+  __syncthreads();
+  const float* po = a.part_o + (int64_t)unit * a.nsplit * a.G * D + (int64_t)h * D + tid;
+  float acc = 0.f;
+#pragma unroll 4
+  for (int sp = 0; sp < a.nsplit; ++sp) acc += wts[sp] * po[(int64_t)sp * a.G * D];
+  reinterpret_cast<typename TR::storage*>(a.out)[(((int64_t)b * a.Tq + i) * a.Hq + g * a.G + h) * D + tid] =
+      TR::from_float(acc);
 }
 
-// S[b, g, 0, j] = sum over the group's heads of 2^(logit2 - lse2)
-__global__ __launch_bounds__(256) void decode_scores_kernel(const float* logits, const float* lse2, float* scores,
-                                                            int Hkv, int G, int Tkv, int nchunk) {
-  const int unit = blockIdx.x / nchunk, c = blockIdx.x - (blockIdx.x / nchunk) * nchunk;
-  const int b = unit / Hkv, g = unit - b * Hkv, Hq = Hkv * G;
-  const int j0 = c * kScoreChunk + 4 * threadIdx.x;
-  if (j0 >= Tkv) return;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  const bool vec = ((Tkv & 3) == 0) && (j0 + 3 < Tkv);
-  for (int h = 0; h < G; ++h) {
-    const int64_t hrow = (int64_t)b * Hq + g * G + h;
-    const float L = lse2[hrow];
-    const float* row = logits + hrow * Tkv;
+struct FinishArgs {
+  const float* part_o;
+  const float* part_ml;
+  const float* logits;
+  int nsplit, G, Hkv, Tkv, nchunk, units;
+  void* out;
+  float* lse;
+  float* scores;
+};
+
+// Base-2 log-sum-exp of every head of a unit from its split states, into
+// lse_s[0..G).  All 256 threads take part; the reduction order is fixed, so
+// every workgroup of the finish kernel computes bit-identical values.
+__device__ __forceinline__ void unit_lse2(const float* pml, int nsplit, int G, float* lse_s) {
+  // 16 threads per head, each over a strided subset of splits, then a
+  // 16-lane butterfly
+  const int tid = threadIdx.x, h = tid >> 4, t = tid & 15;
+  float M = kNegInf;
+  if (h < G)
+    for (int sp = t; sp < nsplit; sp += 16) M = fmaxf(M, pml[(sp * G + h) * 2]);
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
+  const float mu = (M == kNegInf) ? 0.f : M;
+  float L = 0.f;
+  if (h < G)
+    for (int sp = t; sp < nsplit; sp += 16) L += pml[(sp * G + h) * 2 + 1] * exp2f(pml[(sp * G + h) * 2] - mu);
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) L += __shfl_xor(L, off, 16);
+  if (h < G && t == 0) lse_s[h] = (L > 0.f) ? mu + log2f(L) : kNegInf;
+  __syncthreads();
+}
+
+// Blocks [0, units*G): output row of one (unit, head): O = sum_s 2^(m_s - lse2) O_s.
+// Blocks [units*G, ...): importance scores of one chunk of keys of a unit:
+//   S[b, g, 0, j] = sum over the group's heads of 2^(logit2[h, j] - lse2[h]).
+template <typename TR, int D>
+__global__ __launch_bounds__(256) void decode_full_finish_kernel(FinishArgs f) {
+  __shared__ float lse_s[16];
+  __shared__ float red[256 / D][D];
+  const int tid = threadIdx.x;
+  const int nrow = f.units * f.G;
+  const int Hq = f.Hkv * f.G;
+  if ((int)blockIdx.x < nrow) {
+    const int unit = blockIdx.x / f.G, h = blockIdx.x - (blockIdx.x / f.G) * f.G;
+    const int b = unit / f.Hkv, g = unit - b * f.Hkv;
+    const float* pml = f.part_ml + (int64_t)unit * f.nsplit * f.G * 2;
+    const float* po = f.part_o + (int64_t)unit * f.nsplit * f.G * D;
+    unit_lse2(pml, f.nsplit, f.G, lse_s);
+    const float l2 = lse_s[h];
+    constexpr int NS = 256 / D;  // split phases
+    const int d = tid % D, ph = tid / D;
+    float acc = 0.f;
+#pragma unroll 4
+    for (int sp = ph; sp < f.nsplit; sp += NS) acc += exp2f(pml[(sp * f.G + h) * 2] - l2) * po[((int64_t)sp * f.G + h) * D + d];
+    red[ph][d] = acc;
+    __syncthreads();
+    if (ph == 0) {
+      for (int x = 1; x < NS; ++x) acc += red[x][d];
+      const int hq = g * f.G + h;
+      reinterpret_cast<typename TR::storage*>(f.out)[((int64_t)b * Hq + hq) * D + d] = TR::from_float(acc);
+      if (d == 0 && f.lse) f.lse[(int64_t)b * Hq + hq] = l2 * kLn2;
+    }
+    return;
+  }
+  const int bid = blockIdx.x - nrow;
+  const int unit = bid / f.nchunk, c = bid - (bid / f.nchunk) * f.nchunk;
+  const int b = unit / f.Hkv, g = unit - b * f.Hkv;
+  unit_lse2(f.part_ml + (int64_t)unit * f.nsplit * f.G * 2, f.nsplit, f.G, lse_s);
+  float* srow = f.scores + (int64_t)unit * f.Tkv;
+  const bool vec_ok = (f.Tkv & 3) == 0;
+  for (int sub = 0; sub < kScoreChunk / 1024; ++sub) {
+    const int j0 = c * kScoreChunk + sub * 1024 + 4 * tid;
+    if (j0 >= f.Tkv) break;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    const bool vec = vec_ok && (j0 + 3 < f.Tkv);
+    for (int h = 0; h < f.G; ++h) {
+      const float L = lse_s[h];
+      const float* row = f.logits + ((int64_t)b * Hq + g * f.G + h) * f.Tkv;
+      if (vec) {
+        const float4 x = *reinterpret_cast<const float4*>(row + j0);
+        acc[0] += exp2f(x.x - L);
+        acc[1] += exp2f(x.y - L);
+        acc[2] += exp2f(x.z - L);
+        acc[3] += exp2f(x.w - L);
+      } else {
+        for (int e = 0; e < 4; ++e)
+          if (j0 + e < f.Tkv) acc[e] += exp2f(row[j0 + e] - L);
+      }
+    }
     if (vec) {
-      const float4 x = *reinterpret_cast<const float4*>(row + j0);
-      acc[0] += exp2f(x.x - L);
-      acc[1] += exp2f(x.y - L);
-      acc[2] += exp2f(x.z - L);
-      acc[3] += exp2f(x.w - L);
+      *reinterpret_cast<float4*>(srow + j0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     } else {
       for (int e = 0; e < 4; ++e)
-        if (j0 + e < Tkv) acc[e] += exp2f(row[j0 + e] - L);
+        if (j0 + e < f.Tkv) srow[j0 + e] = acc[e];
     }
   }
-  float* srow = scores + (int64_t)unit * Tkv;
-  if (vec) {
-    *reinterpret_cast<float4*>(srow + j0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  } else {
-    for (int e = 0; e < 4; ++e)
-      if (j0 + e < Tkv) srow[j0 + e] = acc[e];
-  }
-}
-
-template <typename TR, int D>
-__global__ __launch_bounds__(D) void decode_sparse_reduce_kernel(const float* part_o, const float* part_ml,
-                                                                 int nsplit, int nsg, int G, int Hkv, int Tq,
-                                                                 const float* gate, void* out) {
-  const int unit = blockIdx.x / G, h = blockIdx.x - (blockIdx.x / G) * G;
-  const int i = unit % Tq, bg = unit / Tq;
-  const int b = bg / Hkv, g = bg - b * Hkv;
-  const int Hq = Hkv * G, d = threadIdx.x;
-  const float* po = part_o + (int64_t)unit * nsplit * G * D;
-  const float* pml = part_ml + (int64_t)unit * nsplit * G * 2;
-  const float og = merge_splits(po, pml, 0, nsg, G, D, h, d, nullptr);
-  const float ol = merge_splits(po, pml, nsg, nsplit, G, D, h, d, nullptr);
-  const float gt = 1.f / (1.f + expf(-gate[g * G + h]));
-  const float y = gt * og + (1.f - gt) * ol;
-  reinterpret_cast<typename TR::storage*>(out)[(((int64_t)b * Tq + i) * Hq + g * G + h) * D + d] = TR::from_float(y);
 }
 
 DecodeArgs make_args(const Geom& g, const DecodePlan& p, const void* q, const void* k, const void* v) {
@@ -400,6 +484,7 @@ DecodeArgs make_args(const Geom& g, const DecodePlan& p, const void* q, const vo
   a.G = g.G;
   a.sl2 = g.scale * kLog2e;
   a.chunk = p.chunk;
+  a.wchunk = p.wchunk;
   a.nsplit = p.nsplit;
   a.nsg = p.nsg;
   return a;
@@ -439,27 +524,32 @@ DecodePlan plan_full_decode(const Geom& g) {
   int chunk = (g.Tkv + ns - 1) / ns;
   chunk = (chunk + quantum - 1) / quantum * quantum;
   p.chunk = chunk;
+  p.wchunk = 0;
   p.nsplit = (g.Tkv + chunk - 1) / chunk;
   p.nsg = p.nsplit;
   return p;
 }
 
 DecodePlan plan_sparse_rows(const Geom& g, int k_top, int window) {
+  // at most 48 global and 16 window splits (kMaxSparseSplits merge weights)
   DecodePlan p{};
+  const int quantum = kWaves * kStep;
   p.units = g.B * g.Hkv * g.Tq;
-  p.chunk = kWaves * kStep;
-  p.nsg = (k_top + p.chunk - 1) / p.chunk;
-  p.nsplit = p.nsg + (window + p.chunk - 1) / p.chunk;
+  int cg = (k_top + 47) / 48;
+  cg = (cg + quantum - 1) / quantum * quantum;
+  p.chunk = cg;
+  int cw = (window + 15) / 16;
+  cw = (cw + quantum - 1) / quantum * quantum;
+  p.wchunk = cw;
+  p.nsg = (k_top + cg - 1) / cg;
+  p.nsplit = p.nsg + (window + cw - 1) / cw;
   return p;
 }
 
 static size_t decode_ws(const Geom& g, const DecodePlan& p, bool full) {
   size_t n = align_up((size_t)p.units * p.nsplit * g.G * g.D * sizeof(float));
   n += align_up((size_t)p.units * p.nsplit * g.G * 2 * sizeof(float));
-  if (full) {
-    n += align_up((size_t)g.B * g.Hq * g.Tkv * sizeof(float));
-    n += align_up((size_t)g.B * g.Hq * sizeof(float));
-  }
+  if (full) n += align_up((size_t)g.B * g.Hq * g.Tkv * sizeof(float));
   return n;
 }
 
@@ -475,11 +565,7 @@ DecodeWs carve_decode_ws(const Geom& g, const DecodePlan& p, void* ws, bool full
   c += align_up((size_t)p.units * p.nsplit * g.G * g.D * sizeof(float));
   w.part_ml = reinterpret_cast<float*>(c);
   c += align_up((size_t)p.units * p.nsplit * g.G * 2 * sizeof(float));
-  if (full) {
-    w.logits = reinterpret_cast<float*>(c);
-    c += align_up((size_t)g.B * g.Hq * g.Tkv * sizeof(float));
-    w.lse2 = reinterpret_cast<float*>(c);
-  }
+  if (full) w.logits = reinterpret_cast<float*>(c);
   return w;
 }
 
@@ -491,13 +577,29 @@ hipError_t launch_full_decode(const Geom& g, const void* q, const void* k, const
   a.logits = w.logits;
   a.part_o = w.part_o;
   a.part_ml = w.part_ml;
-  const int nchunk = (g.Tkv + kScoreChunk - 1) / kScoreChunk;
+  FinishArgs f{};
+  f.part_o = w.part_o;
+  f.part_ml = w.part_ml;
+  f.logits = w.logits;
+  f.nsplit = p.nsplit;
+  f.G = g.G;
+  f.Hkv = g.Hkv;
+  f.Tkv = g.Tkv;
+  f.nchunk = (g.Tkv + kScoreChunk - 1) / kScoreChunk;
+  f.units = p.units;
+  f.out = out;
+  f.lse = lse;
+  f.scores = scores;
   HYS_DISPATCH(g, {
-    decode_split_kernel<TR, DD, true><<<p.units * p.nsplit, 256, 0, st>>>(a);
-    decode_full_reduce_kernel<TR, DD><<<p.units * g.G, DD, 0, st>>>(w.part_o, w.part_ml, p.nsplit, g.G, g.Hkv,
-                                                                     out, lse, w.lse2);
+    {
+      TraceScope ts(st, "full_decode_split");
+      decode_split_kernel<TR, DD, true><<<p.units * p.nsplit, 256, 0, st>>>(a);
+    }
+    {
+      TraceScope ts(st, "full_decode_finish");
+      decode_full_finish_kernel<TR, DD><<<p.units * (g.G + f.nchunk), 256, 0, st>>>(f);
+    }
   });
-  decode_scores_kernel<<<p.units * nchunk, 256, 0, st>>>(w.logits, w.lse2, scores, g.Hkv, g.G, g.Tkv, nchunk);
   return hipGetLastError();
 }
 
@@ -514,10 +616,17 @@ hipError_t launch_sparse_rows(const Geom& g, const void* q, const void* k, const
   a.window = window;
   a.part_o = w.part_o;
   a.part_ml = w.part_ml;
+  a.gate = gate;
+  a.out = out;
   HYS_DISPATCH(g, {
-    decode_split_kernel<TR, DD, false><<<p.units * p.nsplit, 256, 0, st>>>(a);
-    decode_sparse_reduce_kernel<TR, DD><<<p.units * g.G, DD, 0, st>>>(w.part_o, w.part_ml, p.nsplit, p.nsg, g.G,
-                                                                       g.Hkv, g.Tq, gate, out);
+    {
+      TraceScope ts(st, "sparse_decode");
+      decode_split_kernel<TR, DD, false><<<p.units * p.nsplit, 256, 0, st>>>(a);
+    }
+    {
+      TraceScope ts(st, "sparse_merge");
+      sparse_merge_kernel<TR, DD><<<p.units * g.G, DD, 0, st>>>(a);
+    }
   });
   return hipGetLastError();
 }

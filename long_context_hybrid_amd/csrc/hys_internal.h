@@ -47,12 +47,23 @@ __host__ __device__ inline int32_t valid_len_of(const ValidLen& v, int64_t row) 
 
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
+// Kernel-level event tracing (see hysparse_trace_begin): every launch site
+// wraps its kernel launch in a TraceScope.
+void trace_pre(hipStream_t st, const char* name);
+void trace_post(hipStream_t st);
+struct TraceScope {
+  hipStream_t st;
+  TraceScope(hipStream_t s, const char* name) : st(s) { trace_pre(s, name); }
+  ~TraceScope() { trace_post(st); }
+};
+
 // ---------------------------------------------------------------- decode path
 // Split-K attention of one query row per (batch, KV group) unit against a key
 // list (the whole cache for the full layer; idx + window for a sparse layer).
 struct DecodePlan {
   int units;     // full: B*Hkv ; sparse: B*Hkv*Tq
-  int chunk;     // keys per split
+  int chunk;     // keys per split (full layer; sparse global branch)
+  int wchunk;    // sparse: window keys per split
   int nsplit;    // splits per unit
   int nsg;       // sparse: global splits (the remaining ones cover the window)
 };
@@ -63,7 +74,6 @@ struct DecodeWs {
   float* part_o;   // [units, nsplit, G, D]
   float* part_ml;  // [units, nsplit, G, 2]
   float* logits;   // full only: [B, Hq, Tkv] base-2 scaled logits
-  float* lse2;     // full only: [B, Hq] base-2 log-sum-exp
 };
 size_t decode_full_ws_bytes(const Geom& g);
 size_t decode_sparse_ws_bytes(const Geom& g, int k_top, int window);

@@ -9,9 +9,18 @@
 
 #include "hys_internal.h"
 
+#include <vector>
+
 namespace {
 
 thread_local std::string g_err;
+
+// kernel-level event trace of the calling thread (profiling hook)
+thread_local hipEvent_t* t_events = nullptr;
+thread_local int32_t t_capacity = 0;
+thread_local int32_t t_count = 0;
+thread_local const char* t_current = "";
+thread_local std::vector<const char*> t_names;
 
 hys_status fail(hys_status s, const std::string& msg) {
   g_err = msg;
@@ -122,6 +131,20 @@ hipError_t run_sparse(const hys::Geom& g, const void* q, const void* k, const vo
 }
 
 }  // namespace
+
+namespace hys {
+void trace_pre(hipStream_t st, const char* name) {
+  t_current = name;
+  if (t_events && 2 * t_count + 1 < t_capacity) (void)hipEventRecord(t_events[2 * t_count], st);
+}
+void trace_post(hipStream_t st) {
+  if (t_events && 2 * t_count + 1 < t_capacity) {
+    (void)hipEventRecord(t_events[2 * t_count + 1], st);
+    t_names.push_back(t_current);
+    ++t_count;
+  }
+}
+}  // namespace hys
 
 extern "C" {
 
@@ -279,5 +302,22 @@ const char* hysparse_status_string(hys_status status) {
 const char* hysparse_last_error(void) { return g_err.c_str(); }
 
 int32_t hysparse_version(void) { return 100; }
+
+void hysparse_trace_begin(hipEvent_t* events, int32_t capacity) {
+  t_events = events;
+  t_capacity = events ? capacity : 0;
+  t_count = 0;
+  t_names.clear();
+}
+
+int32_t hysparse_trace_end(void) {
+  t_events = nullptr;
+  t_capacity = 0;
+  return t_count;
+}
+
+const char* hysparse_trace_name(int32_t i) {
+  return (i >= 0 && i < (int32_t)t_names.size()) ? t_names[i] : "";
+}
 
 }  // extern "C"

@@ -27,7 +27,8 @@ STATUS = {0: "HYS_OK", 1: "HYS_ERR_NULL_PTR", 2: "HYS_ERR_BAD_SHAPE", 3: "HYS_ER
 
 EXPORTS = ("hysparse_full_attn_scores", "hysparse_topk", "hysparse_sparse_attn", "hysparse_hybrid_block",
            "hysparse_workspace_bytes", "hysparse_topk_workspace_bytes", "hysparse_status_string",
-           "hysparse_last_error", "hysparse_version")
+           "hysparse_last_error", "hysparse_version", "hysparse_trace_begin", "hysparse_trace_end",
+           "hysparse_trace_name")
 
 
 class HysAttnDesc(ctypes.Structure):
@@ -73,6 +74,12 @@ def lib() -> ctypes.CDLL:
     L.hysparse_last_error.argtypes = []
     L.hysparse_last_error.restype = ctypes.c_char_p
     L.hysparse_version.restype = i32
+    L.hysparse_trace_begin.argtypes = [_P, i32]
+    L.hysparse_trace_begin.restype = None
+    L.hysparse_trace_end.argtypes = []
+    L.hysparse_trace_end.restype = i32
+    L.hysparse_trace_name.argtypes = [i32]
+    L.hysparse_trace_name.restype = ctypes.c_char_p
     _lib = L
     return L
 
@@ -227,3 +234,51 @@ def hysparse_hybrid_block(q_full, k, v, q_sparse: Sequence[torch.Tensor], gate_l
                                        os_arr, _ptr(lse), _ptr(scores), _ptr(idx), _ptr(ws),
                                        0 if ws is None else ws.numel(), _stream(dev)))
     return {"out_full": out_full, "out": list(out_sparse), "lse": lse, "scores": scores, "idx": idx}
+
+
+class KernelTrace:
+    """Per-kernel HIP-event timing through the library's trace hook.
+
+    Events are recorded by the library on the stream each kernel is launched
+    on, immediately before and after the kernel.  Usage::
+
+        tr = KernelTrace(capacity_kernels=4096)
+        tr.begin(); ...library calls...; rows = tr.end()   # [(name, ms), ...]
+    """
+
+    def __init__(self, capacity_kernels: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(_P)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _P, _P]
+        self._hip.hipEventSynchronize.argtypes = [_P]
+        self._hip.hipEventDestroy.argtypes = [_P]
+        self.capacity = 2 * int(capacity_kernels)
+        self.events = (_P * self.capacity)()
+        for i in range(self.capacity):
+            ev = _P()
+            if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events[i] = ev
+
+    def begin(self) -> None:
+        lib().hysparse_trace_begin(ctypes.cast(self.events, _P), self.capacity)
+
+    def end(self):
+        n = lib().hysparse_trace_end()
+        names = [lib().hysparse_trace_name(i).decode() for i in range(n)]
+        out = []
+        if n:
+            self._hip.hipEventSynchronize(self.events[2 * n - 1])
+        for i in range(n):
+            ms = ctypes.c_float()
+            if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.events[2 * i], self.events[2 * i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append((names[i], float(ms.value)))
+        return out
+
+    def __del__(self):
+        try:
+            for i in range(self.capacity):
+                self._hip.hipEventDestroy(self.events[i])
+        except Exception:
+            pass

@@ -94,9 +94,9 @@ def test_topk_validation():
     assert L.hysparse_topk(FAKE, 4, 100, 50, None, 8, FAKE, FAKE, 1 << 30, None) == 2    # stride < len
     assert L.hysparse_topk(FAKE, 4, 100, 102, None, 8, FAKE, FAKE, 1 << 30, None) == 4   # stride % 4
     assert L.hysparse_topk(None, 4, 100, 100, None, 8, FAKE, FAKE, 1 << 30, None) == 1
-    assert L.hysparse_topk(FAKE, 4, 100, 100, None, 8, FAKE, FAKE, 16, None) == 5       # workspace
     assert L.hysparse_topk(FAKE, 0, 100, 100, None, 8, FAKE, None, 0, None) == 0        # empty: no-op
-    assert L.hysparse_topk_workspace_bytes(16, 131072, 2048) > 16 * 4096 * 4
+    assert L.hysparse_topk_workspace_bytes(16, 131072, 2048) == 0                        # one workgroup per row
+    assert L.hysparse_topk_workspace_bytes(-1, 131072, 2048) == 0
 
 
 def test_sparse_and_hybrid_validation():
