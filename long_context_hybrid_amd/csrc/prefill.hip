@@ -1,20 +1,486 @@
-// Prefill kernels (placeholder until the MFMA prefill path lands).
-#include "hys_common.h"
+// Prefill path (q_len > 1) on gfx950 MFMA with LDS-staged 64-key tiles.
+//
+// Full layer, two sweeps (the importance score of a key needs each query's
+// final log-sum-exp before any probability can be summed):
+//   1. prefill_fwd:    causal flash attention per (KV group, query tile):
+//                      O and the base-2 log-sum-exp of every (query, head) row;
+//   2. prefill_scores: per (KV group, score block, key range): recompute the
+//                      logits, P = 2^(logit2 - lse2) exactly, and sum P over
+//                      the group's heads and the block's queries
+//                      (score_block 64) or over the heads only (score_block 1).
+// Sparse layer with 64-query score blocks (sparse_block): per (KV group,
+// block, row chunk) the window keys of the block and then its selected keys
+// are staged as 64-key tiles; each query row keeps a window state and a
+// global state (online softmax) and the epilogue applies the sigmoid gate.
+//
+// Pages: the HySparse abstract (the full layer selects tokens for the sparse
+// layers); the intelliparadigm article sections 2.2 and 3.1 (global branch on
+// the shared KV at the TopK indices, 128-token window branch, gated sum,
+// index sharing); the Baidu article's gather-then-attend pseudocode.
+#include "attn_tile.h"
 #include "hys_internal.h"
 
 namespace hys {
 
+namespace {
+
+constexpr int kNW = 8;   // waves per workgroup
+constexpr int kRTW = 2;  // row tiles (16 rows each) per wave
+constexpr int kNT = kNW * 64;
+constexpr int kRowsWG = kNW * kRTW * 16;  // 256 rows per workgroup
+constexpr int kSRTW = 1;  // sparse layer: row tiles per wave (two output states per row)
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t qs_b, qs_t, qs_h, ks_b, ks_t, ks_h;
+  int B, Tq, Tkv, Hq, Hkv, G;
+  float sl2;
+  int HW, QTW, NHC, nqt;  // heads and queries per workgroup, head chunks, query tiles
+  void* out;
+  float* lse;
+  float* lse2;            // [B, Hq, Tq] base-2
+  // scores
+  float* scores;          // [B, Hkv, NB, Tkv]
+  int SB, NB, nqb, nkr;   // score block, score blocks, query blocks of the kernel, key ranges
+  // sparse
+  const int32_t* idx;
+  int k_top, window;
+  const float* gate;
+  int nrc;                // row chunks per score block
+};
+
+template <typename TR, int D>
+__device__ __forceinline__ void load_q_frags(const PrefillArgs& a, int b, int i, int h, bool ok, int quad,
+                                             typename TR::frag (&qf)[D / 32]) {
+  const typename TR::storage* qrow =
+      (const typename TR::storage*)a.q + (int64_t)b * a.qs_b + (int64_t)i * a.qs_t + (int64_t)h * a.qs_h;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) qf[c] = ok ? TR::load8(qrow + 32 * c + 8 * quad) : TR::zero8();
+}
+
+// ------------------------------------------------------------- sweep 1: fwd
+template <typename TR, int D>
+__global__ __launch_bounds__(kNT) void prefill_fwd_kernel(PrefillArgs a) {
+  using ST = typename TR::storage;
+  using L = TileLayout<TR, D>;
+  constexpr int KC = D / 32, DT = D / 16;
+  __shared__ __align__(16) unsigned char sm[L::kBytes];
+  __shared__ int kj[kTK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, quad = lane >> 4;
+  const int per_qt = a.B * a.Hkv * a.NHC;
+  const int qt = a.nqt - 1 - (int)(blockIdx.x / per_qt);  // longest causal prefixes first
+  const int rest = blockIdx.x - (blockIdx.x / per_qt) * per_qt;
+  const int hc = rest % a.NHC, bg = rest / a.NHC;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int i0 = qt * a.QTW;
+
+  typename TR::frag qf[kRTW][KC];
+  int rpos[kRTW];
+#pragma unroll
+  for (int rt = 0; rt < kRTW; ++rt) {
+    const int rho = (wave * kRTW + rt) * 16 + col;
+    const int hl = rho / a.QTW, qi = rho - hl * a.QTW, i = i0 + qi;
+    const bool ok = hl < a.HW && i < a.Tq;
+    rpos[rt] = ok ? a.Tkv - a.Tq + i : -1;
+    load_q_frags<TR, D>(a, b, i, g * a.G + hc * a.HW + hl, ok, quad, qf[rt]);
+  }
+  const int last_i = min(i0 + a.QTW, a.Tq) - 1;
+  const int pos_max = a.Tkv - a.Tq + last_i;
+  const int nkt = pos_max / kTK + 1;
+  const ST* kbase = (const ST*)a.k + (int64_t)b * a.ks_b + (int64_t)g * a.ks_h;
+  const ST* vbase = (const ST*)a.v + (int64_t)b * a.ks_b + (int64_t)g * a.ks_h;
+  const int Tkv = a.Tkv;
+
+  TileStage<TR, D, kNT, true> stg;
+  stg.load(kbase, vbase, a.ks_t, [=](int t) { return t < Tkv ? t : -1; });
+  RowState<kRTW, D> st;
+  st.reset();
+  for (int it = 0; it < nkt; ++it) {
+    __syncthreads();
+    stg.store(sm, kj);
+    __syncthreads();
+    if (it + 1 < nkt) {
+      const int t0 = (it + 1) * kTK;
+      stg.load(kbase, vbase, a.ks_t, [=](int t) { return t0 + t < Tkv ? t0 + t : -1; });
+    }
+    attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, [&](int rt, int j) { return j <= rpos[rt]; });
+  }
+
+#pragma unroll
+  for (int rt = 0; rt < kRTW; ++rt) {
+    const float lt = wave_sum16x4(st.l[rt]);
+    {
+      const int rho = (wave * kRTW + rt) * 16 + col;
+      const int hl = rho / a.QTW, qi = rho - hl * a.QTW, i = i0 + qi;
+      if (quad == 0 && hl < a.HW && i < a.Tq) {
+        const int h = g * a.G + hc * a.HW + hl;
+        const float l2 = st.m[rt] + log2f(lt);
+        a.lse2[((int64_t)b * a.Hq + h) * a.Tq + i] = l2;
+        if (a.lse) a.lse[((int64_t)b * a.Hq + h) * a.Tq + i] = l2 * kLn2;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float lr = __shfl(lt, 4 * quad + r);
+      const int rho = (wave * kRTW + rt) * 16 + 4 * quad + r;
+      const int hl = rho / a.QTW, qi = rho - hl * a.QTW, i = i0 + qi;
+      if (hl < a.HW && i < a.Tq) {
+        const int h = g * a.G + hc * a.HW + hl;
+        const float inv = 1.f / lr;
+        ST* orow = (ST*)a.out + (((int64_t)b * a.Tq + i) * a.Hq + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) orow[16 * dt + col] = TR::from_float(st.o[rt][dt][r] * inv);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------- sweep 2: scores
+// SB = 64: rows of a workgroup = the block's 64 queries x G heads (row tile
+//          rt = head rt / 4, queries 16 * (rt % 4) ..); output one score row.
+// SB = 1 : rows = 16 queries x G heads (row tile rt = head rt); output 16 rows.
+// Key range of R keys per workgroup; S = Q . K^T in the 16x16 accumulator
+// layout gives each lane one key (l % 16) and four rows (4 * (l / 16) + r).
+template <typename TR, int D, int SB>
+__global__ __launch_bounds__(kNT) void prefill_scores_kernel(PrefillArgs a) {
+  using ST = typename TR::storage;
+  using L = TileLayout<TR, D>;
+  constexpr int KC = D / 32;
+  constexpr int QB = SB == 64 ? 64 : 16;
+  constexpr int R = SB == 64 ? 512 : 128;  // keys per workgroup
+  constexpr int NKT = R / kTK;
+  // per-wave partial sums (fixed-order reduction over the waves at the end):
+  //   SB = 64: [wave][R]      SB = 1: [wave][16 queries][R]
+  constexpr int RED = SB == 64 ? kNW * R : kNW * 16 * R;
+  __shared__ __align__(16) unsigned char sm[L::kKBytes];
+  __shared__ int kj[kTK];
+  __shared__ float red[RED];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, quad = lane >> 4;
+
+  const int kr = blockIdx.x % a.nkr;
+  const int rest = blockIdx.x / a.nkr;
+  const int per_q = a.B * a.Hkv;
+  const int qb = a.nqb - 1 - rest / per_q;
+  const int bg = rest - (rest / per_q) * per_q;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int i0 = qb * QB, i1 = min(i0 + QB, a.Tq);
+  const int pos_last = a.Tkv - a.Tq + i1 - 1;
+  const int r0 = kr * R;
+  const int RT = (QB / 16) * a.G;
+  const int npass = (RT + kNW * kRTW - 1) / (kNW * kRTW);
+
+  for (int x = tid; x < RED; x += kNT) red[x] = 0.f;
+
+  if (r0 <= pos_last) {
+    const int nkt = min(NKT, (pos_last - r0) / kTK + 1);
+    const ST* kbase = (const ST*)a.k + (int64_t)b * a.ks_b + (int64_t)g * a.ks_h;
+    const int Tkv = a.Tkv;
+    float* wred = red + (SB == 64 ? wave * R : wave * 16 * R);
+    for (int ps = 0; ps < npass; ++ps) {
+      typename TR::frag qf[kRTW][KC];
+      float lrow[kRTW][4];
+      int rowpos[kRTW][4];
+#pragma unroll
+      for (int x = 0; x < kRTW; ++x) {
+        const int rt = ps * kNW * kRTW + wave * kRTW + x;
+        const int hl = SB == 64 ? rt / 4 : rt;
+        const int qoff = SB == 64 ? 16 * (rt % 4) : 0;
+        {  // A-operand row (l % 16)
+          const int i = i0 + qoff + col;
+          const bool ok = rt < RT && i < a.Tq;
+          load_q_frags<TR, D>(a, b, i, g * a.G + hl, ok, quad, qf[x]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {  // accumulator rows 4 * quad + r
+          const int i = i0 + qoff + 4 * quad + r;
+          const bool ok = rt < RT && i < a.Tq;
+          rowpos[x][r] = ok ? a.Tkv - a.Tq + i : -1;
+          lrow[x][r] = ok ? a.lse2[((int64_t)b * a.Hq + g * a.G + hl) * a.Tq + i] : 0.f;
+        }
+      }
+      TileStage<TR, D, kNT, false> stg;
+      stg.load(kbase, kbase, a.ks_t, [=](int t) { return r0 + t < Tkv ? r0 + t : -1; });
+      for (int it = 0; it < nkt; ++it) {
+        __syncthreads();
+        stg.store(sm, kj);
+        __syncthreads();
+        if (it + 1 < nkt) {
+          const int t0 = r0 + (it + 1) * kTK;
+          stg.load(kbase, kbase, a.ks_t, [=](int t) { return t0 + t < Tkv ? t0 + t : -1; });
+        }
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          typename TR::frag kf[KC];
+#pragma unroll
+          for (int c = 0; c < KC; ++c) kf[c] = lds_k_frag<TR, D>(sm, ct, c, col, quad);
+          const int j = kj[16 * ct + col];
+          float pr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int x = 0; x < kRTW; ++x) {
+            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < KC; ++c) TR::mma(s, qf[x][c], kf[c]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              pr[r] += (j >= 0 && j <= rowpos[x][r]) ? exp2f(s[r] * a.sl2 - lrow[x][r]) : 0.f;
+          }
+          const int kc = it * kTK + 16 * ct + col;  // key within the range
+          if constexpr (SB == 64) {
+            const float v = wave_sum16x4(pr[0] + pr[1] + pr[2] + pr[3]);
+            if (quad == 0) wred[kc] += v;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wred[(4 * quad + r) * R + kc] += pr[r];
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  float* srow_base = a.scores + ((int64_t)(b * a.Hkv + g) * a.NB) * a.Tkv;
+  if constexpr (SB == 64) {
+    float* srow = srow_base + (int64_t)qb * a.Tkv;
+    for (int x = tid; x < R; x += kNT) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) v += red[w * R + x];
+      if (r0 + x < a.Tkv) srow[r0 + x] = v;
+    }
+  } else {
+    for (int x = tid; x < 16 * R; x += kNT) {
+      const int qi = x / R, jj = x - qi * R;
+      const int i = i0 + qi;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) v += red[w * 16 * R + x];
+      if (i < a.Tq && r0 + jj < a.Tkv) srow_base[(int64_t)i * a.Tkv + r0 + jj] = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------ sparse block
+template <typename TR, int D, int kRTW>
+__global__ __launch_bounds__(kNT) void sparse_block_kernel(PrefillArgs a) {
+  using ST = typename TR::storage;
+  using L = TileLayout<TR, D>;
+  constexpr int KC = D / 32, DT = D / 16;
+  __shared__ __align__(16) unsigned char sm[L::kBytes];
+  __shared__ int kj[kTK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, quad = lane >> 4;
+
+  // the row chunks of one block share their gathered rows: keep them on one
+  // XCD (blocks are dealt to the XCDs round-robin by workgroup id)
+  const int per_b = a.B * a.Hkv * a.NB;
+  int rc, unit;
+  {
+    const int w = blockIdx.x;
+    const int grp = w / (8 * a.nrc), inner = w - grp * (8 * a.nrc);
+    rc = inner / 8;
+    unit = grp * 8 + (inner - rc * 8);
+  }
+  if (unit >= per_b) return;
+  const int n = unit % a.NB, bg = unit / a.NB;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int i0 = n * 64, i1 = min(i0 + 64, a.Tq);
+  const int pos_first = a.Tkv - a.Tq + i0, pos_last = a.Tkv - a.Tq + i1 - 1;
+
+  typename TR::frag qf[kRTW][KC];
+  int rpos[kRTW];
+  float gt[kRTW];
+  bool tile_ok[kRTW];
+#pragma unroll
+  for (int x = 0; x < kRTW; ++x) {
+    const int rt = rc * (kNW * kRTW) + wave * kRTW + x;
+    const int hl = rt / 4, qoff = 16 * (rt % 4);
+    tile_ok[x] = hl < a.G;
+    const int i = i0 + qoff + col;
+    const bool ok = tile_ok[x] && i < a.Tq;
+    rpos[x] = ok ? a.Tkv - a.Tq + i : -1;
+    load_q_frags<TR, D>(a, b, i, g * a.G + hl, ok, quad, qf[x]);
+    gt[x] = tile_ok[x] ? 1.f / (1.f + expf(-a.gate[g * a.G + hl])) : 0.f;
+  }
+  const ST* kbase = (const ST*)a.k + (int64_t)b * a.ks_b + (int64_t)g * a.ks_h;
+  const ST* vbase = (const ST*)a.v + (int64_t)b * a.ks_b + (int64_t)g * a.ks_h;
+  const int W = a.window;
+  const int wlo = max(0, pos_first - W + 1);
+  const int nwt = (pos_last - wlo) / kTK + 1;
+  const int ngt = (a.k_top + kTK - 1) / kTK;
+  const int32_t* idx_row = a.idx + ((int64_t)(b * a.Hkv + g) * a.NB + n) * a.k_top;
+  const int ktop = a.k_top;
+  auto key_of = [=](int tile) {
+    return [=](int t) -> int {
+      if (tile < nwt) {
+        const int j = wlo + tile * kTK + t;
+        return j <= pos_last ? j : -1;
+      }
+      const int e = (tile - nwt) * kTK + t;
+      if (e >= ktop) return -1;
+      const int j = idx_row[e];
+      return (j >= 0 && j <= pos_last) ? j : -1;
+    };
+  };
+
+  TileStage<TR, D, kNT, true> stg;
+  stg.load(kbase, vbase, a.ks_t, key_of(0));
+  RowState<kRTW, D> st;
+  st.reset();
+  f32x4_t ol[kRTW][DT];  // (1 - g) * window output, rows 4 * quad + r
+  const int ntiles = nwt + ngt;
+  for (int it = 0; it < ntiles; ++it) {
+    __syncthreads();
+    stg.store(sm, kj);
+    const int any = __syncthreads_or(tid < kTK && stg.jk >= 0);
+    if (it + 1 < ntiles) stg.load(kbase, vbase, a.ks_t, key_of(it + 1));
+    if (any) {
+      if (it < nwt)
+        attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2,
+                                 [&](int rt, int j) { return j <= rpos[rt] && j > rpos[rt] - W; });
+      else
+        attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, [&](int rt, int j) { return j <= rpos[rt]; });
+    }
+    if (it == nwt - 1) {
+      // window branch done: keep (1 - g) * o_window, restart for the global branch
+#pragma unroll
+      for (int x = 0; x < kRTW; ++x) {
+        const float lt = wave_sum16x4(st.l[x]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float lr = __shfl(lt, 4 * quad + r);
+          const float sc = lr > 0.f ? (1.f - gt[x]) / lr : 0.f;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) ol[x][dt][r] = st.o[x][dt][r] * sc;
+        }
+      }
+      st.reset();
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < kRTW; ++x) {
+    const float lt = wave_sum16x4(st.l[x]);
+    const int rt = rc * (kNW * kRTW) + wave * kRTW + x;
+    const int hl = rt / 4, qoff = 16 * (rt % 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float lr = __shfl(lt, 4 * quad + r);
+      const int i = i0 + qoff + 4 * quad + r;
+      if (tile_ok[x] && i < a.Tq) {
+        const float sc = lr > 0.f ? gt[x] / lr : 0.f;
+        ST* orow = (ST*)a.out + (((int64_t)b * a.Tq + i) * a.Hq + g * a.G + hl) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) orow[16 * dt + col] = TR::from_float(st.o[x][dt][r] * sc + ol[x][dt][r]);
+      }
+    }
+  }
+}
+
+PrefillArgs base_args(const Geom& g, const void* q, const void* k, const void* v) {
+  PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.qs_b = g.qs_b;
+  a.qs_t = g.qs_t;
+  a.qs_h = g.qs_h;
+  a.ks_b = g.ks_b;
+  a.ks_t = g.ks_t;
+  a.ks_h = g.ks_h;
+  a.B = g.B;
+  a.Tq = g.Tq;
+  a.Tkv = g.Tkv;
+  a.Hq = g.Hq;
+  a.Hkv = g.Hkv;
+  a.G = g.G;
+  a.sl2 = g.scale * kLog2e;
+  return a;
+}
+
+#define HYS_PF_DISPATCH(g, ...)  \
+  do {                           \
+    if ((g).dtype == 1 && (g).D == 128) {                       \
+      using TR = BF16;                                          \
+      constexpr int DD = 128;                                   \
+      __VA_ARGS__;                                              \
+    } else if ((g).dtype == 1 && (g).D == 64) {                 \
+      using TR = BF16;                                          \
+      constexpr int DD = 64;                                    \
+      __VA_ARGS__;                                              \
+    } else if ((g).dtype == 0 && (g).D == 128) {                \
+      using TR = F32;                                           \
+      constexpr int DD = 128;                                   \
+      __VA_ARGS__;                                              \
+    } else {                                                    \
+      using TR = F32;                                           \
+      constexpr int DD = 64;                                    \
+      __VA_ARGS__;                                              \
+    }                                                           \
+  } while (0)
+
+}  // namespace
+
 size_t prefill_full_ws_bytes(const Geom& g, int /*score_block*/) {
   return align_up((size_t)g.B * g.Hq * g.Tq * sizeof(float));
 }
-hipError_t launch_full_prefill(const Geom&, const void*, const void*, const void*, int, void*, float*, float*, void*,
-                               hipStream_t) {
-  return hipErrorNotSupported;
+
+hipError_t launch_full_prefill(const Geom& g, const void* q, const void* k, const void* v, int score_block, void* out,
+                               float* lse, float* scores, void* ws, hipStream_t st) {
+  PrefillArgs a = base_args(g, q, k, v);
+  // heads per workgroup: the largest power of two dividing G (at most 16)
+  int hw = 1;
+  while (hw < 16 && g.G % (hw * 2) == 0) hw *= 2;
+  a.HW = hw;
+  a.QTW = kRowsWG / hw;
+  a.NHC = g.G / hw;
+  a.nqt = (g.Tq + a.QTW - 1) / a.QTW;
+  a.out = out;
+  a.lse = lse;
+  a.lse2 = static_cast<float*>(ws);
+  a.scores = scores;
+  a.SB = score_block;
+  a.NB = (g.Tq + score_block - 1) / score_block;
+  HYS_PF_DISPATCH(g, {
+    {
+      TraceScope ts(st, "full_prefill_fwd");
+      prefill_fwd_kernel<TR, DD><<<a.nqt * g.B * g.Hkv * a.NHC, kNT, 0, st>>>(a);
+    }
+    if (score_block == 64) {
+      a.nqb = a.NB;
+      a.nkr = (g.Tkv + 511) / 512;
+      TraceScope ts(st, "full_prefill_scores");
+      prefill_scores_kernel<TR, DD, 64><<<a.nqb * g.B * g.Hkv * a.nkr, kNT, 0, st>>>(a);
+    } else {
+      a.nqb = (g.Tq + 15) / 16;
+      a.nkr = (g.Tkv + 127) / 128;
+      TraceScope ts(st, "full_prefill_scores");
+      prefill_scores_kernel<TR, DD, 1><<<a.nqb * g.B * g.Hkv * a.nkr, kNT, 0, st>>>(a);
+    }
+  });
+  return hipGetLastError();
 }
+
 size_t sparse_block_ws_bytes(const Geom&, int, int) { return 0; }
-hipError_t launch_sparse_block(const Geom&, const void*, const void*, const void*, const int32_t*, int, int, int,
-                               const float*, void*, void*, hipStream_t) {
-  return hipErrorNotSupported;
+
+hipError_t launch_sparse_block(const Geom& g, const void* q, const void* k, const void* v, const int32_t* idx,
+                               int k_top, int score_block, int window, const float* gate, void* out, void* /*ws*/,
+                               hipStream_t st) {
+  (void)score_block;  // 64 (rows of one block share its index set)
+  PrefillArgs a = base_args(g, q, k, v);
+  a.NB = (g.Tq + 63) / 64;
+  a.idx = idx;
+  a.k_top = k_top;
+  a.window = window;
+  a.gate = gate;
+  a.out = out;
+  a.nrc = (4 * g.G + kNW * kSRTW - 1) / (kNW * kSRTW);
+  const int units = g.B * g.Hkv * a.NB;
+  const int grid = ((units + 7) / 8) * 8 * a.nrc;
+  HYS_PF_DISPATCH(g, {
+    TraceScope ts(st, "sparse_prefill");
+    sparse_block_kernel<TR, DD, kSRTW><<<grid, kNT, 0, st>>>(a);
+  });
+  return hipGetLastError();
 }
 
 }  // namespace hys

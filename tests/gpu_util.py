@@ -6,6 +6,8 @@ import sys
 import numpy as np
 import torch
 
+from oracle import hysparse_oracle as orc
+
 # Tolerances on attention outputs: the stated max-abs bounds plus a relative
 # l2 bound (outputs here are often ~1e-2, where max-abs alone would accept 0).
 TOL = {"bf16": dict(max_abs=2e-2, rel_l2=1e-2), "f32": dict(max_abs=1e-4, rel_l2=1e-5)}
@@ -61,3 +63,44 @@ def eps_valid(idx_row: np.ndarray, s_ref_row: np.ndarray, valid: int, eps_rel=S_
     lo = s[sel].min()
     hi = s[m].max()
     return lo >= hi - (eps_rel * abs(hi) + eps_abs)
+
+
+def _unit_mask(shape_btHd, units, Tq, Sb, G):
+    """Boolean mask over [B, Tq, Hq, D] selecting the rows of the listed (b, g, n) units."""
+    m = np.zeros(shape_btHd[:3], dtype=bool)
+    for (b, g, n) in units:
+        m[b, n * Sb:min((n + 1) * Sb, Tq), g * G:(g + 1) * G] = True
+    return m
+
+
+def check_hybrid(wl, inp, res, n_check_layers=None, blocks=None):
+    """End-to-end criteria: GPU scores within tolerance of the oracle's; GPU
+    indices equal the oracle's top-K of the GPU scores (bit-exact) and are
+    eps-valid against the oracle's scores; sparse outputs match the oracle
+    evaluated on the GPU's indices.  ``blocks`` restricts every check to the
+    listed (b, g, n) units (the oracle then computes only those)."""
+    Tq, Tkv, Sb, K = wl.q_len, wl.kv_len, wl.score_block, wl.k_top
+    O_ref, LSE_ref, S_ref = orc.full_layer(inp.q_full, inp.k, inp.v, Sb, blocks=blocks)
+    B, Hkv, NB, _ = S_ref.shape
+    units = blocks if blocks is not None else [(b, g, n) for b in range(B) for g in range(Hkv) for n in range(NB)]
+    rows = _unit_mask(O_ref.shape, units, Tq, Sb, wl.group) if blocks is not None else None
+    assert_attn_close(res["out_full"], O_ref, wl.dtype, "O_full", mask=rows)
+    S_gpu = host(res["scores"]).astype(np.float32)
+    sel = tuple(np.array(units).T)
+    assert_scores_close(torch.from_numpy(S_gpu[sel]), S_ref[sel])
+    idx_gpu = host(res["idx"])
+    idx_from_gpu_S = orc.select_indices(S_gpu, Tq, Tkv, Sb, K, blocks=units)
+    np.testing.assert_array_equal(idx_gpu[sel], idx_from_gpu_S[sel])
+    idx_ref = orc.select_indices(S_ref, Tq, Tkv, Sb, K, blocks=units)
+    differ = 0
+    for (b, g, n) in units:
+        c = orc.candidate_count(n, Tq, Tkv, Sb)
+        assert eps_valid(idx_gpu[b, g, n], S_ref[b, g, n], c)
+        differ += int(not np.array_equal(idx_gpu[b, g, n], idx_ref[b, g, n]))
+    say(f"  index rows differing from the oracle's own selection: {differ}/{len(units)}")
+    layers = range(len(inp.q_sparse)) if n_check_layers is None else range(n_check_layers)
+    for l in layers:
+        ref = orc.sparse_layer(inp.q_sparse[l], inp.k, inp.v, idx_gpu, Sb, wl.window, inp.gate_logits[l],
+                               blocks=blocks)
+        assert_attn_close(res["out"][l], ref, wl.dtype, f"sparse layer {l}", mask=rows)
+    return S_ref, idx_gpu

@@ -10,7 +10,7 @@ import torch
 from long_context_hybrid_amd import hysparse as hy
 from long_context_hybrid_amd import inputs as gen
 from oracle import hysparse_oracle as orc
-from tests.gpu_util import (assert_attn_close, assert_scores_close, dev_tensor, eps_valid, host, say)
+from tests.gpu_util import (assert_attn_close, assert_scores_close, check_hybrid, dev_tensor, host, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -117,36 +117,6 @@ def test_sparse_decode_on_oracle_indices(name):
 
 
 # ----------------------------------------------------------- hybrid block e2e
-
-def check_hybrid(wl, inp, res, n_check_layers=None):
-    """End-to-end criteria: GPU scores within tolerance of the oracle's; GPU
-    indices equal the oracle's top-K of the GPU scores (bit-exact) and are
-    eps-valid against the oracle's scores; sparse outputs match the oracle
-    evaluated on the GPU's indices."""
-    O_ref, LSE_ref, S_ref = orc.full_layer(inp.q_full, inp.k, inp.v, wl.score_block)
-    assert_attn_close(res["out_full"], O_ref, wl.dtype, "O_full")
-    assert_scores_close(res["scores"], S_ref)
-    S_gpu = host(res["scores"]).astype(np.float32)
-    idx_gpu = host(res["idx"])
-    idx_from_gpu_S = orc.select_indices(S_gpu, wl.q_len, wl.kv_len, wl.score_block, wl.k_top)
-    np.testing.assert_array_equal(idx_gpu, idx_from_gpu_S)
-    idx_ref = orc.select_indices(S_ref, wl.q_len, wl.kv_len, wl.score_block, wl.k_top)
-    B, Hkv, NB, _ = S_ref.shape
-    differ = 0
-    for b in range(B):
-        for g in range(Hkv):
-            for n in range(NB):
-                c = orc.candidate_count(n, wl.q_len, wl.kv_len, wl.score_block)
-                assert eps_valid(idx_gpu[b, g, n], S_ref[b, g, n], c)
-                differ += int(not np.array_equal(idx_gpu[b, g, n], idx_ref[b, g, n]))
-    say(f"  index rows differing from the oracle's own selection: {differ}/{B * Hkv * NB}")
-    layers = range(len(inp.q_sparse)) if n_check_layers is None else range(n_check_layers)
-    for l in layers:
-        ref = orc.sparse_layer(inp.q_sparse[l], inp.k, inp.v, idx_gpu, wl.score_block, wl.window,
-                               inp.gate_logits[l])
-        assert_attn_close(res["out"][l], ref, wl.dtype, f"sparse layer {l}")
-    return S_ref, idx_gpu
-
 
 @pytest.mark.parametrize("name", list(DECODE_CASES))
 def test_hybrid_block_decode(name):
