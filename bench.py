@@ -27,6 +27,7 @@ import numpy as np
 METRIC = "sparse-layer decode tokens/s + HBM GB/s (% roofline) at 128K ctx, K=2048"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
 
 
 def parse():
@@ -57,6 +58,32 @@ def sparse_layer_bytes(wl, idx_np):
         rows += nsel + nwin
     q_out = 2 * wl.batch * Tq * wl.n_q_heads * wl.head_dim * e
     return 2 * rows * row + q_out + idx_np.size * 4
+
+
+def full_layer_flops(wl):
+    """Algorithmic FLOPs of the causal full layer: QK^T and PV over every
+    (query, head, key <= position) triple, 2 FLOPs per multiply-add."""
+    Tq, Tkv = wl.q_len, wl.kv_len
+    pairs = Tq * (Tkv - Tq) + Tq * (Tq + 1) // 2
+    return 4 * wl.head_dim * wl.batch * wl.n_q_heads * pairs
+
+
+def sparse_layer_flops(wl, idx_np):
+    """Algorithmic FLOPs of one sparse layer: QK^T and PV over each query
+    head's global keys (selected, <= position) and window keys."""
+    B, Hkv, NB, K = idx_np.shape
+    Tq, Tkv, Sb, W = wl.q_len, wl.kv_len, wl.score_block, wl.window
+    pos = Tkv - Tq + np.arange(Tq)
+    total = 0
+    for n in range(NB):
+        i0, i1 = n * Sb, min((n + 1) * Sb, Tq)
+        p = pos[i0:i1]
+        rows = np.sort(np.where(idx_np[:, :, n] >= 0, idx_np[:, :, n], np.iinfo(np.int32).max), axis=-1)
+        rows = rows.reshape(-1, K)
+        glob = sum(int(np.searchsorted(r, p, side="right").sum()) for r in rows)
+        win = int(np.minimum(W, p + 1).sum()) * B * Hkv
+        total += glob + win
+    return 4 * wl.head_dim * wl.group * total
 
 
 def full_split_bytes(wl):
@@ -182,16 +209,47 @@ def main():
         return {"kernel": name, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": gbs / HBM_PEAK_GBS, "traffic": None, "alg_bytes_per_launch": alg_bytes, "avg_us": us}
 
+    mfma_peak = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+
+    def roof_flops(name, flops):
+        if name not in kernels:
+            return None
+        us = kernels[name]["avg_us"]
+        tf = flops / (us * 1e-6) / 1e12
+        return {"kernel": name, "bound": "mfma", "achieved": tf, "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": tf / mfma_peak, "traffic": None, "alg_flops_per_launch": flops, "avg_us": us}
+
+    dom = max(kernels, key=lambda n: kernels[n]["us_per_step"])
+    result["dominant_kernel"] = dom
     if Tq == 1:
-        dom = max(kernels, key=lambda n: kernels[n]["us_per_step"])
-        result["roofline"] = roof("full_decode_split", full_split_bytes(wl)) if dom == "full_decode_split" else None
         sb = sparse_layer_bytes(wl, idx_np)
+        rf = roof("full_decode_split", full_split_bytes(wl))
         rs = roof("sparse_decode", sb)
+        result["roofline"] = rf if dom == "full_decode_split" else (rs if dom == "sparse_decode" else rf)
+        result["roofline_full"] = rf
         result["roofline_sparse"] = rs
         if rs:
-            result["sparse_layer"] = {"tokens_per_s": tokens_per_step / (rs["avg_us"] * 1e-6),
-                                      "us_per_layer": rs["avg_us"], "GB_per_s": rs["achieved"],
-                                      "frac_hbm": rs["frac"], "alg_bytes": sb}
+            layer_us = rs["avg_us"] + kernels.get("sparse_merge", {"avg_us": 0.0})["avg_us"]
+            result["sparse_layer"] = {"tokens_per_s": tokens_per_step / (layer_us * 1e-6), "us_per_layer": layer_us,
+                                      "GB_per_s": sb / (layer_us * 1e-6) / 1e9,
+                                      "frac_hbm": sb / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "alg_bytes": sb,
+                                      "split_kernel_us": rs["avg_us"]}
+    else:
+        ff = full_layer_flops(wl)
+        rf = roof_flops("full_prefill_fwd", ff)
+        rsc = roof_flops("full_prefill_scores", ff // 2)
+        sf = sparse_layer_flops(wl, idx_np)
+        rsp = roof_flops("sparse_prefill", sf)
+        by = {"full_prefill_fwd": rf, "full_prefill_scores": rsc, "sparse_prefill": rsp}
+        result["roofline"] = by.get(dom) or rf
+        result["roofline_full_fwd"] = rf
+        result["roofline_full_scores"] = rsc
+        result["roofline_sparse"] = rsp
+        if rf and rsc:
+            t_full = (rf["avg_us"] + rsc["avg_us"]) * 1e-6
+            result["full_layer"] = {"tflops_algorithmic": ff / t_full / 1e12, "frac_peak": ff / t_full / 1e12 / mfma_peak,
+                                    "us": t_full * 1e6, "alg_flops": ff,
+                                    "note": "two sweeps: the score sweep recomputes QK^T after the final LSE"}
     result["kernels"] = kernels
     result["traced_ms_per_step"] = traced_ms
     result["input_sha256"] = inp.sha256()
