@@ -36,7 +36,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kStep = 32;  // keys per wave step
 constexpr int kVPad = 4;   // extra key slots per transposed-V row (bank spread)
-constexpr int kScoreChunk = 4096;  // keys per score workgroup (multiple of 1024)
+constexpr int kScoreChunk = 1024;  // keys per score workgroup (multiple of 1024)
 
 
 struct DecodeArgs {
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int DT = D / 16;            // 16-column output tiles
 
   __shared__ __align__(16) unsigned char smem[DecodeSmem<TR, D>::kBytes];
-  __shared__ int kj_s[kWaves][kStep];
+  __shared__ int kj_s[kWaves][2 * kStep];
   __shared__ float ml_s[kWaves][16][2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -144,45 +144,70 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   if (FULL && col < a.G) lg_row = a.logits + ((int64_t)b * a.Hq + g * a.G + col) * a.Tkv;
   const bool lg_vec = (a.Tkv & 3) == 0;
 
-  for (int t0 = t_begin + wave * kStep; t0 < t_end; t0 += kWaves * kStep) {
-    wave_lds_sync();
-    if (lane < kStep) {
-      const int t = t0 + lane;
-      int j = -1;
-      if (t < t_end) j = (kind == 0) ? t : (kind == 1 ? idx_row[t] : wbase + t);
-      kj[lane] = (j >= 0 && j <= pos) ? j : -1;
-    }
-    wave_lds_sync();
-
-    // A operand: K rows of list entries t0 + 16*kt + col
-    frag kf[2][KC];
+  // key index of list entry t (-1: past the list, negative index or after pos)
+  auto key_at = [&](int t) -> int {
+    int j = -1;
+    if (t < t_end) j = (kind == 0) ? t : (kind == 1 ? idx_row[t] : wbase + t);
+    return (j >= 0 && j <= pos) ? j : -1;
+  };
+  // issue the K and V row loads of one step whose key indices are in kjb
+  frag kf[2][KC];
+  uint4 vr[NP][4];
+  auto issue_loads = [&](const int* kjb) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int j = kj[16 * kt + col];
+      const int j = kjb[16 * kt + col];
       const ST* kr = kbase + (int64_t)(j >= 0 ? j : 0) * a.ks_t;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) kf[kt][c] = TR::load8(kr + 32 * c + 8 * quad);
+      for (int c = 0; c < KC; ++c) kf[kt][c] = TR::template load8_stream<FULL>(kr + 32 * c + 8 * quad);
     }
-    // V rows: lane owns (chunk tc, key quad kq) pairs, four rows each
-    uint4 vr[NP][4];
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) {
       const int pidx = lane + 64 * pp;
       const int tc = pidx % CPR, kq = pidx / CPR;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = kj[4 * kq + r];
-        vr[pp][r] = *reinterpret_cast<const uint4*>(vbase + (int64_t)(j >= 0 ? j : 0) * a.ks_t + tc * EPC);
+        const int j = kjb[4 * kq + r];
+        vr[pp][r] = load16_stream<FULL>(vbase + (int64_t)(j >= 0 ? j : 0) * a.ks_t + tc * EPC);
       }
     }
+  };
 
+  // software pipeline: the next step's loads are in flight while this step computes
+  int buf = 0;
+  if (t_begin + wave * kStep < t_end) {
+    if (lane < kStep) kj[lane] = key_at(t_begin + wave * kStep + lane);
+    wave_lds_sync();
+    issue_loads(kj);
+  }
+  for (int t0 = t_begin + wave * kStep; t0 < t_end; t0 += kWaves * kStep) {
+    wave_lds_sync();
+    frag kfc[2][KC];
+    uint4 vrc[NP][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) kfc[kt][c] = kf[kt][c];
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vrc[pp][r] = vr[pp][r];
+    const int* kjc = kj + buf * kStep;
+    const int t1 = t0 + kWaves * kStep;
+    if (t1 < t_end) {
+      int* kjn = kj + (buf ^ 1) * kStep;
+      if (lane < kStep) kjn[lane] = key_at(t1 + lane);
+      wave_lds_sync();
+      issue_loads(kjn);
+    }
+    buf ^= 1;
     // S^T = K . Q^T ; sacc[kt][r] = logit of key 16*kt + 4*quad + r for head col
     f32x4_t sacc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       sacc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < KC; ++c) TR::mma(sacc[kt], kf[kt][c], qf[c]);
+      for (int c = 0; c < KC; ++c) TR::mma(sacc[kt], kfc[kt][c], qf[c]);
     }
     float s[2][4];
     float mt = kNegInf;
@@ -191,7 +216,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       bool all_valid = true;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = kj[16 * kt + 4 * quad + r];
+        const int j = kjc[16 * kt + 4 * quad + r];
         s[kt][r] = (j >= 0) ? sacc[kt][r] * a.sl2 : kNegInf;
         all_valid = all_valid && (j >= 0);
         mt = fmaxf(mt, s[kt][r]);
@@ -240,20 +265,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       for (int e = 0; e < EPC; ++e) {
         ST* dst = vt + (tc * EPC + e) * VP + 4 * kq;
         if constexpr (TR::kBytes == 2) {
-          const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vr[pp][0]);
-          const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[pp][1]);
-          const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vr[pp][2]);
-          const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vr[pp][3]);
+          const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vrc[pp][0]);
+          const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vrc[pp][1]);
+          const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vrc[pp][2]);
+          const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vrc[pp][3]);
           const int sh = 16 * (e & 1);
           uint2 pk;
           pk.x = ((w0[e >> 1] >> sh) & 0xFFFFu) | (((w1[e >> 1] >> sh) & 0xFFFFu) << 16);
           pk.y = ((w2[e >> 1] >> sh) & 0xFFFFu) | (((w3[e >> 1] >> sh) & 0xFFFFu) << 16);
           *reinterpret_cast<uint2*>(dst) = pk;
         } else {
-          const float* f0 = reinterpret_cast<const float*>(&vr[pp][0]);
-          const float* f1 = reinterpret_cast<const float*>(&vr[pp][1]);
-          const float* f2 = reinterpret_cast<const float*>(&vr[pp][2]);
-          const float* f3 = reinterpret_cast<const float*>(&vr[pp][3]);
+          const float* f0 = reinterpret_cast<const float*>(&vrc[pp][0]);
+          const float* f1 = reinterpret_cast<const float*>(&vrc[pp][1]);
+          const float* f2 = reinterpret_cast<const float*>(&vrc[pp][2]);
+          const float* f3 = reinterpret_cast<const float*>(&vrc[pp][3]);
           *reinterpret_cast<float4*>(dst) = make_float4(f0[e], f1[e], f2[e], f3[e]);
         }
       }
@@ -442,18 +467,27 @@ __global__ __launch_bounds__(256) void decode_full_finish_kernel(FinishArgs f) {
     if (j0 >= f.Tkv) break;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     const bool vec = vec_ok && (j0 + 3 < f.Tkv);
-    for (int h = 0; h < f.G; ++h) {
-      const float L = lse_s[h];
-      const float* row = f.logits + ((int64_t)b * Hq + g * f.G + h) * f.Tkv;
-      if (vec) {
-        const float4 x = *reinterpret_cast<const float4*>(row + j0);
-        acc[0] += exp2f(x.x - L);
-        acc[1] += exp2f(x.y - L);
-        acc[2] += exp2f(x.z - L);
-        acc[3] += exp2f(x.w - L);
-      } else {
+    const float* row0 = f.logits + ((int64_t)b * Hq + g * f.G) * f.Tkv;
+    if (vec) {
+      // all the group's rows in flight at once, then the exponentials
+      float4 x[16];
+#pragma unroll
+      for (int h = 0; h < 16; ++h)
+        if (h < f.G) x[h] = *reinterpret_cast<const float4*>(row0 + (int64_t)h * f.Tkv + j0);
+#pragma unroll
+      for (int h = 0; h < 16; ++h)
+        if (h < f.G) {
+          const float L = lse_s[h];
+          acc[0] += exp2f(x[h].x - L);
+          acc[1] += exp2f(x[h].y - L);
+          acc[2] += exp2f(x[h].z - L);
+          acc[3] += exp2f(x[h].w - L);
+        }
+    } else {
+      for (int h = 0; h < f.G; ++h) {
+        const float L = lse_s[h];
         for (int e = 0; e < 4; ++e)
-          if (j0 + e < f.Tkv) acc[e] += exp2f(row[j0 + e] - L);
+          if (j0 + e < f.Tkv) acc[e] += exp2f(row0[(int64_t)h * f.Tkv + j0 + e] - L);
       }
     }
     if (vec) {

@@ -32,6 +32,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load; NT = true marks it non-temporal (streamed once, not worth
+// keeping in the caches: the full layer's pass over the whole cache).
+template <bool NT>
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  if constexpr (NT) {
+    const u32x4_t u = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(u[0], u[1], u[2], u[3]);
+  } else {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+}
+
 struct BF16 {
   using storage = uint16_t;
   using frag = bf16x8_t;
@@ -40,6 +54,10 @@ struct BF16 {
   __device__ static __forceinline__ frag load8(const storage* p) {
     uint4 u = *reinterpret_cast<const uint4*>(p);
     return __builtin_bit_cast(frag, u);
+  }
+  template <bool NT>
+  __device__ static __forceinline__ frag load8_stream(const storage* p) {
+    return __builtin_bit_cast(frag, load16_stream<NT>(p));
   }
   __device__ static __forceinline__ frag zero8() { return __builtin_bit_cast(frag, make_uint4(0, 0, 0, 0)); }
   __device__ static __forceinline__ void mma(f32x4_t& acc, const frag& a, const frag& b) {
@@ -73,6 +91,14 @@ struct F32 {
     frag f;
     f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
     f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    return f;
+  }
+  template <bool NT>
+  __device__ static __forceinline__ frag load8_stream(const storage* p) {
+    const uint4 a = load16_stream<NT>(p), b = load16_stream<NT>(p + 4);
+    frag f;
+    f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y); f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
+    f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y); f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
     return f;
   }
   __device__ static __forceinline__ frag zero8() {

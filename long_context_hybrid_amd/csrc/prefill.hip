@@ -24,11 +24,13 @@ namespace hys {
 
 namespace {
 
-constexpr int kNW = 8;   // waves per workgroup
-constexpr int kRTW = 2;  // row tiles (16 rows each) per wave
-constexpr int kNT = kNW * 64;
-constexpr int kRowsWG = kNW * kRTW * 16;  // 256 rows per workgroup
-constexpr int kSRTW = 1;  // sparse layer: row tiles per wave (two output states per row)
+// Launch shapes (waves per workgroup NW x row tiles per wave RTW; 16 rows per
+// row tile).  Measured on MI355X: 8 waves x 2 row tiles (2 waves per SIMD)
+// beat 4 x 4 (1 wave per SIMD, half the LDS reads per MFMA) by 1.5x; the
+// second wave per SIMD hides the tile loads and the softmax.
+constexpr int kFwdNW = 8, kFwdRTW = 2;      // full layer, forward sweep
+constexpr int kScNW = 8, kScRTW = 2;        // full layer, score sweep
+constexpr int kSpNW = 8, kSpRTW = 1;        // sparse layer (two output states per row)
 
 struct PrefillArgs {
   const void* q;
@@ -61,8 +63,9 @@ __device__ __forceinline__ void load_q_frags(const PrefillArgs& a, int b, int i,
 }
 
 // ------------------------------------------------------------- sweep 1: fwd
-template <typename TR, int D>
-__global__ __launch_bounds__(kNT) void prefill_fwd_kernel(PrefillArgs a) {
+template <typename TR, int D, int kNW, int kRTW>
+__global__ __launch_bounds__(kNW * 64) void prefill_fwd_kernel(PrefillArgs a) {
+  constexpr int kNT = kNW * 64;
   using ST = typename TR::storage;
   using L = TileLayout<TR, D>;
   constexpr int KC = D / 32, DT = D / 16;
@@ -143,8 +146,9 @@ __global__ __launch_bounds__(kNT) void prefill_fwd_kernel(PrefillArgs a) {
 // SB = 1 : rows = 16 queries x G heads (row tile rt = head rt); output 16 rows.
 // Key range of R keys per workgroup; S = Q . K^T in the 16x16 accumulator
 // layout gives each lane one key (l % 16) and four rows (4 * (l / 16) + r).
-template <typename TR, int D, int SB>
-__global__ __launch_bounds__(kNT) void prefill_scores_kernel(PrefillArgs a) {
+template <typename TR, int D, int SB, int kNW, int kRTW>
+__global__ __launch_bounds__(kNW * 64) void prefill_scores_kernel(PrefillArgs a) {
+  constexpr int kNT = kNW * 64;
   using ST = typename TR::storage;
   using L = TileLayout<TR, D>;
   constexpr int KC = D / 32;
@@ -262,8 +266,9 @@ __global__ __launch_bounds__(kNT) void prefill_scores_kernel(PrefillArgs a) {
 }
 
 // ------------------------------------------------------------ sparse block
-template <typename TR, int D, int kRTW>
-__global__ __launch_bounds__(kNT) void sparse_block_kernel(PrefillArgs a) {
+template <typename TR, int D, int kNW, int kRTW>
+__global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
+  constexpr int kNT = kNW * 64;
   using ST = typename TR::storage;
   using L = TileLayout<TR, D>;
   constexpr int KC = D / 32, DT = D / 16;
@@ -428,8 +433,9 @@ hipError_t launch_full_prefill(const Geom& g, const void* q, const void* k, cons
                                float* lse, float* scores, void* ws, hipStream_t st) {
   PrefillArgs a = base_args(g, q, k, v);
   // heads per workgroup: the largest power of two dividing G (at most 16)
+  constexpr int kRowsWG = kFwdNW * kFwdRTW * 16;
   int hw = 1;
-  while (hw < 16 && g.G % (hw * 2) == 0) hw *= 2;
+  while (hw < 16 && g.G % (hw * 2) == 0 && kRowsWG / (hw * 2) >= 16) hw *= 2;
   a.HW = hw;
   a.QTW = kRowsWG / hw;
   a.NHC = g.G / hw;
@@ -443,18 +449,18 @@ hipError_t launch_full_prefill(const Geom& g, const void* q, const void* k, cons
   HYS_PF_DISPATCH(g, {
     {
       TraceScope ts(st, "full_prefill_fwd");
-      prefill_fwd_kernel<TR, DD><<<a.nqt * g.B * g.Hkv * a.NHC, kNT, 0, st>>>(a);
+      prefill_fwd_kernel<TR, DD, kFwdNW, kFwdRTW><<<a.nqt * g.B * g.Hkv * a.NHC, kFwdNW * 64, 0, st>>>(a);
     }
     if (score_block == 64) {
       a.nqb = a.NB;
       a.nkr = (g.Tkv + 511) / 512;
       TraceScope ts(st, "full_prefill_scores");
-      prefill_scores_kernel<TR, DD, 64><<<a.nqb * g.B * g.Hkv * a.nkr, kNT, 0, st>>>(a);
+      prefill_scores_kernel<TR, DD, 64, kScNW, kScRTW><<<a.nqb * g.B * g.Hkv * a.nkr, kScNW * 64, 0, st>>>(a);
     } else {
       a.nqb = (g.Tq + 15) / 16;
       a.nkr = (g.Tkv + 127) / 128;
       TraceScope ts(st, "full_prefill_scores");
-      prefill_scores_kernel<TR, DD, 1><<<a.nqb * g.B * g.Hkv * a.nkr, kNT, 0, st>>>(a);
+      prefill_scores_kernel<TR, DD, 1, kScNW, kScRTW><<<a.nqb * g.B * g.Hkv * a.nkr, kScNW * 64, 0, st>>>(a);
     }
   });
   return hipGetLastError();
@@ -473,12 +479,12 @@ hipError_t launch_sparse_block(const Geom& g, const void* q, const void* k, cons
   a.window = window;
   a.gate = gate;
   a.out = out;
-  a.nrc = (4 * g.G + kNW * kSRTW - 1) / (kNW * kSRTW);
+  a.nrc = (4 * g.G + kSpNW * kSpRTW - 1) / (kSpNW * kSpRTW);
   const int units = g.B * g.Hkv * a.NB;
   const int grid = ((units + 7) / 8) * 8 * a.nrc;
   HYS_PF_DISPATCH(g, {
     TraceScope ts(st, "sparse_prefill");
-    sparse_block_kernel<TR, DD, kSRTW><<<grid, kNT, 0, st>>>(a);
+    sparse_block_kernel<TR, DD, kSpNW, kSpRTW><<<grid, kSpNW * 64, 0, st>>>(a);
   });
   return hipGetLastError();
 }
