@@ -38,7 +38,51 @@ def parse():
     ap.add_argument("--workload", default="decode128k", choices=["decode128k", "decode8k", "prefill32k", "tiny"])
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 times): the reference for HBM counters")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic.json")
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the HIP source that defines a kernel (traffic figures are only
+    reported while the kernel is unchanged since its counters were taken)."""
+    import hashlib
+    src = {"full_decode_split": "decode.hip", "sparse_decode": "decode.hip", "full_prefill_fwd": "prefill.hip",
+           "full_prefill_scores": "prefill.hip", "sparse_prefill": "prefill.hip", "topk": "topk.hip"}.get(kernel)
+    if src is None:
+        return ""
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_hybrid_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (src, "hys_common.h", "attn_tile.h"):
+        h.update(open(os.path.join(root, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter runs, or None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[workload][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def copy_calibration(mib: int):
+    import torch
+    x = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read_per_launch": mib << 20, "bytes_written_per_launch": mib << 20,
+                      "launches": 5}), flush=True)
 
 
 def sparse_layer_bytes(wl, idx_np):
@@ -121,6 +165,9 @@ def cpu_baseline(wl, inp, budget_s: float):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build measures one GPU; multi-GPU runs are not part of it (use --gpus 1)",
@@ -207,7 +254,8 @@ def main():
         us = kernels[name]["avg_us"]
         gbs = alg_bytes / (us * 1e-6) / 1e9
         return {"kernel": name, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": gbs / HBM_PEAK_GBS, "traffic": None, "alg_bytes_per_launch": alg_bytes, "avg_us": us}
+                "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name, name),
+                "alg_bytes_per_launch": alg_bytes, "avg_us": us}
 
     mfma_peak = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
 
@@ -217,7 +265,8 @@ def main():
         us = kernels[name]["avg_us"]
         tf = flops / (us * 1e-6) / 1e12
         return {"kernel": name, "bound": "mfma", "achieved": tf, "peak": mfma_peak, "unit": "TFLOP/s",
-                "frac": tf / mfma_peak, "traffic": None, "alg_flops_per_launch": flops, "avg_us": us}
+                "frac": tf / mfma_peak, "traffic": measured_traffic(wl.name, name), "alg_flops_per_launch": flops,
+                "avg_us": us}
 
     dom = max(kernels, key=lambda n: kernels[n]["us_per_step"])
     result["dominant_kernel"] = dom

@@ -1,0 +1,128 @@
+"""Summaries of rocprofv3 CSV output for the kernels of libhysparse.
+
+``python -m long_context_hybrid_amd.profiling stats DIR`` prints a markdown
+table of per-kernel durations from ``--kernel-trace --stats -f csv`` output.
+
+``python -m long_context_hybrid_amd.profiling traffic --workload W --fetch DIR
+--write DIR --copy-fetch DIR --copy-write DIR`` turns two ``--pmc FETCH_SIZE``
+/ ``--pmc WRITE_SIZE`` runs of ``bench.py`` into HBM bytes per launch for each
+library kernel, scaled by what the same counters report for a plain device
+copy of known size (``bench.py --copy-calibration``), and merges the result
+into ``profiles/hbm_traffic.json`` (read by ``bench.py``).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import statistics
+
+KERNELS = {  # symbol fragment -> name used by the library's trace hook
+    "decode_split_kernel<hys::BF16, 128, true>": "full_decode_split",
+    "decode_full_finish_kernel": "full_decode_finish",
+    "decode_split_kernel<hys::BF16, 128, false>": "sparse_decode",
+    "sparse_merge_kernel": "sparse_merge",
+    "topk_row_kernel": "topk",
+    "prefill_fwd_kernel": "full_prefill_fwd",
+    "prefill_scores_kernel": "full_prefill_scores",
+    "sparse_block_kernel": "sparse_prefill",
+}
+
+
+def short_name(symbol: str) -> str:
+    for frag, name in KERNELS.items():
+        if frag in symbol:
+            return name
+    return symbol.split("(")[0][-60:]
+
+
+def _one(pattern: str) -> str:
+    hits = glob.glob(pattern, recursive=True)
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def stats_table(d: str) -> str:
+    path = _one(os.path.join(d, "**", "*kernel_stats.csv"))
+    rows = list(csv.DictReader(open(path)))
+    out = ["| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    return "\n".join(out)
+
+
+def counter_per_kernel(d: str, counter: str) -> dict:
+    """Median counter value (KiB) per kernel name over its dispatches."""
+    path = _one(os.path.join(d, "**", "*counter_collection.csv"))
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        vals.setdefault(short_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return {k: statistics.median(v) for k, v in vals.items()}
+
+
+def copy_factor(d: str, counter: str, nbytes: int) -> float:
+    v = counter_per_kernel(d, counter)
+    copy = [x for k, x in v.items() if "copyBuffer" in k or "copy" in k.lower()]
+    if not copy:
+        raise RuntimeError(f"no copy kernel in {d}")
+    return nbytes / (max(copy) * 1024.0)
+
+
+def traffic(args) -> dict:
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from bench import kernel_source_hash  # the hash bench.py checks before reporting traffic
+    nbytes = args.copy_mib << 20
+    ff = copy_factor(args.copy_fetch, "FETCH_SIZE", nbytes)
+    wf = copy_factor(args.copy_write, "WRITE_SIZE", nbytes)
+    fe = counter_per_kernel(args.fetch, "FETCH_SIZE")
+    wr = counter_per_kernel(args.write, "WRITE_SIZE")
+    out = {}
+    for name in sorted(set(fe) & set(wr)):
+        if name not in KERNELS.values():
+            continue
+        rb, wb = fe[name] * 1024.0 * ff, wr[name] * 1024.0 * wf
+        out[name] = {"bytes_per_launch": rb + wb, "read_bytes": rb, "write_bytes": wb,
+                     "fetch_kib_raw": fe[name], "write_kib_raw": wr[name], "fetch_scale": ff, "write_scale": wf,
+                     "source_hash": kernel_source_hash(name)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    t = sub.add_parser("traffic")
+    t.add_argument("--workload", required=True)
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-fetch", required=True)
+    t.add_argument("--copy-write", required=True)
+    t.add_argument("--copy-mib", type=int, default=1024)
+    t.add_argument("--out", default=os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                                 "profiles", "hbm_traffic.json"))
+    args = ap.parse_args()
+    if args.cmd == "stats":
+        print(stats_table(args.dir))
+        return
+    res = traffic(args)
+    try:
+        allr = json.load(open(args.out))
+    except (OSError, ValueError):
+        allr = {}
+    allr[args.workload] = res
+    json.dump(allr, open(args.out, "w"), indent=1, sort_keys=True)
+    for k, v in res.items():
+        print(f"{args.workload} {k}: {v['bytes_per_launch'] / 1e6:.2f} MB per launch "
+              f"(read {v['read_bytes'] / 1e6:.2f}, write {v['write_bytes'] / 1e6:.2f})")
+
+
+if __name__ == "__main__":
+    main()
