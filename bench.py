@@ -35,7 +35,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode128k", choices=["decode128k", "decode8k", "prefill32k", "tiny"])
+    ap.add_argument("--workload", default="decode128k",
+                    choices=["decode128k", "decode8k", "prefill32k", "tiny", "hier128k"])
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -208,6 +209,25 @@ def main():
         hy.hysparse_hybrid_block(qf, k, v, qs, gates, wl.k_top, wl.score_block, wl.window, out_full=out_full,
                                  out_sparse=outs, lse=lse, scores=scores, idx=idx, workspace=ws)
 
+    hier = wl.name == "hier128k"
+    if hier:
+        # full layer -> hierarchical selection (128-key pooled blocks, keep 64) -> sparse layers
+        HB, HKEEP = 128, 64
+        ws_full = torch.empty(hy.hysparse_workspace_bytes(hy.HYS_OP_FULL, desc, 1), dtype=torch.uint8, device=dev)
+        ws_sp = torch.empty(hy.hysparse_workspace_bytes(hy.HYS_OP_SPARSE, desc, 1, wl.k_top, wl.window),
+                            dtype=torch.uint8, device=dev)
+        ws_h = torch.empty(hy.hysparse_hier_workspace_bytes(desc, HB, HKEEP, wl.k_top), dtype=torch.uint8, device=dev)
+        bsc = torch.empty((B, Hkv, -(-Tkv // HB)), dtype=torch.float32, device=dev)
+        blk = torch.empty((B, Hkv, HKEEP), dtype=torch.int32, device=dev)
+
+        def step():
+            hy.hysparse_full_attn_scores(qf, k, v, 1, out=out_full, lse=lse, scores=scores, workspace=ws_full)
+            hy.hysparse_hier_select(qf, k, scores, HB, HKEEP, wl.k_top, idx=idx, block_scores=bsc, blocks=blk,
+                                    workspace=ws_h)
+            for l in range(len(qs)):
+                hy.hysparse_sparse_attn(qs[l], k, v, idx, wl.k_top, 1, wl.window, gates[l], out=outs[l],
+                                        workspace=ws_sp)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -299,10 +319,23 @@ def main():
             result["full_layer"] = {"tflops_algorithmic": ff / t_full / 1e12, "frac_peak": ff / t_full / 1e12 / mfma_peak,
                                     "us": t_full * 1e6, "alg_flops": ff,
                                     "note": "two sweeps: the score sweep recomputes QK^T after the final LSE"}
+    if hier:
+        from oracle import hysparse_oracle as orc  # set-overlap and recall helpers only (reporting)
+        flat = hy.hysparse_topk(scores.view(B * Hkv, Tkv), wl.k_top).view(B, Hkv, 1, wl.k_top)
+        o_flat = hy.hysparse_sparse_attn(qs[0], k, v, flat, wl.k_top, 1, wl.window, gates[0])
+        torch.cuda.synchronize()
+        fl, hi = flat.cpu().numpy(), idx_np
+        ious = [orc.selection_iou(hi[b, g], fl[b, g]) for b in range(B) for g in range(Hkv)]
+        rec = lambda sel: float(np.mean([np.isin(inp.planted[b], sel[b, g]).mean() for b in range(B)
+                                          for g in range(Hkv)]))
+        oh, of = outs[0].float().cpu().numpy(), o_flat.float().cpu().numpy()
+        result["hierarchical"] = {"block": 128, "blocks_kept": 64, "mean_iou_vs_flat": float(np.mean(ious)),
+                                  "planted_recall": rec(hi), "planted_recall_flat": rec(fl),
+                                  "sparse_out_rel_l2_vs_flat": float(np.linalg.norm(oh - of) / np.linalg.norm(of))}
     result["kernels"] = kernels
     result["traced_ms_per_step"] = traced_ms
     result["input_sha256"] = inp.sha256()
-    if args.cpu_baseline:
+    if args.cpu_baseline and not hier:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

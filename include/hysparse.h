@@ -158,6 +158,37 @@ hys_status hysparse_hybrid_block(const hys_attn_desc* desc, const void* q_full, 
                                  float* lse, float* scores, int32_t* idx, void* ws,
                                  size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Hierarchical selection for decode (q_len 1), a variant of the top-K step
+ * (HISA abstract: a block-level coarse filter over pooled block
+ * representatives, then token-level selection inside the surviving blocks;
+ * Baidu article, "Configuration Considerations": pooled representations for
+ * scoring).
+ *
+ *   1. pooled keys: the mean of each run of `block` consecutive keys of a KV
+ *      group (the last run may be shorter);
+ *   2. block score: softmax over the pooled keys of each query head of the
+ *      group (scale as desc), summed over the group's heads;
+ *   3. the n_keep best blocks by the top-K order rule;
+ *   4. the k_top best tokens of those blocks by the full layer's scores.
+ *
+ *   q, k          as for hysparse_full_attn_scores (q_len must be 1).
+ *   scores        float32 [B, Hkv, 1, Tkv]: the full layer's scores.
+ *   block_scores  float32 [B, Hkv, ceil(Tkv/block)] or NULL (workspace only).
+ *   blocks        int32 [B, Hkv, n_keep] kept block ids, ascending, -1
+ *                 padded; or NULL.
+ *   idx           int32 [B, Hkv, 1, k_top] token indices, ascending, -1 padded.
+ *   ws/ws_bytes   at least hysparse_hier_workspace_bytes(desc, block, n_keep, k_top).
+ */
+hys_status hysparse_hier_select(const hys_attn_desc* desc, const void* q, const void* k,
+                                const float* scores, int32_t block, int32_t n_keep, int32_t k_top,
+                                float* block_scores, int32_t* blocks, int32_t* idx, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for hysparse_hier_select (0 for invalid arguments). */
+size_t hysparse_hier_workspace_bytes(const hys_attn_desc* desc, int32_t block, int32_t n_keep,
+                                     int32_t k_top);
+
 /* Workspace bytes for op (HYS_OP_*) on desc; k_top and window are ignored
  * where they do not apply.  For HYS_OP_HYBRID the figure covers scores and
  * idx kept in the workspace (the NULL-output case) and any n_sparse.

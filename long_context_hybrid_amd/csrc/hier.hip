@@ -1,0 +1,223 @@
+// Hierarchical selection for decode (HISA abstract: a block-level coarse
+// filter over pooled block representatives prunes regions, then the
+// token-level selection runs only inside the surviving blocks).
+//
+//   1. pool_keys:     kbar[b, m, g, :] = mean of the keys of block m (the last
+//                     block may be shorter), fp32;
+//   2. block_scores:  per KV group, each query head's softmax over the pooled
+//                     keys, summed over the group's heads;
+//   3. top n_keep blocks by the top-K kernel (same order rule);
+//   4. gather:        the full layer's scores S at the kept blocks' tokens, in
+//                     ascending token order (only the last block can be short,
+//                     and it sorts last);
+//   5. top k_top candidates by the top-K kernel, mapped back to token indices.
+#include "hys_common.h"
+#include "hys_internal.h"
+
+namespace hys {
+
+namespace {
+
+constexpr int kMaxBlocks = 1 << 20;  // pooled blocks per row
+
+template <typename TR, int D>
+__global__ __launch_bounds__(D) void pool_keys_kernel(const void* k, int64_t ks_b, int64_t ks_t, int64_t ks_h, int Tkv,
+                                                      int Hkv, int M, int block, float* kbar) {
+  const int id = blockIdx.x;  // (b, m, g)
+  const int g = id % Hkv, m = (id / Hkv) % M, b = id / (Hkv * M);
+  const int d = threadIdx.x;
+  const int j0 = m * block, j1 = min(j0 + block, Tkv);
+  const typename TR::storage* base = (const typename TR::storage*)k + (int64_t)b * ks_b + (int64_t)g * ks_h + d;
+  float s = 0.f;
+#pragma unroll 8
+  for (int j = j0; j < j1; ++j) s += TR::to_float(base[(int64_t)j * ks_t]);
+  kbar[(((int64_t)b * M + m) * Hkv + g) * D + d] = s / (float)(j1 - j0);
+}
+
+// Block logits: one workgroup per (b, g, run of 64 pooled blocks); thread
+// (block m, head h) computes logit2[b, g, h, m] = tau * log2(e) * q_h . kbar_m.
+template <typename TR, int D>
+__global__ __launch_bounds__(256) void block_logits_kernel(const void* q, int64_t qs_b, int64_t qs_h, const float* kbar,
+                                                           int Hkv, int G, int M, float sl2, float* logit2) {
+  __shared__ float qs[16 * D];
+  __shared__ float ks[64 * (D + 1)];
+  const int nchunk = (M + 63) / 64;
+  const int bg = blockIdx.x / nchunk, ch = blockIdx.x - (blockIdx.x / nchunk) * nchunk;
+  const int b = bg / Hkv, g = bg - (bg / Hkv) * Hkv;
+  const int t = threadIdx.x;
+  const int m0 = ch * 64;
+  for (int x = t; x < G * D; x += 256) {
+    const int h = x / D, d = x - h * D;
+    qs[x] = TR::to_float(((const typename TR::storage*)q)[(int64_t)b * qs_b + (int64_t)(g * G + h) * qs_h + d]);
+  }
+  for (int x = t; x < 64 * D; x += 256) {
+    const int mm = x / D, d = x - mm * D;
+    ks[mm * (D + 1) + d] = (m0 + mm < M) ? kbar[(((int64_t)b * M + m0 + mm) * Hkv + g) * D + d] : 0.f;
+  }
+  __syncthreads();
+  for (int x = t; x < 64 * G; x += 256) {
+    const int mm = x & 63, h = x >> 6;
+    float acc = 0.f;
+    for (int d = 0; d < D; ++d) acc += qs[h * D + d] * ks[mm * (D + 1) + d];
+    if (m0 + mm < M) logit2[((int64_t)bg * G + h) * M + m0 + mm] = acc * sl2;
+  }
+}
+
+// Block scores: one workgroup per (b, g): per head the softmax over the
+// pooled blocks (16 threads per head, fixed order), summed over heads.
+__global__ __launch_bounds__(256) void block_softmax_kernel(const float* logit2, int G, int M, float* bscore) {
+  __shared__ float lse[16];
+  const int bg = blockIdx.x, t = threadIdx.x;
+  const int h = t >> 4, s = t & 15;
+  const float* lg = logit2 + (int64_t)bg * G * M;
+  float mx = kNegInf;
+  if (h < G)
+    for (int m = s; m < M; m += 16) mx = fmaxf(mx, lg[(int64_t)h * M + m]);
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+  float sum = 0.f;
+  if (h < G)
+    for (int m = s; m < M; m += 16) sum += exp2f(lg[(int64_t)h * M + m] - mx);
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
+  if (s == 0 && h < G) lse[h] = mx + log2f(sum);
+  __syncthreads();
+  for (int m = t; m < M; m += 256) {
+    float v = 0.f;
+    for (int hh = 0; hh < G; ++hh) v += exp2f(lg[(int64_t)hh * M + m] - lse[hh]);
+    bscore[(int64_t)bg * M + m] = v;
+  }
+}
+
+// cand[row][c] = S[row][token(c)], token(c) = blk[c / block] * block + c % block,
+// for the kept blocks in ascending order; valid[row] = number of candidates.
+__global__ __launch_bounds__(256) void gather_candidates_kernel(const float* S, int Tkv, const int32_t* blk, int n_keep,
+                                                                int block, float* cand, int32_t* valid) {
+  const int row = blockIdx.y;
+  const int64_t ncand = (int64_t)n_keep * block;
+  const int32_t* br = blk + (int64_t)row * n_keep;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < ncand; c += (int64_t)gridDim.x * 256) {
+    const int bi = (int)(c / block), o = (int)(c - (int64_t)bi * block);
+    const int m = br[bi];
+    const int64_t j = (int64_t)m * block + o;
+    cand[(int64_t)row * ncand + c] = (m >= 0 && j < Tkv) ? S[(int64_t)row * Tkv + j] : 0.f;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    int nv = 0;
+    for (int bi = 0; bi < n_keep; ++bi) {
+      const int m = br[bi];
+      if (m < 0) break;
+      nv += min(block, Tkv - m * block);
+    }
+    valid[row] = nv;
+  }
+}
+
+__global__ __launch_bounds__(256) void map_positions_kernel(const int32_t* pos, const int32_t* blk, int n_keep,
+                                                            int block, int k_top, int64_t n, int32_t* idx) {
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256) {
+    const int64_t row = x / k_top;
+    const int p = pos[x];
+    idx[x] = p < 0 ? -1 : blk[row * n_keep + p / block] * block + p % block;
+  }
+}
+
+struct HierWs {
+  float* kbar;
+  float* logit2;
+  float* bscore;
+  int32_t* blk;
+  float* cand;
+  int32_t* valid;
+  int32_t* pos;
+};
+
+HierWs carve(const Geom& g, int block, int n_keep, int k_top, void* ws) {
+  const int M = (g.Tkv + block - 1) / block;
+  const int64_t rows = (int64_t)g.B * g.Hkv;
+  HierWs w{};
+  unsigned char* c = static_cast<unsigned char*>(ws);
+  w.kbar = reinterpret_cast<float*>(c);
+  c += align_up((size_t)g.B * M * g.Hkv * g.D * sizeof(float));
+  w.logit2 = reinterpret_cast<float*>(c);
+  c += align_up((size_t)rows * g.G * M * sizeof(float));
+  w.bscore = reinterpret_cast<float*>(c);
+  c += align_up((size_t)rows * M * sizeof(float));
+  w.blk = reinterpret_cast<int32_t*>(c);
+  c += align_up((size_t)rows * n_keep * sizeof(int32_t));
+  w.cand = reinterpret_cast<float*>(c);
+  c += align_up((size_t)rows * n_keep * block * sizeof(float));
+  w.valid = reinterpret_cast<int32_t*>(c);
+  c += align_up((size_t)rows * sizeof(int32_t));
+  w.pos = reinterpret_cast<int32_t*>(c);
+  return w;
+}
+
+}  // namespace
+
+int hier_max_blocks() { return kMaxBlocks; }
+
+size_t hier_ws_bytes(const Geom& g, int block, int n_keep, int k_top) {
+  const int M = (g.Tkv + block - 1) / block;
+  const int64_t rows = (int64_t)g.B * g.Hkv;
+  return align_up((size_t)g.B * M * g.Hkv * g.D * sizeof(float)) + align_up((size_t)rows * g.G * M * sizeof(float)) +
+         align_up((size_t)rows * M * sizeof(float)) +
+         align_up((size_t)rows * n_keep * sizeof(int32_t)) + align_up((size_t)rows * n_keep * block * sizeof(float)) +
+         align_up((size_t)rows * sizeof(int32_t)) + align_up((size_t)rows * k_top * sizeof(int32_t));
+}
+
+hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const float* scores, int block, int n_keep,
+                              int k_top, float* bscore_out, int32_t* blk_out, int32_t* idx, void* ws, hipStream_t st) {
+  const int M = (g.Tkv + block - 1) / block;
+  const int rows = g.B * g.Hkv;
+  HierWs w = carve(g, block, n_keep, k_top, ws);
+  float* bscore = bscore_out ? bscore_out : w.bscore;
+  int32_t* blk = blk_out ? blk_out : w.blk;
+  const float sl2 = g.scale * kLog2e;
+  hipError_t e;
+#define HIER_DT(...)                                                     \
+  do {                                                                   \
+    if (g.dtype == 1 && g.D == 128) { using TR = BF16; constexpr int DD = 128; __VA_ARGS__; } \
+    else if (g.dtype == 1) { using TR = BF16; constexpr int DD = 64; __VA_ARGS__; }           \
+    else if (g.D == 128) { using TR = F32; constexpr int DD = 128; __VA_ARGS__; }            \
+    else { using TR = F32; constexpr int DD = 64; __VA_ARGS__; }                              \
+  } while (0)
+  HIER_DT({
+    {
+      TraceScope ts(st, "hier_pool_keys");
+      pool_keys_kernel<TR, DD><<<g.B * M * g.Hkv, DD, 0, st>>>(k, g.ks_b, g.ks_t, g.ks_h, g.Tkv, g.Hkv, M, block,
+                                                               w.kbar);
+    }
+    {
+      TraceScope ts(st, "hier_block_logits");
+      block_logits_kernel<TR, DD><<<rows * ((M + 63) / 64), 256, 0, st>>>(q, g.qs_b, g.qs_h, w.kbar, g.Hkv, g.G, M,
+                                                                            sl2, w.logit2);
+    }
+    {
+      TraceScope ts(st, "hier_block_softmax");
+      block_softmax_kernel<<<rows, 256, 0, st>>>(w.logit2, g.G, M, bscore);
+    }
+  });
+#undef HIER_DT
+  ValidLen all{nullptr, M, 0, 1, 1, 1, 1};
+  if ((e = launch_topk(bscore, rows, M, M, all, n_keep, blk, nullptr, st)) != hipSuccess) return e;
+  const int64_t ncand = (int64_t)n_keep * block;
+  {
+    TraceScope ts(st, "hier_gather");
+    int gx = (int)((ncand + 255) / 256);
+    if (gx > 64) gx = 64;
+    gather_candidates_kernel<<<dim3(gx, rows), 256, 0, st>>>(scores, g.Tkv, blk, n_keep, block, w.cand, w.valid);
+  }
+  ValidLen vl{w.valid, (int32_t)ncand, 0, 1, 1, 1, 1};
+  if ((e = launch_topk(w.cand, rows, (int32_t)ncand, ncand, vl, k_top, w.pos, nullptr, st)) != hipSuccess) return e;
+  {
+    TraceScope ts(st, "hier_map");
+    const int64_t n = (int64_t)rows * k_top;
+    int gb = (int)((n + 255) / 256);
+    if (gb > 4096) gb = 4096;
+    map_positions_kernel<<<gb, 256, 0, st>>>(w.pos, blk, n_keep, block, k_top, n, idx);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hys

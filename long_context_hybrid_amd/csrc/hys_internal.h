@@ -100,4 +100,10 @@ size_t topk_ws_bytes(int64_t n_rows, int32_t row_len, int32_t k);
 hipError_t launch_topk(const float* scores, int64_t n_rows, int32_t row_len, int64_t row_stride,
                        const ValidLen& vl, int32_t k, int32_t* idx, void* ws, hipStream_t st);
 
+// ------------------------------------------------------ hierarchical select
+int hier_max_blocks();
+size_t hier_ws_bytes(const Geom& g, int block, int n_keep, int k_top);
+hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const float* scores, int block, int n_keep,
+                              int k_top, float* bscore_out, int32_t* blk_out, int32_t* idx, void* ws, hipStream_t st);
+
 }  // namespace hys

@@ -281,6 +281,38 @@ size_t hysparse_workspace_bytes(int32_t op, const hys_attn_desc* desc, int32_t s
   }
 }
 
+static hys_status check_hier(const hys_attn_desc* desc, int32_t block, int32_t n_keep, int32_t k_top, hys::Geom* g) {
+  hys_status s;
+  if ((s = check_desc(desc, g))) return s;
+  if (g->Tq != 1) return fail(HYS_ERR_UNSUPPORTED, "hierarchical selection is implemented for decode (q_len 1)");
+  if (block < 1 || n_keep < 1 || k_top < 1) return fail(HYS_ERR_BAD_SHAPE, "block, n_keep and k_top must be >= 1");
+  if ((int64_t)n_keep * block > (int64_t)1 << 30) return fail(HYS_ERR_BAD_SHAPE, "n_keep * block too large");
+  if ((g->Tkv + block - 1) / block > hys::hier_max_blocks())
+    return fail(HYS_ERR_UNSUPPORTED, "more than " + std::to_string(hys::hier_max_blocks()) + " pooled blocks per row");
+  return HYS_OK;
+}
+
+hys_status hysparse_hier_select(const hys_attn_desc* desc, const void* q, const void* k, const float* scores,
+                                int32_t block, int32_t n_keep, int32_t k_top, float* block_scores, int32_t* blocks,
+                                int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hys::Geom g;
+  hys_status s;
+  if ((s = check_hier(desc, block, n_keep, k_top, &g))) return s;
+  if ((s = check_tensor(q, "q", 16)) || (s = check_tensor(k, "k", 16)) || (s = check_tensor(scores, "scores", 16)) ||
+      (s = check_tensor(idx, "idx", 4)))
+    return s;
+  if (block_scores && !aligned(block_scores, 4)) return fail(HYS_ERR_ALIGN, "block_scores is not 4-byte aligned");
+  if (blocks && !aligned(blocks, 4)) return fail(HYS_ERR_ALIGN, "blocks is not 4-byte aligned");
+  if ((s = check_ws(ws, ws_bytes, hys::hier_ws_bytes(g, block, n_keep, k_top)))) return s;
+  return from_hip(hys::launch_hier_select(g, q, k, scores, block, n_keep, k_top, block_scores, blocks, idx, ws, stream));
+}
+
+size_t hysparse_hier_workspace_bytes(const hys_attn_desc* desc, int32_t block, int32_t n_keep, int32_t k_top) {
+  hys::Geom g;
+  if (check_hier(desc, block, n_keep, k_top, &g) != HYS_OK) return 0;
+  return hys::hier_ws_bytes(g, block, n_keep, k_top);
+}
+
 size_t hysparse_topk_workspace_bytes(int64_t n_rows, int32_t row_len, int32_t k) {
   if (n_rows < 0 || row_len < 1 || k < 1) return 0;
   return hys::topk_ws_bytes(n_rows, row_len, k);

@@ -28,7 +28,7 @@ STATUS = {0: "HYS_OK", 1: "HYS_ERR_NULL_PTR", 2: "HYS_ERR_BAD_SHAPE", 3: "HYS_ER
 EXPORTS = ("hysparse_full_attn_scores", "hysparse_topk", "hysparse_sparse_attn", "hysparse_hybrid_block",
            "hysparse_workspace_bytes", "hysparse_topk_workspace_bytes", "hysparse_status_string",
            "hysparse_last_error", "hysparse_version", "hysparse_trace_begin", "hysparse_trace_end",
-           "hysparse_trace_name")
+           "hysparse_trace_name", "hysparse_hier_select", "hysparse_hier_workspace_bytes")
 
 
 class HysAttnDesc(ctypes.Structure):
@@ -74,6 +74,10 @@ def lib() -> ctypes.CDLL:
     L.hysparse_last_error.argtypes = []
     L.hysparse_last_error.restype = ctypes.c_char_p
     L.hysparse_version.restype = i32
+    L.hysparse_hier_select.argtypes = [D, _P, _P, _P, i32, i32, i32, _P, _P, _P, _P, sz, _P]
+    L.hysparse_hier_select.restype = i32
+    L.hysparse_hier_workspace_bytes.argtypes = [D, i32, i32, i32]
+    L.hysparse_hier_workspace_bytes.restype = sz
     L.hysparse_trace_begin.argtypes = [_P, i32]
     L.hysparse_trace_begin.restype = None
     L.hysparse_trace_end.argtypes = []
@@ -234,6 +238,28 @@ def hysparse_hybrid_block(q_full, k, v, q_sparse: Sequence[torch.Tensor], gate_l
                                        os_arr, _ptr(lse), _ptr(scores), _ptr(idx), _ptr(ws),
                                        0 if ws is None else ws.numel(), _stream(dev)))
     return {"out_full": out_full, "out": list(out_sparse), "lse": lse, "scores": scores, "idx": idx}
+
+
+def hysparse_hier_workspace_bytes(desc: HysAttnDesc, block: int, n_keep: int, k_top: int) -> int:
+    return int(lib().hysparse_hier_workspace_bytes(ctypes.byref(desc), block, n_keep, k_top))
+
+
+def hysparse_hier_select(q, k, scores, block: int, n_keep: int, k_top: int, idx=None, block_scores=None,
+                         blocks=None, want_blocks: bool = True, workspace=None, scale: float = 0.0):
+    """Hierarchical token selection for decode; returns (idx, block_scores, blocks)."""
+    dev = _same_device(q, k, scores)
+    desc = make_desc(q, k, scale)
+    B, Hkv, Tkv = q.shape[0], k.shape[2], k.shape[1]
+    M = -(-Tkv // block)
+    idx = torch.empty((B, Hkv, 1, k_top), dtype=torch.int32, device=dev) if idx is None else idx
+    if want_blocks:
+        block_scores = torch.empty((B, Hkv, M), dtype=torch.float32, device=dev) if block_scores is None else block_scores
+        blocks = torch.empty((B, Hkv, n_keep), dtype=torch.int32, device=dev) if blocks is None else blocks
+    ws = _workspace(hysparse_hier_workspace_bytes(desc, block, n_keep, k_top), dev, workspace)
+    _check(lib().hysparse_hier_select(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(scores), block, n_keep, k_top,
+                                      _ptr(block_scores), _ptr(blocks), _ptr(idx), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(dev)))
+    return idx, block_scores, blocks
 
 
 class KernelTrace:

@@ -328,3 +328,68 @@ def attention_mass_covered(p_row, idx_row) -> float:
     sel = sel[sel >= 0]
     p = np.asarray(p_row, dtype=F64)
     return float(p[sel].sum() / p.sum())
+
+
+# ---------------------------------------------------------------------------
+# Hierarchical selection (HISA abstract: a block-level coarse filter scores
+# pooled block representatives and prunes regions, then the token-level
+# selection runs only inside the surviving blocks; the Baidu article's
+# "Configuration Considerations" mention pooled representations for scoring).
+# Decode only (one query row): the token-level refinement uses the full
+# layer's own scores S restricted to the kept blocks.
+# ---------------------------------------------------------------------------
+
+def pooled_keys(k, block: int):
+    """Mean of each run of `block` consecutive keys (the last run may be
+    shorter): [B, T, Hkv, D] -> [B, M, Hkv, D] float64."""
+    B, T, Hkv, D = k.shape
+    M = -(-T // block)
+    out = np.empty((B, M, Hkv, D))
+    for m in range(M):
+        out[:, m] = k[:, m * block:min((m + 1) * block, T)].astype(F64).mean(axis=1)
+    return out
+
+
+def block_scores(q, kbar, scale=None):
+    """Block score of a KV group for one query row: the group's query heads'
+    softmax over the pooled keys, summed over the heads.  q: [B, 1, Hq, D];
+    kbar: [B, M, Hkv, D] -> [B, Hkv, M] float64."""
+    B, _, Hq, D = q.shape
+    M, Hkv = kbar.shape[1], kbar.shape[2]
+    G = Hq // Hkv
+    scale = default_scale(D) if scale is None else scale
+    out = np.empty((B, Hkv, M))
+    for b in range(B):
+        for g in range(Hkv):
+            lg = scale * (q[b, 0, g * G:(g + 1) * G].astype(F64) @ kbar[b, :, g].T)   # [G, M]
+            p, _, _ = _softmax_masked(lg, np.ones_like(lg, dtype=bool))
+            out[b, g] = p.sum(axis=0)
+    return out
+
+
+def hier_select(q, k, S, block: int, n_keep: int, k_top: int, scale=None, block_scores_f32=None):
+    """Kept blocks (ascending, -1 padded) and token indices (ascending, -1
+    padded) of the hierarchical selection for decode.
+
+    Blocks: the n_keep largest block scores (rounded once to float32) by the
+    same order rule as the token top-K.  Tokens: the k_top largest entries of
+    the flat scores S among the tokens of the kept blocks.  ``block_scores_f32``
+    lets a caller supply the block scores (to check a selection made on
+    another implementation's block scores)."""
+    B, T, Hkv, _ = k.shape
+    M = -(-T // block)
+    bs = (block_scores(q, pooled_keys(k, block), scale).astype(np.float32)
+          if block_scores_f32 is None else np.asarray(block_scores_f32, dtype=np.float32))
+    blk = np.full((B, Hkv, n_keep), -1, dtype=np.int32)
+    idx = np.full((B, Hkv, 1, k_top), -1, dtype=np.int32)
+    for b in range(B):
+        for g in range(Hkv):
+            kept = topk_row(bs[b, g], M, n_keep)
+            blk[b, g] = kept
+            kept = kept[kept >= 0]
+            cand = np.concatenate([np.arange(m * block, min((m + 1) * block, T)) for m in kept]) if kept.size \
+                else np.zeros(0, dtype=np.int64)
+            pos_in = topk_row(np.asarray(S[b, g, 0], dtype=np.float32)[cand], cand.size, k_top)
+            sel = pos_in[pos_in >= 0]
+            idx[b, g, 0, :sel.size] = cand[sel]
+    return blk, idx, bs

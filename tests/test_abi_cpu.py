@@ -118,6 +118,19 @@ def test_sparse_and_hybrid_validation():
     assert st == 2
 
 
+def test_hier_validation():
+    L = hy.lib()
+    d = _desc(Tq=1, Tkv=4096)
+    call = lambda dd, blk, keep, kt: L.hysparse_hier_select(ctypes.byref(dd), FAKE, FAKE, FAKE, blk, keep, kt, None,
+                                                            None, FAKE, FAKE, 1 << 40, None)
+    assert call(d, 0, 8, 64) == 2
+    assert call(d, 128, 0, 64) == 2
+    assert call(_desc(Tq=4, Tkv=4096), 128, 8, 64) == 3            # decode only
+    assert L.hysparse_hier_select(ctypes.byref(d), FAKE, FAKE, None, 128, 8, 64, None, None, FAKE, FAKE,
+                                  1 << 40, None) == 1
+    assert L.hysparse_hier_workspace_bytes(ctypes.byref(d), 128, 8, 64) > 0
+
+
 def test_workspace_query_grows_with_problem():
     L = hy.lib()
     small = L.hysparse_workspace_bytes(hy.HYS_OP_HYBRID, ctypes.byref(_desc(Tkv=1024)), 1, 64, 128)

@@ -330,3 +330,43 @@ def test_selection_helpers():
     assert orc.selection_iou([1, 2, 3, -1], [2, 3, 4, -1]) == 0.5
     p = np.array([0.5, 0.25, 0.125, 0.125])
     assert orc.attention_mass_covered(p, [0, 2, -1]) == 0.625
+
+
+# ------------------------------------------------------ hierarchical select
+
+def test_pooled_keys_and_block_scores_closed_forms():
+    rng = np.random.default_rng(80)
+    B, T, Hkv, D, blk = 1, 300, 2, 8, 64
+    k = rng.standard_normal((B, T, Hkv, D))
+    kb = orc.pooled_keys(k, blk)
+    assert kb.shape == (1, 5, 2, 8)
+    np.testing.assert_allclose(kb[0, 1, 0], k[0, 64:128, 0].mean(axis=0), atol=1e-14)
+    np.testing.assert_allclose(kb[0, 4, 1], k[0, 256:300, 1].mean(axis=0), atol=1e-14)   # partial last block
+    q = rng.standard_normal((B, 1, 6, D))
+    bs = orc.block_scores(q, kb)
+    np.testing.assert_allclose(bs.sum(-1), 3.0, rtol=1e-12)                           # G heads x softmax
+    # constant keys inside a block: the pooled key is that key
+    kc = np.repeat(k[:, ::blk][:, :, None], blk, axis=2).reshape(B, -1, Hkv, D)[:, :T]
+    np.testing.assert_allclose(orc.pooled_keys(kc, blk)[0, 2, 1], kc[0, 128, 1], atol=1e-14)
+
+
+def test_hier_select_keeping_every_block_equals_flat():
+    """With as many kept blocks as there are blocks, the hierarchical selection
+    is the flat top-K (IoU 1)."""
+    wl = gen.WORKLOADS["decode128k"].replace(kv_len=2048, batch=1, n_sparse=1, k_top=100, n_planted=8)
+    inp = gen.make_inputs(wl)
+    _, _, S = orc.full_layer(inp.q_full, inp.k, inp.v, 1)
+    flat = orc.select_indices(S, 1, wl.kv_len, 1, wl.k_top)
+    blk, idx, _ = orc.hier_select(inp.q_full, inp.k, S, 128, 16, wl.k_top)
+    np.testing.assert_array_equal(idx, flat)
+    np.testing.assert_array_equal(blk[0, 0], np.arange(16))
+    blk, idx, _ = orc.hier_select(inp.q_full, inp.k, S, 128, 4, wl.k_top)
+    for g in range(wl.n_kv_heads):
+        sel = idx[0, g, 0][idx[0, g, 0] >= 0]
+        assert sel.size == wl.k_top and np.all(np.isin(sel // 128, blk[0, g]))
+        assert np.all(np.diff(sel) > 0)
+        # the kept tokens are the best of the kept blocks by the flat scores
+        cand = np.concatenate([np.arange(m * 128, (m + 1) * 128) for m in blk[0, g]])
+        rest = np.setdiff1d(cand, sel)
+        assert S[0, g, 0, sel].min() >= S[0, g, 0, rest].max()
+    assert 0.0 <= orc.selection_iou(idx[0, 0], flat[0, 0]) < 1.0
