@@ -370,3 +370,36 @@ def test_hier_select_keeping_every_block_equals_flat():
         rest = np.setdiff1d(cand, sel)
         assert S[0, g, 0, sel].min() >= S[0, g, 0, rest].max()
     assert 0.0 <= orc.selection_iou(idx[0, 0], flat[0, 0]) < 1.0
+
+
+def test_block_scores_with_unit_blocks_are_the_full_layer_scores():
+    """Blocks of one key: the pooled keys are the keys and the block scores
+    are the full layer's decode scores S (softmax per head summed over the
+    group), computed independently by full_layer."""
+    wl = gen.WORKLOADS["decode128k"].replace(kv_len=700, batch=2, n_sparse=1, k_top=64, n_planted=4)
+    inp = gen.make_inputs(wl)
+    _, _, S = orc.full_layer(inp.q_full, inp.k, inp.v, 1)
+    kb = orc.pooled_keys(inp.k, 1)
+    np.testing.assert_array_equal(kb, inp.k.astype(np.float64))
+    bs = orc.block_scores(inp.q_full, kb)
+    np.testing.assert_allclose(bs, S[:, :, 0], rtol=1.2e-7, atol=0)   # S is stored rounded to float32
+    blk, idx, _ = orc.hier_select(inp.q_full, inp.k, S, 1, wl.kv_len, wl.k_top)
+    np.testing.assert_array_equal(idx, orc.select_indices(S, 1, wl.kv_len, 1, wl.k_top))
+
+
+def test_planted_block_outranks_the_rest():
+    """A block whose keys all point along a group's summed query direction
+    gets that group's largest block score and is kept; other groups are not
+    affected."""
+    rng = np.random.default_rng(81)
+    B, T, Hq, Hkv, D, blk = 1, 1024, 8, 2, 16, 64
+    q = rng.standard_normal((B, 1, Hq, D))
+    k = rng.standard_normal((B, T, Hkv, D)) * 0.5
+    u = q[0, 0, 0:4].sum(axis=0)
+    k[0, 5 * blk:6 * blk, 0] = 6.0 * u / np.linalg.norm(u)
+    bs = orc.block_scores(q, orc.pooled_keys(k, blk))
+    assert int(np.argmax(bs[0, 0])) == 5
+    assert int(np.argmax(bs[0, 1])) != 5 or bs[0, 1, 5] < 0.5
+    S = np.zeros((B, Hkv, 1, T))
+    kept, _, _ = orc.hier_select(q, k, S, blk, 3, 8)
+    assert 5 in kept[0, 0]
