@@ -23,8 +23,11 @@ template <typename TR, int D>
 struct TileLayout {
   static constexpr int EPC = 16 / TR::kBytes;          // elements per 16-byte chunk
   static constexpr int CPR = D / EPC;                  // chunks per row
-  static constexpr int KP = D * TR::kBytes + 16;       // K row pitch, bytes
-  static constexpr int VPE = kTK + 16 / TR::kBytes;    // Vt row pitch, elements
+  static constexpr int KP = D * TR::kBytes + 16;       // K row pitch, bytes (68 dwords for D = 128 bf16)
+  // Vt row pitch: 68 elements = 34 dwords (bf16) or 68 dwords (fp32), so the
+  // fragment reads of 16 (bf16, 8-byte) or 8 (fp32, 16-byte) consecutive d
+  // rows hit distinct banks.
+  static constexpr int VPE = kTK + 4;
   static constexpr int kKBytes = kTK * KP;
   static constexpr int kVBytes = D * VPE * TR::kBytes;
   static constexpr int kBytes = kKBytes + kVBytes;
@@ -37,9 +40,16 @@ struct TileStage {
   using ST = typename TR::storage;
   using L = TileLayout<TR, D>;
   static constexpr int NK = (kTK * L::CPR + NT - 1) / NT;
-  static constexpr int NV = WITH_V ? (16 * L::CPR + NT - 1) / NT : 0;
-  uint4 kr[NK];
-  uint4 vr[NV > 0 ? NV : 1][4];
+  // V is staged by key pairs: unit u = (pair u % 32, chunk u / 32), so the 32
+  // lanes of one LDS store pass write 32 consecutive dwords of a Vt row
+  // (bf16; fp32 stores 8 bytes per lane, 16 lanes per pass)
+  static constexpr int NV = WITH_V ? (32 * L::CPR + NT - 1) / NT : 0;
+  static constexpr bool kExactK = (kTK * L::CPR) % NT == 0;
+  static constexpr bool kExactV = (32 * L::CPR) % NT == 0;
+  // native vectors, not HIP's uint4 struct: struct copies become memcpys that
+  // keep the staging array in scratch memory
+  u32x4_t kr[NK];
+  u32x4_t vr[NV > 0 ? NV : 1][2];
   int jk;
 
   // key(t) -> key index of tile entry t, or -1 when the entry is invalid
@@ -49,22 +59,24 @@ struct TileStage {
 #pragma unroll
     for (int s = 0; s < NK; ++s) {
       const int x = tid + s * NT;
-      if (x < kTK * L::CPR) {
+      // the guard is static when NT divides the tile's chunk count: a
+      // conditional write here would keep kr out of registers
+      if (kExactK || x < kTK * L::CPR) {
         const int t = x / L::CPR, c = x - (x / L::CPR) * L::CPR;
         const int j = key(t);
-        kr[s] = *reinterpret_cast<const uint4*>(kbase + (int64_t)(j >= 0 ? j : 0) * ks_t + c * L::EPC);
+        kr[s] = *reinterpret_cast<const u32x4_t*>(kbase + (int64_t)(j >= 0 ? j : 0) * ks_t + c * L::EPC);
       }
     }
     if constexpr (WITH_V) {
 #pragma unroll
       for (int s = 0; s < NV; ++s) {
         const int x = tid + s * NT;
-        if (x < 16 * L::CPR) {
-          const int kq = x / L::CPR, c = x - (x / L::CPR) * L::CPR;
+        if (kExactV || x < 32 * L::CPR) {
+          const int kp = x & 31, c = x >> 5;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = key(4 * kq + r);
-            vr[s][r] = *reinterpret_cast<const uint4*>(vbase + (int64_t)(j >= 0 ? j : 0) * ks_t + c * L::EPC);
+          for (int r = 0; r < 2; ++r) {
+            const int j = key(2 * kp + r);
+            vr[s][r] = *reinterpret_cast<const u32x4_t*>(vbase + (int64_t)(j >= 0 ? j : 0) * ks_t + c * L::EPC);
           }
         }
       }
@@ -77,9 +89,9 @@ struct TileStage {
 #pragma unroll
     for (int s = 0; s < NK; ++s) {
       const int x = tid + s * NT;
-      if (x < kTK * L::CPR) {
+      if (kExactK || x < kTK * L::CPR) {
         const int t = x / L::CPR, c = x - (x / L::CPR) * L::CPR;
-        *reinterpret_cast<uint4*>(sm + t * L::KP + c * 16) = kr[s];
+        *reinterpret_cast<u32x4_t*>(sm + t * L::KP + c * 16) = kr[s];
       }
     }
     if constexpr (WITH_V) {
@@ -87,22 +99,19 @@ struct TileStage {
 #pragma unroll
       for (int s = 0; s < NV; ++s) {
         const int x = tid + s * NT;
-        if (x < 16 * L::CPR) {
-          const int kq = x / L::CPR, c = x - (x / L::CPR) * L::CPR;
+        if (kExactV || x < 32 * L::CPR) {
+          const int kp = x & 31, c = x >> 5;
 #pragma unroll
           for (int e = 0; e < L::EPC; ++e) {
-            ST* dst = vt + (c * L::EPC + e) * L::VPE + 4 * kq;
+            ST* dst = vt + (c * L::EPC + e) * L::VPE + 2 * kp;
             if constexpr (TR::kBytes == 2) {
               const int w = e >> 1, sh = 16 * (e & 1);
-              const uint32_t a0 = (reinterpret_cast<const uint32_t*>(&vr[s][0])[w] >> sh) & 0xFFFFu;
-              const uint32_t a1 = (reinterpret_cast<const uint32_t*>(&vr[s][1])[w] >> sh) & 0xFFFFu;
-              const uint32_t a2 = (reinterpret_cast<const uint32_t*>(&vr[s][2])[w] >> sh) & 0xFFFFu;
-              const uint32_t a3 = (reinterpret_cast<const uint32_t*>(&vr[s][3])[w] >> sh) & 0xFFFFu;
-              *reinterpret_cast<uint2*>(dst) = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+              const uint32_t a0 = (vr[s][0][w] >> sh) & 0xFFFFu;
+              const uint32_t a1 = (vr[s][1][w] >> sh) & 0xFFFFu;
+              *reinterpret_cast<uint32_t*>(dst) = a0 | (a1 << 16);
             } else {
-              *reinterpret_cast<float4*>(dst) =
-                  make_float4(reinterpret_cast<const float*>(&vr[s][0])[e], reinterpret_cast<const float*>(&vr[s][1])[e],
-                              reinterpret_cast<const float*>(&vr[s][2])[e], reinterpret_cast<const float*>(&vr[s][3])[e]);
+              typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+              *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{vr[s][0][e], vr[s][1][e]};
             }
           }
         }
@@ -150,10 +159,18 @@ struct RowState {
   }
 };
 
-// One wave attends its RTW row tiles to the staged tile.  valid(rt, j) says
-// whether key j may be used by the lane's row (l % 16) of row tile rt;
-// j < 0 marks an invalid tile entry.
-template <typename TR, int D, int RTW, class Valid>
+// Lazy rescaling: a row's running max m is only raised when some logit of the
+// tile exceeds it by more than this many powers of two, so unnormalised
+// probabilities stay below 2^kRescaleSlack and the O rescale (and its
+// cross-lane traffic) is skipped for most tiles.  O / l is unchanged: m
+// cancels between numerator and denominator.
+constexpr float kRescaleSlack = 8.f;
+
+// One wave attends its RTW row tiles to the staged tile.  MASK = false when
+// every tile entry is a valid key that every row of the wave may use;
+// otherwise valid(rt, j) says whether key j may be used by the lane's row
+// (l % 16) of row tile rt, and j < 0 marks an invalid tile entry.
+template <typename TR, int D, int RTW, bool MASK, class Valid>
 __device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename TR::frag (&qf)[RTW][D / 32],
                                             const unsigned char* sm, const int* kj, float sl2, Valid valid) {
   using frag = typename TR::frag;
@@ -173,43 +190,52 @@ __device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename
     }
   }
   int jj[4][4];
+  if constexpr (MASK) {
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) jj[kt][r] = kj[16 * kt + 4 * quad + r];
+      for (int r = 0; r < 4; ++r) jj[kt][r] = kj[16 * kt + 4 * quad + r];
+  }
   frag pa[RTW][2];
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
     float s[4][4];
-    float mt = kNegInf;
+    float lm = kNegInf;  // lane-local max of the raw logits
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = jj[kt][r];
-        s[kt][r] = (j >= 0 && valid(rt, j)) ? sacc[rt][kt][r] * sl2 : kNegInf;
-        mt = fmaxf(mt, s[kt][r]);
+        if constexpr (MASK) {
+          const int j = jj[kt][r];
+          s[kt][r] = (j >= 0 && valid(rt, j)) ? sacc[rt][kt][r] : kNegInf;
+        } else {
+          s[kt][r] = sacc[rt][kt][r];
+        }
+        lm = fmaxf(lm, s[kt][r]);
       }
-    mt = wave_max16x4(mt);
-    const float m_new = fmaxf(st.m[rt], mt);
-    const float mu = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = exp2f(st.m[rt] - mu);
+    // scale > 0, so max(raw) * sl2 is the max of the scaled logits
+    if (__builtin_amdgcn_ballot_w64(lm * sl2 > st.m[rt] + kRescaleSlack)) {
+      const float m_new = fmaxf(st.m[rt], wave_max16x4(lm) * sl2);
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(st.m[rt] - m_new);
+      st.l[rt] *= alpha;
+      st.m[rt] = m_new;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, 4 * quad + r);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) st.o[rt][dt][r] *= ar;
+      }
+    }
+    const float nmu = (st.m[rt] == kNegInf) ? 0.f : -st.m[rt];
     float ls = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s[kt][r] = exp2f(s[kt][r] - mu);
+        s[kt][r] = fast_exp2(fmaf(s[kt][r], sl2, nmu));
         ls += s[kt][r];
       }
-    st.l[rt] = st.l[rt] * alpha + ls;
-    st.m[rt] = m_new;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float ar = __shfl(alpha, 4 * quad + r);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) st.o[rt][dt][r] *= ar;
-    }
+    st.l[rt] += ls;
     pa[rt][0] = TR::pack(s[0], s[1]);
     pa[rt][1] = TR::pack(s[2], s[3]);
   }
@@ -221,6 +247,14 @@ __device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt) TR::mma(st.o[rt][dt], pa[rt][kk], vb);
     }
+}
+
+// Whether a wave must mask a staged tile: some entry is invalid (j < 0) or
+// lies after `pos_min`, the smallest position among the wave's rows.  One
+// LDS read per lane and a ballot; the result is wave-uniform.
+__device__ __forceinline__ bool tile_needs_mask(const int* kj, int pos_min) {
+  const int j = kj[threadIdx.x & 63];
+  return __builtin_amdgcn_ballot_w64(j < 0 || j > pos_min) != 0;
 }
 
 }  // namespace hys

@@ -25,11 +25,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// float -> bf16, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+
+// 2^x with one v_exp_f32: results below 2^-126 flush to zero (a probability
+// that small is below any tolerance of the sums it enters).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -67,11 +74,8 @@ struct BF16 {
   __device__ static __forceinline__ float to_float(storage x) { return bf16_to_f32(x); }
   // pack two groups of four floats (RNE) into one fragment
   __device__ static __forceinline__ frag pack(const float* lo4, const float* hi4) {
-    uint4 u;
-    u.x = (uint32_t)f32_to_bf16_rne(lo4[0]) | ((uint32_t)f32_to_bf16_rne(lo4[1]) << 16);
-    u.y = (uint32_t)f32_to_bf16_rne(lo4[2]) | ((uint32_t)f32_to_bf16_rne(lo4[3]) << 16);
-    u.z = (uint32_t)f32_to_bf16_rne(hi4[0]) | ((uint32_t)f32_to_bf16_rne(hi4[1]) << 16);
-    u.w = (uint32_t)f32_to_bf16_rne(hi4[2]) | ((uint32_t)f32_to_bf16_rne(hi4[3]) << 16);
+    const u32x4_t u = {pack_bf16x2(lo4[0], lo4[1]), pack_bf16x2(lo4[2], lo4[3]), pack_bf16x2(hi4[0], hi4[1]),
+                       pack_bf16x2(hi4[2], hi4[3])};
     return __builtin_bit_cast(frag, u);
   }
   // four consecutive elements (8 bytes, 8-byte aligned) as a raw vector
@@ -138,16 +142,35 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 // between lanes of one wave exchanging data through a wave-private LDS region.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Cross-row exchange with the gfx950 permlane swaps.  With both operands the
+// same register, permlane16_swap returns, in every lane l, the values of lanes
+// (l & ~16) and (l | 16); permlane32_swap those of (l & ~32) and (l | 32).
+__device__ __forceinline__ void pair16(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
+// max / sum over the four lanes l, l^16, l^32, l^48 that share (l % 16); the
+// sum is formed in the same order in all four lanes (bit-identical results)
 __device__ __forceinline__ float wave_max16x4(float x) {
-  // max over the four lanes l, l^16, l^32, l^48 that share (l % 16)
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  float a, b;
+  pair16(x, a, b);
+  x = fmaxf(a, b);
+  pair32(x, a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float wave_sum16x4(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  float a, b;
+  pair16(x, a, b);
+  x = a + b;
+  pair32(x, a, b);
+  return a + b;
 }
 
 }  // namespace hys

@@ -53,6 +53,12 @@ struct PrefillArgs {
   int nrc;                // row chunks per score block
 };
 
+__device__ __forceinline__ int wave_min_int(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = min(x, __shfl_xor(x, off));
+  return x;
+}
+
 template <typename TR, int D>
 __device__ __forceinline__ void load_q_frags(const PrefillArgs& a, int b, int i, int h, bool ok, int quad,
                                              typename TR::frag (&qf)[D / 32]) {
@@ -89,6 +95,12 @@ __global__ __launch_bounds__(kNW * 64) void prefill_fwd_kernel(PrefillArgs a) {
     rpos[rt] = ok ? a.Tkv - a.Tq + i : -1;
     load_q_frags<TR, D>(a, b, i, g * a.G + hc * a.HW + hl, ok, quad, qf[rt]);
   }
+  // smallest position among the wave's rows (rows past Tq are discarded): a
+  // tile whose last key is not after it needs no causal mask
+  int pmin = 0x7fffffff;
+#pragma unroll
+  for (int rt = 0; rt < kRTW; ++rt) pmin = rpos[rt] >= 0 ? min(pmin, rpos[rt]) : pmin;
+  pmin = wave_min_int(pmin);
   const int last_i = min(i0 + a.QTW, a.Tq) - 1;
   const int pos_max = a.Tkv - a.Tq + last_i;
   const int nkt = pos_max / kTK + 1;
@@ -108,7 +120,11 @@ __global__ __launch_bounds__(kNW * 64) void prefill_fwd_kernel(PrefillArgs a) {
       const int t0 = (it + 1) * kTK;
       stg.load(kbase, vbase, a.ks_t, [=](int t) { return t0 + t < Tkv ? t0 + t : -1; });
     }
-    attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, [&](int rt, int j) { return j <= rpos[rt]; });
+    auto causal = [&](int rt, int j) { return j <= rpos[rt]; };
+    if ((it + 1) * kTK - 1 > pmin)
+      attend_tile<TR, D, kRTW, true>(st, qf, sm, kj, a.sl2, causal);
+    else
+      attend_tile<TR, D, kRTW, false>(st, qf, sm, kj, a.sl2, causal);
   }
 
 #pragma unroll
@@ -141,6 +157,169 @@ __global__ __launch_bounds__(kNW * 64) void prefill_fwd_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------- sweep 2: scores
+// One staged tile for the streaming score sweep: per key, the sum of P over
+// the wave's RTW row tiles, written to wred[key] (lanes of quad 0).
+template <typename TR, int D, int RTW, bool MASK>
+__device__ __forceinline__ void block_score_tile(const typename TR::frag (&qf)[RTW][D / 32],
+                                                 const float (&nl)[RTW][4], const int (&rowpos)[RTW][4],
+                                                 const unsigned char* sm, const int* kj, float sl2, float* wred) {
+  constexpr int KC = D / 32;
+  const int lane = threadIdx.x & 63, col = lane & 15, quad = lane >> 4;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    typename TR::frag kf[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) kf[c] = lds_k_frag<TR, D>(sm, ct, c, col, quad);
+    const int j = MASK ? kj[16 * ct + col] : 0;
+    float pr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int x = 0; x < RTW; ++x) {
+      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) TR::mma(s, qf[x][c], kf[c]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(fmaf(s[r], sl2, nl[x][r]));
+        if constexpr (MASK)
+          pr[r] += (j >= 0 && j <= rowpos[x][r]) ? p : 0.f;
+        else
+          pr[r] += p;
+      }
+    }
+    const float v = wave_sum16x4(pr[0] + pr[1] + pr[2] + pr[3]);
+    if (quad == 0) wred[16 * ct + col] = v;
+  }
+}
+
+// One staged 64-key tile of the score sweep for a wave's RTW row tiles:
+// P = 2^(logit2 - lse2) per (row, key), summed into the wave's partials.
+template <typename TR, int D, int SB, int RTW, int R, bool MASK>
+__device__ __forceinline__ void score_tile(const typename TR::frag (&qf)[RTW][D / 32], const float (&nl)[RTW][4],
+                                           const int (&rowpos)[RTW][4], const unsigned char* sm, const int* kj,
+                                           float sl2, float* wred, int it) {
+  constexpr int KC = D / 32;
+  const int lane = threadIdx.x & 63, col = lane & 15, quad = lane >> 4;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    typename TR::frag kf[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) kf[c] = lds_k_frag<TR, D>(sm, ct, c, col, quad);
+    const int j = MASK ? kj[16 * ct + col] : 0;
+    float pr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int x = 0; x < RTW; ++x) {
+      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) TR::mma(s, qf[x][c], kf[c]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(fmaf(s[r], sl2, nl[x][r]));
+        if constexpr (MASK)
+          pr[r] += (j >= 0 && j <= rowpos[x][r]) ? p : 0.f;
+        else
+          pr[r] += p;
+      }
+    }
+    const int kc = it * kTK + 16 * ct + col;  // key within the range
+    if constexpr (SB == 64) {
+      const float v = wave_sum16x4(pr[0] + pr[1] + pr[2] + pr[3]);
+      if (quad == 0) wred[kc] += v;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wred[(4 * quad + r) * R + kc] += pr[r];
+    }
+  }
+}
+
+// SB = 64, streaming form: one workgroup per (b, g, score block n), longest
+// prefixes first, so that the workgroups of one KV group run together (the
+// groups of consecutive workgroups are dealt to different XCDs) and share its
+// key tiles in that XCD's L2.  The block's 64 queries x G heads are covered in
+// passes of NW * RTW row tiles (row tile rt: head rt / 4, queries
+// 16 * (rt % 4) ..); every pass streams keys [0, last(n)] through LDS.  Per
+// tile each wave sums P over its rows per key into red[wave][key]; the
+// workgroup adds the wave sums in a fixed order and writes S (first pass) or
+// adds to it (later passes; the same thread owns the same key in every pass).
+template <typename TR, int D, int kNW, int kRTW>
+__global__ __launch_bounds__(kNW * 64) void prefill_block_scores_kernel(PrefillArgs a) {
+  constexpr int kNT = kNW * 64;
+  using ST = typename TR::storage;
+  using L = TileLayout<TR, D>;
+  constexpr int KC = D / 32;
+  __shared__ __align__(16) unsigned char sm[L::kKBytes];
+  __shared__ int kj[kTK];
+  __shared__ float red[kNW * kTK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, quad = lane >> 4;
+  const int per_n = a.B * a.Hkv;
+  const int n = a.NB - 1 - (int)(blockIdx.x / per_n);
+  const int bg = blockIdx.x - (blockIdx.x / per_n) * per_n;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int i0 = n * 64, i1 = min(i0 + 64, a.Tq);
+  const int pos_last = a.Tkv - a.Tq + i1 - 1;
+  const int nkt = pos_last / kTK + 1;
+  const int RT = 4 * a.G;
+  const int npass = (RT + kNW * kRTW - 1) / (kNW * kRTW);
+  const int Tkv = a.Tkv;
+  float* srow = a.scores + ((int64_t)bg * a.NB + n) * Tkv;
+  const ST* kbase = (const ST*)a.k + (int64_t)b * a.ks_b + (int64_t)g * a.ks_h;
+
+  // keys after the last tile are 0 for this block
+  for (int j = nkt * kTK + tid; j < Tkv; j += kNT) srow[j] = 0.f;
+
+  for (int ps = 0; ps < npass; ++ps) {
+    typename TR::frag qf[kRTW][KC];
+    float nl[kRTW][4];
+    int rowpos[kRTW][4];
+    int pmin = 0x7fffffff;
+#pragma unroll
+    for (int x = 0; x < kRTW; ++x) {
+      const int rt = ps * kNW * kRTW + wave * kRTW + x;
+      const int hl = rt / 4, qoff = 16 * (rt % 4);
+      {
+        const int i = i0 + qoff + col;
+        load_q_frags<TR, D>(a, b, i, g * a.G + hl, rt < RT && i < a.Tq, quad, qf[x]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + qoff + 4 * quad + r;
+        const bool ok = rt < RT && i < a.Tq;
+        rowpos[x][r] = ok ? a.Tkv - a.Tq + i : -1;
+        nl[x][r] = ok ? -a.lse2[((int64_t)b * a.Hq + g * a.G + hl) * a.Tq + i] : kNegInf;
+        pmin = ok ? min(pmin, rowpos[x][r]) : pmin;
+      }
+    }
+    pmin = wave_min_int(pmin);
+    auto flush = [&](int t) {  // tile t's key sums -> S (threads 0..63)
+      const int j = t * kTK + tid;
+      if (j < Tkv) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) v += red[w * kTK + tid];
+        srow[j] = ps == 0 ? v : srow[j] + v;
+      }
+    };
+    TileStage<TR, D, kNT, false> stg;
+    stg.load(kbase, kbase, a.ks_t, [=](int t) { return t < Tkv ? t : -1; });
+    for (int it = 0; it < nkt; ++it) {
+      __syncthreads();
+      if (it > 0 && tid < kTK) flush(it - 1);
+      stg.store(sm, kj);
+      __syncthreads();
+      if (it + 1 < nkt) {
+        const int t0 = (it + 1) * kTK;
+        stg.load(kbase, kbase, a.ks_t, [=](int t) { return t0 + t < Tkv ? t0 + t : -1; });
+      }
+      if (tile_needs_mask(kj, pmin))
+        block_score_tile<TR, D, kRTW, true>(qf, nl, rowpos, sm, kj, a.sl2, red + wave * kTK);
+      else
+        block_score_tile<TR, D, kRTW, false>(qf, nl, rowpos, sm, kj, a.sl2, red + wave * kTK);
+    }
+    __syncthreads();
+    if (tid < kTK) flush(nkt - 1);
+  }
+}
+
+// Score sweep by key ranges (used for score_block 1).
 // SB = 64: rows of a workgroup = the block's 64 queries x G heads (row tile
 //          rt = head rt / 4, queries 16 * (rt % 4) ..); output one score row.
 // SB = 1 : rows = 16 queries x G heads (row tile rt = head rt); output 16 rows.
@@ -184,8 +363,9 @@ __global__ __launch_bounds__(kNW * 64) void prefill_scores_kernel(PrefillArgs a)
     float* wred = red + (SB == 64 ? wave * R : wave * 16 * R);
     for (int ps = 0; ps < npass; ++ps) {
       typename TR::frag qf[kRTW][KC];
-      float lrow[kRTW][4];
+      float nl[kRTW][4];  // -lse2 of the accumulator rows
       int rowpos[kRTW][4];
+      int pmin = 0x7fffffff;
 #pragma unroll
       for (int x = 0; x < kRTW; ++x) {
         const int rt = ps * kNW * kRTW + wave * kRTW + x;
@@ -201,9 +381,12 @@ __global__ __launch_bounds__(kNW * 64) void prefill_scores_kernel(PrefillArgs a)
           const int i = i0 + qoff + 4 * quad + r;
           const bool ok = rt < RT && i < a.Tq;
           rowpos[x][r] = ok ? a.Tkv - a.Tq + i : -1;
-          lrow[x][r] = ok ? a.lse2[((int64_t)b * a.Hq + g * a.G + hl) * a.Tq + i] : 0.f;
+          // padding rows get P = 2^-inf = 0, also on tiles taken unmasked
+          nl[x][r] = ok ? -a.lse2[((int64_t)b * a.Hq + g * a.G + hl) * a.Tq + i] : kNegInf;
+          pmin = ok ? min(pmin, rowpos[x][r]) : pmin;
         }
       }
+      pmin = wave_min_int(pmin);
       TileStage<TR, D, kNT, false> stg;
       stg.load(kbase, kbase, a.ks_t, [=](int t) { return r0 + t < Tkv ? r0 + t : -1; });
       for (int it = 0; it < nkt; ++it) {
@@ -214,31 +397,10 @@ __global__ __launch_bounds__(kNW * 64) void prefill_scores_kernel(PrefillArgs a)
           const int t0 = r0 + (it + 1) * kTK;
           stg.load(kbase, kbase, a.ks_t, [=](int t) { return t0 + t < Tkv ? t0 + t : -1; });
         }
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          typename TR::frag kf[KC];
-#pragma unroll
-          for (int c = 0; c < KC; ++c) kf[c] = lds_k_frag<TR, D>(sm, ct, c, col, quad);
-          const int j = kj[16 * ct + col];
-          float pr[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int x = 0; x < kRTW; ++x) {
-            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < KC; ++c) TR::mma(s, qf[x][c], kf[c]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              pr[r] += (j >= 0 && j <= rowpos[x][r]) ? exp2f(s[r] * a.sl2 - lrow[x][r]) : 0.f;
-          }
-          const int kc = it * kTK + 16 * ct + col;  // key within the range
-          if constexpr (SB == 64) {
-            const float v = wave_sum16x4(pr[0] + pr[1] + pr[2] + pr[3]);
-            if (quad == 0) wred[kc] += v;
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) wred[(4 * quad + r) * R + kc] += pr[r];
-          }
-        }
+        if (tile_needs_mask(kj, pmin))
+          score_tile<TR, D, SB, kRTW, R, true>(qf, nl, rowpos, sm, kj, a.sl2, wred, it);
+        else
+          score_tile<TR, D, SB, kRTW, R, false>(qf, nl, rowpos, sm, kj, a.sl2, wred, it);
       }
     }
   }
@@ -307,6 +469,10 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
     load_q_frags<TR, D>(a, b, i, g * a.G + hl, ok, quad, qf[x]);
     gt[x] = tile_ok[x] ? 1.f / (1.f + expf(-a.gate[g * a.G + hl])) : 0.f;
   }
+  int pmin = 0x7fffffff;  // smallest position among the wave's rows
+#pragma unroll
+  for (int x = 0; x < kRTW; ++x) pmin = rpos[x] >= 0 ? min(pmin, rpos[x]) : pmin;
+  pmin = wave_min_int(pmin);
   const ST* kbase = (const ST*)a.k + (int64_t)b * a.ks_b + (int64_t)g * a.ks_h;
   const ST* vbase = (const ST*)a.v + (int64_t)b * a.ks_b + (int64_t)g * a.ks_h;
   const int W = a.window;
@@ -340,11 +506,16 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
     const int any = __syncthreads_or(tid < kTK && stg.jk >= 0);
     if (it + 1 < ntiles) stg.load(kbase, vbase, a.ks_t, key_of(it + 1));
     if (any) {
-      if (it < nwt)
-        attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2,
-                                 [&](int rt, int j) { return j <= rpos[rt] && j > rpos[rt] - W; });
-      else
-        attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, [&](int rt, int j) { return j <= rpos[rt]; });
+      if (it < nwt) {
+        attend_tile<TR, D, kRTW, true>(st, qf, sm, kj, a.sl2,
+                                       [&](int rt, int j) { return j <= rpos[rt] && j > rpos[rt] - W; });
+      } else {
+        auto causal = [&](int rt, int j) { return j <= rpos[rt]; };
+        if (tile_needs_mask(kj, pmin))
+          attend_tile<TR, D, kRTW, true>(st, qf, sm, kj, a.sl2, causal);
+        else
+          attend_tile<TR, D, kRTW, false>(st, qf, sm, kj, a.sl2, causal);
+      }
     }
     if (it == nwt - 1) {
       // window branch done: keep (1 - g) * o_window, restart for the global branch
@@ -452,10 +623,8 @@ hipError_t launch_full_prefill(const Geom& g, const void* q, const void* k, cons
       prefill_fwd_kernel<TR, DD, kFwdNW, kFwdRTW><<<a.nqt * g.B * g.Hkv * a.NHC, kFwdNW * 64, 0, st>>>(a);
     }
     if (score_block == 64) {
-      a.nqb = a.NB;
-      a.nkr = (g.Tkv + 511) / 512;
       TraceScope ts(st, "full_prefill_scores");
-      prefill_scores_kernel<TR, DD, 64, kScNW, kScRTW><<<a.nqb * g.B * g.Hkv * a.nkr, kScNW * 64, 0, st>>>(a);
+      prefill_block_scores_kernel<TR, DD, kScNW, kScRTW><<<a.NB * g.B * g.Hkv, kScNW * 64, 0, st>>>(a);
     } else {
       a.nqb = (g.Tq + 15) / 16;
       a.nkr = (g.Tkv + 127) / 128;

@@ -27,6 +27,7 @@ KERNELS = {  # symbol fragment -> name used by the library's trace hook
     "topk_row_kernel": "topk",
     "prefill_fwd_kernel": "full_prefill_fwd",
     "prefill_scores_kernel": "full_prefill_scores",
+    "prefill_block_scores_kernel": "full_prefill_scores",
     "sparse_block_kernel": "sparse_prefill",
 }
 
