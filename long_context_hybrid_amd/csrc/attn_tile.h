@@ -196,26 +196,30 @@ __device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename
 #pragma unroll
       for (int r = 0; r < 4; ++r) jj[kt][r] = kj[16 * kt + 4 * quad + r];
   }
-  frag pa[RTW][2];
+  // masked logits in place, lane-local maxima, and one vote per tile on
+  // whether any row must raise its running max
+  float lm[RTW];
+  bool over = false;
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
-    float s[4][4];
-    float lm = kNegInf;  // lane-local max of the raw logits
+    lm[rt] = kNegInf;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if constexpr (MASK) {
           const int j = jj[kt][r];
-          s[kt][r] = (j >= 0 && valid(rt, j)) ? sacc[rt][kt][r] : kNegInf;
-        } else {
-          s[kt][r] = sacc[rt][kt][r];
+          if (!(j >= 0 && valid(rt, j))) sacc[rt][kt][r] = kNegInf;
         }
-        lm = fmaxf(lm, s[kt][r]);
+        lm[rt] = fmaxf(lm[rt], sacc[rt][kt][r]);
       }
     // scale > 0, so max(raw) * sl2 is the max of the scaled logits
-    if (__builtin_amdgcn_ballot_w64(lm * sl2 > st.m[rt] + kRescaleSlack)) {
-      const float m_new = fmaxf(st.m[rt], wave_max16x4(lm) * sl2);
+    over = over || (lm[rt] * sl2 > st.m[rt] + kRescaleSlack);
+  }
+  if (__builtin_amdgcn_ballot_w64(over)) {
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const float m_new = fmaxf(st.m[rt], wave_max16x4(lm[rt]) * sl2);
       const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(st.m[rt] - m_new);
       st.l[rt] *= alpha;
       st.m[rt] = m_new;
@@ -226,18 +230,23 @@ __device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename
         for (int dt = 0; dt < DT; ++dt) st.o[rt][dt][r] *= ar;
       }
     }
+  }
+  frag pa[RTW][2];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) {
     const float nmu = (st.m[rt] == kNegInf) ? 0.f : -st.m[rt];
+    float p[4][4];
     float ls = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s[kt][r] = fast_exp2(fmaf(s[kt][r], sl2, nmu));
-        ls += s[kt][r];
+        p[kt][r] = fast_exp2(fmaf(sacc[rt][kt][r], sl2, nmu));
+        ls += p[kt][r];
       }
     st.l[rt] += ls;
-    pa[rt][0] = TR::pack(s[0], s[1]);
-    pa[rt][1] = TR::pack(s[2], s[3]);
+    pa[rt][0] = TR::pack(p[0], p[1]);
+    pa[rt][1] = TR::pack(p[2], p[3]);
   }
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)

@@ -25,12 +25,27 @@ namespace hys {
 namespace {
 
 // Launch shapes (waves per workgroup NW x row tiles per wave RTW; 16 rows per
-// row tile).  Measured on MI355X: 8 waves x 2 row tiles (2 waves per SIMD)
-// beat 4 x 4 (1 wave per SIMD, half the LDS reads per MFMA) by 1.5x; the
-// second wave per SIMD hides the tile loads and the softmax.
-constexpr int kFwdNW = 8, kFwdRTW = 2;      // full layer, forward sweep
-constexpr int kScNW = 8, kScRTW = 2;        // full layer, score sweep
-constexpr int kSpNW = 8, kSpRTW = 1;        // sparse layer (two output states per row)
+// row tile), measured on MI355X at 32K: forward 8 x 2 (2 waves per SIMD) beats
+// 4 x 4 by 1.3x, the second wave hiding the tile loads and the softmax; the
+// score sweep (no O accumulators, one exp per product) prefers 4 x 4 (half
+// the LDS reads per MFMA) by 1.2x; the sparse layer keeps two output states
+// per row and fits only 8 x 1 without spills (4 x 2 is 1.25x slower).
+#ifndef HYS_FWD_SHAPE
+#define HYS_FWD_SHAPE 8, 2, 2
+#endif
+#ifndef HYS_SC_SHAPE
+#define HYS_SC_SHAPE 4, 4
+#endif
+#ifndef HYS_SP_SHAPE
+#define HYS_SP_SHAPE 8, 1
+#endif
+constexpr int kFwdShape[3] = {HYS_FWD_SHAPE};  // full layer, forward sweep (+ min waves per SIMD)
+constexpr int kScShape[2] = {HYS_SC_SHAPE};    // full layer, score sweep
+constexpr int kSpShape[2] = {HYS_SP_SHAPE};    // sparse layer (two output states per row)
+constexpr int kFwdNW = kFwdShape[0], kFwdRTW = kFwdShape[1], kFwdWPE = kFwdShape[2];
+constexpr int kScNW = kScShape[0], kScRTW = kScShape[1];
+constexpr int kSpNW = kSpShape[0], kSpRTW = kSpShape[1];
+constexpr int kIdxCh = 1024;                // sparse layer: selected indices staged in LDS per refill
 
 struct PrefillArgs {
   const void* q;
@@ -69,8 +84,8 @@ __device__ __forceinline__ void load_q_frags(const PrefillArgs& a, int b, int i,
 }
 
 // ------------------------------------------------------------- sweep 1: fwd
-template <typename TR, int D, int kNW, int kRTW>
-__global__ __launch_bounds__(kNW * 64) void prefill_fwd_kernel(PrefillArgs a) {
+template <typename TR, int D, int kNW, int kRTW, int kWPE>
+__global__ __launch_bounds__(kNW * 64, kWPE) void prefill_fwd_kernel(PrefillArgs a) {
   constexpr int kNT = kNW * 64;
   using ST = typename TR::storage;
   using L = TileLayout<TR, D>;
@@ -436,6 +451,7 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
   constexpr int KC = D / 32, DT = D / 16;
   __shared__ __align__(16) unsigned char sm[L::kBytes];
   __shared__ int kj[kTK];
+  __shared__ int idx_stage[kIdxCh];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, quad = lane >> 4;
 
   // the row chunks of one block share their gathered rows: keep them on one
@@ -481,6 +497,17 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
   const int ngt = (a.k_top + kTK - 1) / kTK;
   const int32_t* idx_row = a.idx + ((int64_t)(b * a.Hkv + g) * a.NB + n) * a.k_top;
   const int ktop = a.k_top;
+  // The selected indices are staged in LDS kIdxCh at a time (validated: -1
+  // for padding and for keys after the block), so a gathered tile's row loads
+  // do not wait on an index load from global memory.
+  int* idx_s = idx_stage;
+  auto refill = [&](int e0) {
+    for (int x = tid; x < kIdxCh; x += kNT) {
+      const int e = e0 + x;
+      int j = e < ktop ? idx_row[e] : -1;
+      idx_s[x] = (j >= 0 && j <= pos_last) ? j : -1;
+    }
+  };
   auto key_of = [=](int tile) {
     return [=](int t) -> int {
       if (tile < nwt) {
@@ -488,12 +515,12 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
         return j <= pos_last ? j : -1;
       }
       const int e = (tile - nwt) * kTK + t;
-      if (e >= ktop) return -1;
-      const int j = idx_row[e];
-      return (j >= 0 && j <= pos_last) ? j : -1;
+      return e < ktop ? idx_s[e & (kIdxCh - 1)] : -1;
     };
   };
 
+  refill(0);
+  __syncthreads();
   TileStage<TR, D, kNT, true> stg;
   stg.load(kbase, vbase, a.ks_t, key_of(0));
   RowState<kRTW, D> st;
@@ -504,7 +531,14 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
     __syncthreads();
     stg.store(sm, kj);
     const int any = __syncthreads_or(tid < kTK && stg.jk >= 0);
-    if (it + 1 < ntiles) stg.load(kbase, vbase, a.ks_t, key_of(it + 1));
+    if (it + 1 < ntiles) {
+      const int e1 = (it + 1 - nwt) * kTK;  // first list entry of the next tile
+      if (e1 > 0 && (e1 & (kIdxCh - 1)) == 0) {
+        refill(e1);  // the previous chunk's last reader was load(it), before the barrier above
+        __syncthreads();
+      }
+      stg.load(kbase, vbase, a.ks_t, key_of(it + 1));
+    }
     if (any) {
       if (it < nwt) {
         attend_tile<TR, D, kRTW, true>(st, qf, sm, kj, a.sl2,
@@ -620,7 +654,7 @@ hipError_t launch_full_prefill(const Geom& g, const void* q, const void* k, cons
   HYS_PF_DISPATCH(g, {
     {
       TraceScope ts(st, "full_prefill_fwd");
-      prefill_fwd_kernel<TR, DD, kFwdNW, kFwdRTW><<<a.nqt * g.B * g.Hkv * a.NHC, kFwdNW * 64, 0, st>>>(a);
+      prefill_fwd_kernel<TR, DD, kFwdNW, kFwdRTW, kFwdWPE><<<a.nqt * g.B * g.Hkv * a.NHC, kFwdNW * 64, 0, st>>>(a);
     }
     if (score_block == 64) {
       TraceScope ts(st, "full_prefill_scores");
