@@ -355,6 +355,12 @@ __global__ __launch_bounds__(D) void sparse_merge_kernel(DecodeArgs a) {
   const int i = unit % a.Tq, bg = unit / a.Tq;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const float* pml = a.part_ml + (int64_t)unit * a.nsplit * a.G * 2;
+  // this thread's output element of every split, loaded before the weights
+  // are known so that both reads are in flight together
+  const float* po = a.part_o + (int64_t)unit * a.nsplit * a.G * D + (int64_t)h * D + tid;
+  float pv[kMaxSparseSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSparseSplits; ++sp) pv[sp] = sp < a.nsplit ? po[(int64_t)sp * a.G * D] : 0.f;
   // weights: lanes 0..nsg-1 of wave 0 handle the global splits, the next
   // lanes the window splits (nsplit <= 64)
   if (tid < 64) {
@@ -384,10 +390,10 @@ __global__ __launch_bounds__(D) void sparse_merge_kernel(DecodeArgs a) {
     if (in) wts[sp] = w * scale;
   }
   __syncthreads();
-  const float* po = a.part_o + (int64_t)unit * a.nsplit * a.G * D + (int64_t)h * D + tid;
   float acc = 0.f;
-#pragma unroll 4
-  for (int sp = 0; sp < a.nsplit; ++sp) acc += wts[sp] * po[(int64_t)sp * a.G * D];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSparseSplits; ++sp)
+    if (sp < a.nsplit) acc += wts[sp] * pv[sp];
   reinterpret_cast<typename TR::storage*>(a.out)[(((int64_t)b * a.Tq + i) * a.Hq + g * a.G + h) * D + tid] =
       TR::from_float(acc);
 }

@@ -130,7 +130,16 @@ struct HierWs {
   float* cand;
   int32_t* valid;
   int32_t* pos;
+  void* topk_ws;  // shared by the two top-K calls (they run in order)
 };
+
+size_t hier_topk_ws(const Geom& g, int block, int n_keep, int k_top) {
+  const int M = (g.Tkv + block - 1) / block;
+  const int64_t rows = (int64_t)g.B * g.Hkv;
+  const size_t a = topk_ws_bytes(rows, M, n_keep);
+  const size_t b = topk_ws_bytes(rows, (int32_t)((int64_t)n_keep * block), k_top);
+  return a > b ? a : b;
+}
 
 HierWs carve(const Geom& g, int block, int n_keep, int k_top, void* ws) {
   const int M = (g.Tkv + block - 1) / block;
@@ -150,6 +159,8 @@ HierWs carve(const Geom& g, int block, int n_keep, int k_top, void* ws) {
   w.valid = reinterpret_cast<int32_t*>(c);
   c += align_up((size_t)rows * sizeof(int32_t));
   w.pos = reinterpret_cast<int32_t*>(c);
+  c += align_up((size_t)rows * k_top * sizeof(int32_t));
+  w.topk_ws = c;
   return w;
 }
 
@@ -163,7 +174,8 @@ size_t hier_ws_bytes(const Geom& g, int block, int n_keep, int k_top) {
   return align_up((size_t)g.B * M * g.Hkv * g.D * sizeof(float)) + align_up((size_t)rows * g.G * M * sizeof(float)) +
          align_up((size_t)rows * M * sizeof(float)) +
          align_up((size_t)rows * n_keep * sizeof(int32_t)) + align_up((size_t)rows * n_keep * block * sizeof(float)) +
-         align_up((size_t)rows * sizeof(int32_t)) + align_up((size_t)rows * k_top * sizeof(int32_t));
+         align_up((size_t)rows * sizeof(int32_t)) + align_up((size_t)rows * k_top * sizeof(int32_t)) +
+         hier_topk_ws(g, block, n_keep, k_top);
 }
 
 hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const float* scores, int block, int n_keep,
@@ -200,7 +212,7 @@ hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const
   });
 #undef HIER_DT
   ValidLen all{nullptr, M, 0, 1, 1, 1, 1};
-  if ((e = launch_topk(bscore, rows, M, M, all, n_keep, blk, nullptr, st)) != hipSuccess) return e;
+  if ((e = launch_topk(bscore, rows, M, M, all, n_keep, blk, w.topk_ws, st)) != hipSuccess) return e;
   const int64_t ncand = (int64_t)n_keep * block;
   {
     TraceScope ts(st, "hier_gather");
@@ -209,7 +221,7 @@ hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const
     gather_candidates_kernel<<<dim3(gx, rows), 256, 0, st>>>(scores, g.Tkv, blk, n_keep, block, w.cand, w.valid);
   }
   ValidLen vl{w.valid, (int32_t)ncand, 0, 1, 1, 1, 1};
-  if ((e = launch_topk(w.cand, rows, (int32_t)ncand, ncand, vl, k_top, w.pos, nullptr, st)) != hipSuccess) return e;
+  if ((e = launch_topk(w.cand, rows, (int32_t)ncand, ncand, vl, k_top, w.pos, w.topk_ws, st)) != hipSuccess) return e;
   {
     TraceScope ts(st, "hier_map");
     const int64_t n = (int64_t)rows * k_top;

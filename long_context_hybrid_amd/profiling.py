@@ -25,6 +25,8 @@ KERNELS = {  # symbol fragment -> name used by the library's trace hook
     "decode_split_kernel<hys::BF16, 128, false>": "sparse_decode",
     "sparse_merge_kernel": "sparse_merge",
     "topk_row_kernel": "topk",
+    "topk_part_kernel": "topk_part",
+    "topk_select_kernel": "topk_select",
     "prefill_fwd_kernel": "full_prefill_fwd",
     "prefill_scores_kernel": "full_prefill_scores",
     "prefill_block_scores_kernel": "full_prefill_scores",

@@ -95,8 +95,12 @@ def test_topk_validation():
     assert L.hysparse_topk(FAKE, 4, 100, 102, None, 8, FAKE, FAKE, 1 << 30, None) == 4   # stride % 4
     assert L.hysparse_topk(None, 4, 100, 100, None, 8, FAKE, FAKE, 1 << 30, None) == 1
     assert L.hysparse_topk(FAKE, 0, 100, 100, None, 8, FAKE, None, 0, None) == 0        # empty: no-op
-    assert L.hysparse_topk_workspace_bytes(16, 131072, 2048) == 0                        # one workgroup per row
+    # few long rows: the candidate filter runs in parts and needs a workspace
+    assert L.hysparse_topk_workspace_bytes(16, 131072, 2048) >= 16 * 32 * 12288 * 8
+    assert L.hysparse_topk_workspace_bytes(4096, 32768, 2048) == 0                        # one workgroup per row
+    assert L.hysparse_topk_workspace_bytes(16, 12288, 2048) == 0                          # rows fit the LDS
     assert L.hysparse_topk_workspace_bytes(-1, 131072, 2048) == 0
+    assert L.hysparse_topk(FAKE, 16, 131072, 131072, None, 2048, FAKE, None, 0, None) == 5   # workspace missing
 
 
 def test_sparse_and_hybrid_validation():

@@ -69,6 +69,39 @@ def test_topk_long_rows_decode128k_shape():
     np.testing.assert_array_equal(host(got), ref)
 
 
+@pytest.mark.parametrize("kind", ["probs", "ties", "signed"])
+@pytest.mark.parametrize("k", [1, 100, 2048])
+def test_topk_few_long_rows_in_parts(kind, k):
+    """Few rows longer than the LDS capacity: the filter runs over parts of
+    each row in separate workgroups; ragged row length, valid lengths from 0 to
+    the full row (including <= k and <= the capacity), ties and signed keys."""
+    say(f"topk parts kind={kind} k={k}")
+    R, L = 20, 50001  # rows of 50001 scores in a buffer 50004 wide (row stride % 4 == 0)
+    S = gen.random_scores(31 + k, R, L + 3, kind)
+    vl = np.random.default_rng(100 + k).integers(0, L + 1, size=R).astype(np.int32)
+    vl[0], vl[1], vl[2], vl[3], vl[4] = 0, L, min(k, L), 12288, 12289
+    ref = orc.topk_rows(S[:, :L], vl, k)
+    got = hy.hysparse_topk(torch.from_numpy(S).cuda()[:, :L], k, valid_len=torch.from_numpy(vl).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(got), ref)
+
+
+def test_topk_parts_strided_rows_and_fallback():
+    """Parts with a row stride wider than the row, and a K above the sample's
+    reach (the filter keeps too many candidates and the whole-row select
+    runs)."""
+    say("topk parts strided / fallback")
+    S = gen.random_scores(41, 6, 40004, "signed")
+    t = torch.from_numpy(S).cuda()[:, :40000]
+    got = host(hy.hysparse_topk(t, 777))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got, orc.topk_rows(S[:, :40000], 40000, 777))
+    S2 = gen.random_scores(42, 3, 131072, "probs")
+    got2 = host(hy.hysparse_topk(torch.from_numpy(S2).cuda(), 5000))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got2, orc.topk_rows(S2, 131072, 5000))
+
+
 def test_topk_row_stride_and_all_equal():
     say("topk strided rows, all-equal rows")
     base = np.full((5, 4100), 0.5, np.float32)
