@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) {
       const int pidx = lane + 64 * pp;
-      const int tc = pidx % CPR, kq = pidx / CPR;
+      const int kq = pidx % (kStep / 4), tc = pidx / (kStep / 4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = kjb[4 * kq + r];
@@ -236,14 +236,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     mt = wave_max16x4(mt);
     const float m_new = fmaxf(m_run, mt);
     const float mu = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - mu);
+    const float alpha = fast_exp2(m_run - mu);
     float p[2][4];
     float ls = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[kt][r] = exp2f(s[kt][r] - mu);
+        p[kt][r] = fast_exp2(s[kt][r] - mu);
         ls += p[kt][r];
       }
     l_run = l_run * alpha + ls;
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) {
       const int pidx = lane + 64 * pp;
-      const int tc = pidx % CPR, kq = pidx / CPR;
+      const int kq = pidx % (kStep / 4), tc = pidx / (kStep / 4);
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
         ST* dst = vt + (tc * EPC + e) * VP + 4 * kq;
@@ -322,12 +322,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
   const int64_t pbase = (int64_t)unit * a.nsplit + split;
   float* po = a.part_o + pbase * a.G * D;
-  for (int x = tid; x < a.G * D; x += 256) {
+  for (int x = 4 * tid; x < a.G * D; x += 4 * 256) {  // four consecutive d per thread
     const int h = x / D, d = x - h * D;
-    float acc = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) acc += obuf[(w * 16 + h) * D + d];
-    po[x] = acc;
+    for (int w = 0; w < kWaves; ++w) {
+      const float4 y = *reinterpret_cast<const float4*>(obuf + (w * 16 + h) * D + d);
+      acc.x += y.x;
+      acc.y += y.y;
+      acc.z += y.z;
+      acc.w += y.w;
+    }
+    *reinterpret_cast<float4*>(po + x) = acc;
   }
   if (tid < a.G) {
     const int h = tid;
@@ -484,16 +490,16 @@ __global__ __launch_bounds__(256) void decode_full_finish_kernel(FinishArgs f) {
       for (int h = 0; h < 16; ++h)
         if (h < f.G) {
           const float L = lse_s[h];
-          acc[0] += exp2f(x[h].x - L);
-          acc[1] += exp2f(x[h].y - L);
-          acc[2] += exp2f(x[h].z - L);
-          acc[3] += exp2f(x[h].w - L);
+          acc[0] += fast_exp2(x[h].x - L);
+          acc[1] += fast_exp2(x[h].y - L);
+          acc[2] += fast_exp2(x[h].z - L);
+          acc[3] += fast_exp2(x[h].w - L);
         }
     } else {
       for (int h = 0; h < f.G; ++h) {
         const float L = lse_s[h];
         for (int e = 0; e < 4; ++e)
-          if (j0 + e < f.Tkv) acc[e] += exp2f(row0[(int64_t)h * f.Tkv + j0 + e] - L);
+          if (j0 + e < f.Tkv) acc[e] += fast_exp2(row0[(int64_t)h * f.Tkv + j0 + e] - L);
       }
     }
     if (vec) {
@@ -570,12 +576,18 @@ DecodePlan plan_full_decode(const Geom& g) {
   return p;
 }
 
+#ifndef HYS_SPARSE_GSPLITS
+#define HYS_SPARSE_GSPLITS 48
+#endif
+
 DecodePlan plan_sparse_rows(const Geom& g, int k_top, int window) {
-  // at most 48 global and 16 window splits (kMaxSparseSplits merge weights)
+  // at most HYS_SPARSE_GSPLITS (<= 48) global and 16 window splits
+  // (kMaxSparseSplits merge weights)
+  static_assert(HYS_SPARSE_GSPLITS >= 1 && HYS_SPARSE_GSPLITS <= 48, "global split bound");
   DecodePlan p{};
   const int quantum = kWaves * kStep;
   p.units = g.B * g.Hkv * g.Tq;
-  int cg = (k_top + 47) / 48;
+  int cg = (k_top + HYS_SPARSE_GSPLITS - 1) / HYS_SPARSE_GSPLITS;
   cg = (cg + quantum - 1) / quantum * quantum;
   p.chunk = cg;
   int cw = (window + 15) / 16;
