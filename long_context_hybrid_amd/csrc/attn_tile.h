@@ -166,13 +166,15 @@ struct RowState {
 // cancels between numerator and denominator.
 constexpr float kRescaleSlack = 8.f;
 
-// One wave attends its RTW row tiles to the staged tile.  MASK = false when
-// every tile entry is a valid key that every row of the wave may use;
-// otherwise valid(rt, j) says whether key j may be used by the lane's row
-// (l % 16) of row tile rt, and j < 0 marks an invalid tile entry.
-template <typename TR, int D, int RTW, bool MASK, class Valid>
+// One wave attends its RTW row tiles to the staged tile.  mask (wave-uniform)
+// is false when every tile entry is a valid key that every row of the wave may
+// use; otherwise valid(rt, j) says whether key j may be used by the lane's row
+// (l % 16) of row tile rt, and j < 0 marks an invalid tile entry.  One code
+// path for both cases keeps a single copy of the step in the caller.
+template <typename TR, int D, int RTW, class Valid>
 __device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename TR::frag (&qf)[RTW][D / 32],
-                                            const unsigned char* sm, const int* kj, float sl2, Valid valid) {
+                                            const unsigned char* sm, const int* kj, float sl2, bool mask,
+                                            Valid valid) {
   using frag = typename TR::frag;
   constexpr int KC = D / 32, DT = D / 16;
   const int lane = threadIdx.x & 63, col = lane & 15, quad = lane >> 4;
@@ -189,15 +191,19 @@ __device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename
       for (int c = 0; c < KC; ++c) TR::mma(sacc[rt][kt], kf[c], qf[rt][c]);
     }
   }
-  int jj[4][4];
-  if constexpr (MASK) {
+  if (mask) {  // masked logits in place
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) jj[kt][r] = kj[16 * kt + 4 * quad + r];
+      for (int r = 0; r < 4; ++r) {
+        const int j = kj[16 * kt + 4 * quad + r];
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+          if (!(j >= 0 && valid(rt, j))) sacc[rt][kt][r] = kNegInf;
+      }
   }
-  // masked logits in place, lane-local maxima, and one vote per tile on
-  // whether any row must raise its running max
+  // lane-local maxima, and one vote per tile on whether any row must raise
+  // its running max
   float lm[RTW];
   bool over = false;
 #pragma unroll
@@ -206,13 +212,7 @@ __device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (MASK) {
-          const int j = jj[kt][r];
-          if (!(j >= 0 && valid(rt, j))) sacc[rt][kt][r] = kNegInf;
-        }
-        lm[rt] = fmaxf(lm[rt], sacc[rt][kt][r]);
-      }
+      for (int r = 0; r < 4; ++r) lm[rt] = fmaxf(lm[rt], sacc[rt][kt][r]);
     // scale > 0, so max(raw) * sl2 is the max of the scaled logits
     over = over || (lm[rt] * sl2 > st.m[rt] + kRescaleSlack);
   }

@@ -37,7 +37,7 @@ namespace {
 #define HYS_SC_SHAPE 4, 4
 #endif
 #ifndef HYS_SP_SHAPE
-#define HYS_SP_SHAPE 8, 1
+#define HYS_SP_SHAPE 8, 2
 #endif
 constexpr int kFwdShape[3] = {HYS_FWD_SHAPE};  // full layer, forward sweep (+ min waves per SIMD)
 constexpr int kScShape[2] = {HYS_SC_SHAPE};    // full layer, score sweep
@@ -135,11 +135,8 @@ __global__ __launch_bounds__(kNW * 64, kWPE) void prefill_fwd_kernel(PrefillArgs
       const int t0 = (it + 1) * kTK;
       stg.load(kbase, vbase, a.ks_t, [=](int t) { return t0 + t < Tkv ? t0 + t : -1; });
     }
-    auto causal = [&](int rt, int j) { return j <= rpos[rt]; };
-    if ((it + 1) * kTK - 1 > pmin)
-      attend_tile<TR, D, kRTW, true>(st, qf, sm, kj, a.sl2, causal);
-    else
-      attend_tile<TR, D, kRTW, false>(st, qf, sm, kj, a.sl2, causal);
+    attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, (it + 1) * kTK - 1 > pmin,
+                             [&](int rt, int j) { return j <= rpos[rt]; });
   }
 
 #pragma unroll
@@ -502,10 +499,17 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
   // do not wait on an index load from global memory.
   int* idx_s = idx_stage;
   auto refill = [&](int e0) {
-    for (int x = tid; x < kIdxCh; x += kNT) {
-      const int e = e0 + x;
-      int j = e < ktop ? idx_row[e] : -1;
-      idx_s[x] = (j >= 0 && j <= pos_last) ? j : -1;
+    constexpr int kPer = (kIdxCh + kNT - 1) / kNT;  // fixed count: the loads are in flight together
+    int jv[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int x = tid + r * kNT, e = e0 + x;
+      jv[r] = (x < kIdxCh && e < ktop) ? idx_row[e] : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int x = tid + r * kNT;
+      if (x < kIdxCh) idx_s[x] = (jv[r] >= 0 && jv[r] <= pos_last) ? jv[r] : -1;
     }
   };
   auto key_of = [=](int tile) {
@@ -525,9 +529,19 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
   stg.load(kbase, vbase, a.ks_t, key_of(0));
   RowState<kRTW, D> st;
   st.reset();
-  f32x4_t ol[kRTW][DT];  // (1 - g) * window output, rows 4 * quad + r
+  // output row (b, i, head) of accumulator row 4 * quad + r of row tile x, or
+  // nullptr for padding rows
+  auto orow_of = [&](int x, int r) -> ST* {
+    const int rt = rc * (kNW * kRTW) + wave * kRTW + x;
+    const int hl = rt / 4, qoff = 16 * (rt % 4);
+    const int i = i0 + qoff + 4 * quad + r;
+    if (!tile_ok[x] || i >= a.Tq) return nullptr;
+    return (ST*)a.out + (((int64_t)b * a.Tq + i) * a.Hq + g * a.G + hl) * D;
+  };
   const int ntiles = nwt + ngt;
-  for (int it = 0; it < ntiles; ++it) {
+  // stage the current tile, prefetch the next one; returns whether any entry
+  // of the staged tile is a key
+  auto stage = [&](int it) -> int {
     __syncthreads();
     stg.store(sm, kj);
     const int any = __syncthreads_or(tid < kTK && stg.jk >= 0);
@@ -539,48 +553,50 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
       }
       stg.load(kbase, vbase, a.ks_t, key_of(it + 1));
     }
-    if (any) {
-      if (it < nwt) {
-        attend_tile<TR, D, kRTW, true>(st, qf, sm, kj, a.sl2,
-                                       [&](int rt, int j) { return j <= rpos[rt] && j > rpos[rt] - W; });
-      } else {
-        auto causal = [&](int rt, int j) { return j <= rpos[rt]; };
-        if (tile_needs_mask(kj, pmin))
-          attend_tile<TR, D, kRTW, true>(st, qf, sm, kj, a.sl2, causal);
-        else
-          attend_tile<TR, D, kRTW, false>(st, qf, sm, kj, a.sl2, causal);
+    return any;
+  };
+  // The two branches run as two loops (one live output state; separate loops
+  // keep the register pressure of one attention step each).
+  for (int it = 0; it < nwt; ++it) {
+    if (stage(it))
+      attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, true,
+                               [&](int rt, int j) { return j <= rpos[rt] && j > rpos[rt] - W; });
+  }
+  // window branch done: its share (1 - g) * o_window goes to the output now
+  // (read back by the same lanes in the epilogue); restart for the global
+  // branch
+#pragma unroll
+  for (int x = 0; x < kRTW; ++x) {
+    const float lt = wave_sum16x4(st.l[x]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float lr = __shfl(lt, 4 * quad + r);
+      const float sc = lr > 0.f ? (1.f - gt[x]) / lr : 0.f;
+      ST* orow = orow_of(x, r);
+      if (orow) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) orow[16 * dt + col] = TR::from_float(st.o[x][dt][r] * sc);
       }
     }
-    if (it == nwt - 1) {
-      // window branch done: keep (1 - g) * o_window, restart for the global branch
-#pragma unroll
-      for (int x = 0; x < kRTW; ++x) {
-        const float lt = wave_sum16x4(st.l[x]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float lr = __shfl(lt, 4 * quad + r);
-          const float sc = lr > 0.f ? (1.f - gt[x]) / lr : 0.f;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) ol[x][dt][r] = st.o[x][dt][r] * sc;
-        }
-      }
-      st.reset();
-    }
+  }
+  st.reset();
+  for (int it = nwt; it < ntiles; ++it) {
+    if (stage(it))
+      attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, tile_needs_mask(kj, pmin),
+                               [&](int rt, int j) { return j <= rpos[rt]; });
   }
 #pragma unroll
   for (int x = 0; x < kRTW; ++x) {
     const float lt = wave_sum16x4(st.l[x]);
-    const int rt = rc * (kNW * kRTW) + wave * kRTW + x;
-    const int hl = rt / 4, qoff = 16 * (rt % 4);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float lr = __shfl(lt, 4 * quad + r);
-      const int i = i0 + qoff + 4 * quad + r;
-      if (tile_ok[x] && i < a.Tq) {
+      ST* orow = orow_of(x, r);
+      if (orow) {
         const float sc = lr > 0.f ? gt[x] / lr : 0.f;
-        ST* orow = (ST*)a.out + (((int64_t)b * a.Tq + i) * a.Hq + g * a.G + hl) * D;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) orow[16 * dt + col] = TR::from_float(st.o[x][dt][r] * sc + ol[x][dt][r]);
+        for (int dt = 0; dt < DT; ++dt)
+          orow[16 * dt + col] = TR::from_float(st.o[x][dt][r] * sc + TR::to_float(orow[16 * dt + col]));
       }
     }
   }

@@ -30,6 +30,10 @@ the HySparse abstract):
 * ``decode128k`` B4, context 131072, Hq 64 / Hkv 4, D 128, bf16, N(0,1); 64 planted
                  key rows per sequence; K 2048, window 128, 9 sparse layers.
 * ``hier128k``   as ``decode128k`` (block-pooled selection variant).
+* ``prefill128k`` B1, T 131072 prefill with the 128K model's attention shape
+                 (Hq 64 / Hkv 4, D 128), bf16, N(0,1)/sqrt(128); score block 64,
+                 K 2048, window 128, 9 sparse layers.  Too large to draw on the
+                 host in float64: ``make_device_inputs`` draws it on the GPU.
 
 Planting (``decode128k``): per sequence, 64 positions drawn without replacement
 from ``[0, ctx - 128)``; at each, the key row of every KV group g is set to
@@ -89,6 +93,8 @@ WORKLOADS = {
                            1.0, "normal", 1, 2048, 128, 9, n_planted=64),
     "hier128k": Workload("hier128k", 4, 4, 1, 131072, 64, 4, 128, "bf16",
                          1.0, "normal", 1, 2048, 128, 9, n_planted=64),
+    "prefill128k": Workload("prefill128k", 5, 1, 131072, 131072, 64, 4, 128, "bf16",
+                            1.0 / np.sqrt(128.0), "normal", 64, 2048, 128, 9),
 }
 
 
@@ -200,3 +206,34 @@ def random_scores(seed: int, n_rows: int, row_len: int, kind: str = "probs") -> 
     else:
         raise ValueError(kind)
     return x.astype(np.float32)
+
+
+def make_device_inputs(wl: Workload, device, n_sparse: Optional[int] = None):
+    """Inputs of the same shapes and distributions as ``make_inputs``, drawn on
+    the GPU with torch's generator (one seed per tensor, from the same
+    (config, tensor, layer) triple), for workloads too large to draw on the
+    host.  Values differ from ``make_inputs``; planting is not supported.
+    Returns (q_full, k, v, [q_sparse], gate_logits) as device tensors."""
+    import torch
+    if wl.n_planted:
+        raise ValueError("device inputs do not plant needles")
+    B, Tq, Tkv = wl.batch, wl.q_len, wl.kv_len
+    Hq, Hkv, D = wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    N = wl.n_sparse if n_sparse is None else n_sparse
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+    def draw(shape, tensor_id, layer=0):
+        seed = int(np.random.SeedSequence([wl.config_id, tensor_id, layer]).generate_state(1, np.uint64)[0] >> 1)
+        g = torch.Generator(device=device)
+        g.manual_seed(seed)
+        x = torch.empty(shape, dtype=torch.float32, device=device)
+        x.normal_(0.0, wl.std, generator=g)
+        return x.to(dt)
+
+    q_full = draw((B, Tq, Hq, D), T_QFULL)
+    k = draw((B, Tkv, Hkv, D), T_K)
+    v = draw((B, Tkv, Hkv, D), T_V)
+    q_sparse = [draw((B, Tq, Hq, D), T_QSPARSE, l) for l in range(N)]
+    grng = _rng(wl.config_id, T_GATE)
+    gates = grng.uniform(-2.0, 2.0, size=(N, Hq)) if wl.gate_dist == "uniform2" else grng.standard_normal(size=(N, Hq))
+    return q_full, k, v, q_sparse, torch.from_numpy(gates.astype(np.float32)).to(device)
