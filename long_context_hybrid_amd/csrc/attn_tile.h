@@ -166,19 +166,18 @@ struct RowState {
 // cancels between numerator and denominator.
 constexpr float kRescaleSlack = 8.f;
 
-// One wave attends its RTW row tiles to the staged tile.  mask (wave-uniform)
-// is false when every tile entry is a valid key that every row of the wave may
-// use; otherwise valid(rt, j) says whether key j may be used by the lane's row
-// (l % 16) of row tile rt, and j < 0 marks an invalid tile entry.  One code
-// path for both cases keeps a single copy of the step in the caller.
-template <typename TR, int D, int RTW, class Valid>
-__device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename TR::frag (&qf)[RTW][D / 32],
-                                            const unsigned char* sm, const int* kj, float sl2, bool mask,
-                                            Valid valid) {
+// The attention step of one wave on one staged tile, in three parts (QK^T,
+// online softmax, PV) so that a caller can interleave the parts of
+// different tiles.
+//
+// qk_tile: S^T[key][row] for the wave's RTW row tiles; sacc[rt][kt][r] is the
+// logit of key 16*kt + 4*quad + r for the lane's row (l % 16).
+template <typename TR, int D, int RTW>
+__device__ __forceinline__ void qk_tile(f32x4_t (&sacc)[RTW][4], const typename TR::frag (&qf)[RTW][D / 32],
+                                        const unsigned char* sm) {
   using frag = typename TR::frag;
-  constexpr int KC = D / 32, DT = D / 16;
+  constexpr int KC = D / 32;
   const int lane = threadIdx.x & 63, col = lane & 15, quad = lane >> 4;
-  f32x4_t sacc[RTW][4];
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     frag kf[KC];
@@ -191,6 +190,17 @@ __device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename
       for (int c = 0; c < KC; ++c) TR::mma(sacc[rt][kt], kf[c], qf[rt][c]);
     }
   }
+}
+
+// softmax_tile: masks the logits when `mask` (wave-uniform) is set (valid(rt,
+// j) says whether key j may be used by the lane's row of row tile rt; j < 0
+// marks an invalid tile entry), updates the running max / sum (rescaling O
+// when a max rises), and packs the probabilities as PV's A operand.
+template <typename TR, int D, int RTW, class Valid>
+__device__ __forceinline__ void softmax_tile(RowState<RTW, D>& st, f32x4_t (&sacc)[RTW][4], const int* kj,
+                                             float sl2, bool mask, Valid valid, typename TR::frag (&pa)[RTW][2]) {
+  constexpr int DT = D / 16;
+  const int lane = threadIdx.x & 63, quad = lane >> 4;
   if (mask) {  // masked logits in place
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -231,7 +241,6 @@ __device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename
       }
     }
   }
-  frag pa[RTW][2];
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
     const float nmu = (st.m[rt] == kNegInf) ? 0.f : -st.m[rt];
@@ -248,6 +257,15 @@ __device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename
     pa[rt][0] = TR::pack(p[0], p[1]);
     pa[rt][1] = TR::pack(p[2], p[3]);
   }
+}
+
+// pv_tile: O += P . V for the wave's row tiles.
+template <typename TR, int D, int RTW>
+__device__ __forceinline__ void pv_tile(RowState<RTW, D>& st, const typename TR::frag (&pa)[RTW][2],
+                                        const unsigned char* sm) {
+  using frag = typename TR::frag;
+  constexpr int DT = D / 16;
+  const int lane = threadIdx.x & 63, col = lane & 15, quad = lane >> 4;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -256,6 +274,19 @@ __device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt) TR::mma(st.o[rt][dt], pa[rt][kk], vb);
     }
+}
+
+// The whole step on one tile.  One code path for masked and unmasked tiles
+// keeps a single copy of the step in the caller.
+template <typename TR, int D, int RTW, class Valid>
+__device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename TR::frag (&qf)[RTW][D / 32],
+                                            const unsigned char* sm, const int* kj, float sl2, bool mask,
+                                            Valid valid) {
+  f32x4_t sacc[RTW][4];
+  qk_tile<TR, D, RTW>(sacc, qf, sm);
+  typename TR::frag pa[RTW][2];
+  softmax_tile<TR, D, RTW>(st, sacc, kj, sl2, mask, valid, pa);
+  pv_tile<TR, D, RTW>(st, pa, sm);
 }
 
 // Whether a wave must mask a staged tile: some entry is invalid (j < 0) or

@@ -31,7 +31,8 @@ the HySparse abstract):
                  key rows per sequence; K 2048, window 128, 9 sparse layers.
 * ``hier128k``   as ``decode128k`` (block-pooled selection variant).
 * ``prefill128k`` B1, T 131072 prefill with the 128K model's attention shape
-                 (Hq 64 / Hkv 4, D 128), bf16, N(0,1)/sqrt(128); score block 64,
+                 (Hq 64 / Hkv 4, D 128), bf16, N(0,1) (unit-std logits, as the 128K
+                 decode); score block 64,
                  K 2048, window 128, 9 sparse layers.  Too large to draw on the
                  host in float64: ``make_device_inputs`` draws it on the GPU.
 
@@ -94,7 +95,7 @@ WORKLOADS = {
     "hier128k": Workload("hier128k", 4, 4, 1, 131072, 64, 4, 128, "bf16",
                          1.0, "normal", 1, 2048, 128, 9, n_planted=64),
     "prefill128k": Workload("prefill128k", 5, 1, 131072, 131072, 64, 4, 128, "bf16",
-                            1.0 / np.sqrt(128.0), "normal", 64, 2048, 128, 9),
+                            1.0, "normal", 64, 2048, 128, 9),
 }
 
 
