@@ -7,7 +7,8 @@ import torch
 from long_context_hybrid_amd import hysparse as hy
 from long_context_hybrid_amd import inputs as gen
 from oracle import hysparse_oracle as orc
-from tests.gpu_util import (assert_attn_close, assert_scores_close, check_hybrid, dev_tensor, host, say)
+from tests.gpu_util import (assert_attn_close, assert_scores_close, check_hybrid, dev_tensor, eps_valid, host,
+                             say)
 
 pytestmark = pytest.mark.gpu
 
@@ -135,3 +136,34 @@ def test_hybrid_block_prefill32k_full_size_sampled():
     NB = wl.n_blocks
     blocks = [(0, g, n) for g in (0, 5) for n in (0, 1, 31, 32, 200, NB - 2, NB - 1)]
     check_hybrid(wl, inp, res, blocks=blocks)
+
+
+def test_hybrid_block_prefill128k_sampled():
+    """The 128K prefill workload (inputs drawn on the GPU) at full size, in the
+    launch configuration bench.py times; the oracle recomputes whole score
+    blocks (O, LSE, S row, top-K on the GPU's scores, sparse output on the
+    GPU's indices) from host copies of the stored input values."""
+    wl = W["prefill128k"].replace(n_sparse=1)
+    say("hybrid prefill128k full size")
+    qf, k, v, qs, gates = gen.make_device_inputs(wl, torch.device("cuda"))
+    lse = torch.empty((1, wl.n_q_heads, wl.q_len), dtype=torch.float32, device="cuda")
+    res = hy.hysparse_hybrid_block(qf, k, v, qs, gates, wl.k_top, wl.score_block, wl.window, lse=lse)
+    torch.cuda.synchronize()
+    f32 = lambda t: t.float().cpu().numpy()  # stored bf16 values, exact in float32
+    qh, kh, vh, qsh = f32(qf), f32(k), f32(v), f32(qs[0])
+    gh = gates[0].cpu().numpy()
+    G, NB, Sb, K = wl.group, wl.n_blocks, wl.score_block, wl.k_top
+    for (g, n) in [(0, 0), (1, 777), (3, NB - 1)]:
+        say(f"  block (g={g}, n={n})")
+        i0, i1 = n * Sb, min((n + 1) * Sb, wl.q_len)
+        O, LSE, S = orc.full_layer_block(qh, kh, vh, 0, g, n, Sb)
+        assert_attn_close(res["out_full"][0, i0:i1, g * G:(g + 1) * G], O, wl.dtype, f"O_full block {n}")
+        np.testing.assert_allclose(host(res["lse"][0, g * G:(g + 1) * G, i0:i1]), LSE, rtol=0, atol=2e-5)
+        S_gpu = res["scores"][0, g, n]
+        assert_scores_close(S_gpu, S.astype(np.float32))
+        c = orc.candidate_count(n, wl.q_len, wl.kv_len, Sb)
+        idx_row = host(res["idx"][0, g, n])
+        np.testing.assert_array_equal(idx_row, orc.topk_row(host(S_gpu).astype(np.float32), c, K))
+        assert eps_valid(idx_row, S.astype(np.float32), c)
+        out, _, _ = orc.sparse_layer_block(qsh, kh, vh, idx_row, 0, g, n, Sb, wl.window, gh)
+        assert_attn_close(res["out"][0][0, i0:i1, g * G:(g + 1) * G], out, wl.dtype, f"sparse block {n}")
