@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode128k",
-                    choices=["decode128k", "decode8k", "prefill32k", "prefill128k", "tiny", "hier128k"])
+                    choices=["decode128k", "decode8k", "prefill32k", "prefill128k", "tiny", "hier128k",
+                             "decode128k_loop"])
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -186,7 +187,10 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     hy.lib()
-    wl = gen.WORKLOADS[args.workload]
+    # decode128k_loop: the decode loop on the 128K workload; every step appends
+    # one token's K/V to the cache and runs the block on the grown cache
+    loop = args.workload.endswith("_loop")
+    wl = gen.WORKLOADS[args.workload[:-len("_loop")] if loop else args.workload]
     t_gen = time.perf_counter()
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
@@ -216,6 +220,25 @@ def main():
     def step():
         hy.hysparse_hybrid_block(qf, k, v, qs, gates, wl.k_top, wl.score_block, wl.window, out_full=out_full,
                                  out_sparse=outs, lse=lse, scores=scores, idx=idx, workspace=ws)
+
+    if loop:
+        # cache = the workload's keys/values; steps append rows L0, L0 + 1, ...
+        n_loop = args.warmup + 2 * args.steps
+        L0 = Tkv - n_loop
+        # token-major copies, so each step's rows [B, 1, Hkv, D] are contiguous
+        k_rows = k[:, L0:].transpose(0, 1).contiguous().unsqueeze(2)
+        v_rows = v[:, L0:].transpose(0, 1).contiguous().unsqueeze(2)
+        kc, vc = k.clone(), v.clone()
+        t_loop = [0]
+
+        def step():
+            t = t_loop[0] % n_loop
+            L = L0 + t + 1
+            hy.hysparse_append_kv(k_rows[t], v_rows[t], kc, vc, L - 1)
+            hy.hysparse_hybrid_block(qf, kc[:, :L], vc[:, :L], qs, gates, wl.k_top, wl.score_block, wl.window,
+                                     out_full=out_full, out_sparse=outs, lse=lse,
+                                     scores=scores.view(-1)[:B * Hkv * L].view(B, Hkv, 1, L), idx=idx, workspace=ws)
+            t_loop[0] += 1
 
     hier = wl.name == "hier128k"
     if hier:
@@ -342,6 +365,11 @@ def main():
                                   "sparse_out_rel_l2_vs_flat": float(np.linalg.norm(oh - of) / np.linalg.norm(of))}
     result["kernels"] = kernels
     result["traced_ms_per_step"] = traced_ms
+    if loop:
+        result["config"]["workload"] = args.workload
+        result["config"]["context"] = f"{L0 + 1}..{L0 + n_loop} (grows by one token per step)"
+        result["config"]["step"] = ("decode step: append one token's K/V to the cache, full layer on the grown cache, "
+                                    "top-K, all sparse layers")
     if inp is not None:
         result["input_sha256"] = inp.sha256()
     else:

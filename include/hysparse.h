@@ -185,6 +185,25 @@ hys_status hysparse_hier_select(const hys_attn_desc* desc, const void* q, const 
                                 float* block_scores, int32_t* blocks, int32_t* idx, void* ws,
                                 size_t ws_bytes, hipStream_t stream);
 
+/*
+ * KV-cache append (intelliparadigm article section 3.1: only the full layers
+ * update the cache; the sparse layers read it).  Copies n_new new rows of keys
+ * and values, each [B, n_new, Hkv, D] contiguous in desc.dtype, into the cache
+ * at token positions [pos, pos + n_new) of every batch entry and KV head.  The
+ * cache is described by desc's kv fields: kv_len is its capacity in tokens,
+ * kv_stride its (batch, token, head) strides; batch, n_kv_heads, head_dim and
+ * dtype as for the other calls.  desc's query fields are not read.  The full
+ * layer then runs on the cache with kv_len = pos + n_new (a decode step:
+ * n_new = 1; chunked prefill: n_new = the chunk length).
+ *
+ *   k_new, v_new      new rows, 16-byte aligned, caller-owned, read.
+ *   k_cache, v_cache  cache, 16-byte aligned, caller-owned, written.
+ *   Errors: NULL pointers -> HYS_ERR_NULL_PTR; n_new < 1, pos < 0 or
+ *   pos + n_new > kv_len -> HYS_ERR_BAD_SHAPE; no workspace is needed.
+ */
+hys_status hysparse_append_kv(const hys_attn_desc* desc, const void* k_new, const void* v_new, int32_t n_new,
+                              int32_t pos, void* k_cache, void* v_cache, hipStream_t stream);
+
 /* Workspace bytes for hysparse_hier_select (0 for invalid arguments). */
 size_t hysparse_hier_workspace_bytes(const hys_attn_desc* desc, int32_t block, int32_t n_keep,
                                      int32_t k_top);

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libhysparse.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["decode.hip", "topk.hip", "prefill.hip", "hier.hip", "hysparse_api.cpp"]
+SOURCES = ["decode.hip", "topk.hip", "prefill.hip", "hier.hip", "cache.hip", "hysparse_api.cpp"]
 # Packed-FP32 instructions are disabled for all device code (they are never
 # emitted by hand either).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

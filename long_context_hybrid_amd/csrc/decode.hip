@@ -49,7 +49,8 @@ struct DecodeArgs {
   const int32_t* idx;
   int k_top, score_block, NB, window;
   int chunk, wchunk, nsplit, nsg;
-  float* logits;
+  float* logits;        // full decode: base-2 logits, rows of ld floats
+  int ld;               // logit row pitch: kv_len rounded up to 4 (16-byte rows)
   float* part_o;
   float* part_ml;
   const float* gate;    // sparse: [Hq] gate logits
@@ -141,8 +142,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   ST* vt = reinterpret_cast<ST*>(smem) + (size_t)wave * D * VP;
   int* kj = kj_s[wave];
   float* lg_row = nullptr;
-  if (FULL && col < a.G) lg_row = a.logits + ((int64_t)b * a.Hq + g * a.G + col) * a.Tkv;
-  const bool lg_vec = (a.Tkv & 3) == 0;
+  if (FULL && col < a.G) lg_row = a.logits + ((int64_t)b * a.Hq + g * a.G + col) * a.ld;
 
   // key index of list entry t (-1: past the list, negative index or after pos)
   auto key_at = [&](int t) -> int {
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       if (FULL && lg_row != nullptr) {
         // full layer: list entry t is key t, so the four keys are consecutive
         const int j0 = t0 + 16 * kt + 4 * quad;
-        if (all_valid && lg_vec) {
+        if (all_valid) {
           *reinterpret_cast<float4*>(lg_row + j0) = make_float4(s[kt][0], s[kt][1], s[kt][2], s[kt][3]);
         } else {
 #pragma unroll
@@ -408,6 +408,7 @@ struct FinishArgs {
   const float* part_o;
   const float* part_ml;
   const float* logits;
+  int ld;               // logit row pitch (multiple of 4)
   int nsplit, G, Hkv, Tkv, nchunk, units;
   void* out;
   float* lse;
@@ -473,36 +474,29 @@ __global__ __launch_bounds__(256) void decode_full_finish_kernel(FinishArgs f) {
   const int b = unit / f.Hkv, g = unit - b * f.Hkv;
   unit_lse2(f.part_ml + (int64_t)unit * f.nsplit * f.G * 2, f.nsplit, f.G, lse_s);
   float* srow = f.scores + (int64_t)unit * f.Tkv;
-  const bool vec_ok = (f.Tkv & 3) == 0;
+  const bool vec_out = (f.Tkv & 3) == 0;  // the score row itself has pitch Tkv
   for (int sub = 0; sub < kScoreChunk / 1024; ++sub) {
     const int j0 = c * kScoreChunk + sub * 1024 + 4 * tid;
     if (j0 >= f.Tkv) break;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    const bool vec = vec_ok && (j0 + 3 < f.Tkv);
-    const float* row0 = f.logits + ((int64_t)b * Hq + g * f.G) * f.Tkv;
-    if (vec) {
-      // all the group's rows in flight at once, then the exponentials
-      float4 x[16];
+    const float* row0 = f.logits + ((int64_t)b * Hq + g * f.G) * f.ld;
+    // all the group's rows in flight at once, then the exponentials (the
+    // logit rows are padded to a multiple of 4: the lanes past Tkv read
+    // padding and are not stored)
+    float4 x[16];
 #pragma unroll
-      for (int h = 0; h < 16; ++h)
-        if (h < f.G) x[h] = *reinterpret_cast<const float4*>(row0 + (int64_t)h * f.Tkv + j0);
+    for (int h = 0; h < 16; ++h)
+      if (h < f.G) x[h] = *reinterpret_cast<const float4*>(row0 + (int64_t)h * f.ld + j0);
 #pragma unroll
-      for (int h = 0; h < 16; ++h)
-        if (h < f.G) {
-          const float L = lse_s[h];
-          acc[0] += fast_exp2(x[h].x - L);
-          acc[1] += fast_exp2(x[h].y - L);
-          acc[2] += fast_exp2(x[h].z - L);
-          acc[3] += fast_exp2(x[h].w - L);
-        }
-    } else {
-      for (int h = 0; h < f.G; ++h) {
+    for (int h = 0; h < 16; ++h)
+      if (h < f.G) {
         const float L = lse_s[h];
-        for (int e = 0; e < 4; ++e)
-          if (j0 + e < f.Tkv) acc[e] += fast_exp2(row0[(int64_t)h * f.Tkv + j0 + e] - L);
+        acc[0] += fast_exp2(x[h].x - L);
+        acc[1] += fast_exp2(x[h].y - L);
+        acc[2] += fast_exp2(x[h].z - L);
+        acc[3] += fast_exp2(x[h].w - L);
       }
-    }
-    if (vec) {
+    if (vec_out && j0 + 3 < f.Tkv) {
       *reinterpret_cast<float4*>(srow + j0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     } else {
       for (int e = 0; e < 4; ++e)
@@ -598,10 +592,12 @@ DecodePlan plan_sparse_rows(const Geom& g, int k_top, int window) {
   return p;
 }
 
+static int logit_pitch(const Geom& g) { return (g.Tkv + 3) & ~3; }
+
 static size_t decode_ws(const Geom& g, const DecodePlan& p, bool full) {
   size_t n = align_up((size_t)p.units * p.nsplit * g.G * g.D * sizeof(float));
   n += align_up((size_t)p.units * p.nsplit * g.G * 2 * sizeof(float));
-  if (full) n += align_up((size_t)g.B * g.Hq * g.Tkv * sizeof(float));
+  if (full) n += align_up((size_t)g.B * g.Hq * logit_pitch(g) * sizeof(float));
   return n;
 }
 
@@ -627,12 +623,14 @@ hipError_t launch_full_decode(const Geom& g, const void* q, const void* k, const
   const DecodeWs w = carve_decode_ws(g, p, ws, true);
   DecodeArgs a = make_args(g, p, q, k, v);
   a.logits = w.logits;
+  a.ld = logit_pitch(g);
   a.part_o = w.part_o;
   a.part_ml = w.part_ml;
   FinishArgs f{};
   f.part_o = w.part_o;
   f.part_ml = w.part_ml;
   f.logits = w.logits;
+  f.ld = logit_pitch(g);
   f.nsplit = p.nsplit;
   f.G = g.G;
   f.Hkv = g.Hkv;

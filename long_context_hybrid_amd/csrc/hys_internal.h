@@ -103,6 +103,10 @@ hipError_t launch_topk(const float* scores, int64_t n_rows, int32_t row_len, int
 // ------------------------------------------------------ hierarchical select
 int hier_max_blocks();
 size_t hier_ws_bytes(const Geom& g, int block, int n_keep, int k_top);
+
+// KV-cache append (cache.hip)
+hipError_t launch_append_kv(const Geom& g, const void* k_new, const void* v_new, int n_new, int pos, void* k_cache,
+                            void* v_cache, hipStream_t st);
 hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const float* scores, int block, int n_keep,
                               int k_top, float* bscore_out, int32_t* blk_out, int32_t* idx, void* ws, hipStream_t st);
 

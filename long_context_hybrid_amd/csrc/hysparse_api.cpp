@@ -307,6 +307,25 @@ hys_status hysparse_hier_select(const hys_attn_desc* desc, const void* q, const 
   return from_hip(hys::launch_hier_select(g, q, k, scores, block, n_keep, k_top, block_scores, blocks, idx, ws, stream));
 }
 
+hys_status hysparse_append_kv(const hys_attn_desc* desc, const void* k_new, const void* v_new, int32_t n_new,
+                              int32_t pos, void* k_cache, void* v_cache, hipStream_t stream) {
+  if (!desc) return fail(HYS_ERR_NULL_PTR, "desc is NULL");
+  // only the cache (kv) fields are used: validate them with a stand-in query
+  hys_attn_desc d = *desc;
+  d.q_len = 1;
+  d.n_q_heads = d.n_kv_heads;
+  for (int x = 0; x < 3; ++x) d.q_stride[x] = d.kv_stride[x];
+  hys::Geom g;
+  hys_status s;
+  if ((s = check_desc(&d, &g))) return s;
+  if (n_new < 1 || pos < 0 || (int64_t)pos + n_new > desc->kv_len)
+    return fail(HYS_ERR_BAD_SHAPE, "need n_new >= 1, pos >= 0 and pos + n_new <= kv_len (the cache capacity)");
+  if ((s = check_tensor(k_new, "k_new", 16)) || (s = check_tensor(v_new, "v_new", 16)) ||
+      (s = check_tensor(k_cache, "k_cache", 16)) || (s = check_tensor(v_cache, "v_cache", 16)))
+    return s;
+  return from_hip(hys::launch_append_kv(g, k_new, v_new, n_new, pos, k_cache, v_cache, stream));
+}
+
 size_t hysparse_hier_workspace_bytes(const hys_attn_desc* desc, int32_t block, int32_t n_keep, int32_t k_top) {
   hys::Geom g;
   if (check_hier(desc, block, n_keep, k_top, &g) != HYS_OK) return 0;

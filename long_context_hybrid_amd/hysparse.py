@@ -28,7 +28,7 @@ STATUS = {0: "HYS_OK", 1: "HYS_ERR_NULL_PTR", 2: "HYS_ERR_BAD_SHAPE", 3: "HYS_ER
 EXPORTS = ("hysparse_full_attn_scores", "hysparse_topk", "hysparse_sparse_attn", "hysparse_hybrid_block",
            "hysparse_workspace_bytes", "hysparse_topk_workspace_bytes", "hysparse_status_string",
            "hysparse_last_error", "hysparse_version", "hysparse_trace_begin", "hysparse_trace_end",
-           "hysparse_trace_name", "hysparse_hier_select", "hysparse_hier_workspace_bytes")
+           "hysparse_trace_name", "hysparse_hier_select", "hysparse_hier_workspace_bytes", "hysparse_append_kv")
 
 
 class HysAttnDesc(ctypes.Structure):
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
     L.hysparse_hier_select.argtypes = [D, _P, _P, _P, i32, i32, i32, _P, _P, _P, _P, sz, _P]
     L.hysparse_hier_select.restype = i32
     L.hysparse_hier_workspace_bytes.argtypes = [D, i32, i32, i32]
+    L.hysparse_append_kv.argtypes = [D, _P, _P, i32, i32, _P, _P, _P]
+    L.hysparse_append_kv.restype = i32
     L.hysparse_hier_workspace_bytes.restype = sz
     L.hysparse_trace_begin.argtypes = [_P, i32]
     L.hysparse_trace_begin.restype = None
@@ -308,3 +310,19 @@ class KernelTrace:
                 self._hip.hipEventDestroy(self.events[i])
         except Exception:
             pass
+
+
+def hysparse_append_kv(k_new, v_new, k_cache, v_cache, pos: int):
+    """Write the rows k_new/v_new [B, n, Hkv, D] (contiguous) into the cache
+    tensors [B, capacity, Hkv, D] (head_dim contiguous) at token positions
+    [pos, pos + n)."""
+    _same_device(k_new, v_new, k_cache, v_cache)
+    if k_new.shape != v_new.shape or k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
+        raise ValueError("k/v shapes or cache strides differ")
+    if not (k_new.is_contiguous() and v_new.is_contiguous()):
+        raise ValueError("new rows must be contiguous [B, n, Hkv, D]")
+    if k_new.dtype != k_cache.dtype or k_new.shape[0] != k_cache.shape[0] or k_new.shape[2:] != k_cache.shape[2:]:
+        raise ValueError("new rows and cache disagree in dtype, batch, heads or head_dim")
+    desc = make_desc(k_cache, k_cache)
+    _check(lib().hysparse_append_kv(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), k_new.shape[1], pos,
+                                    _ptr(k_cache), _ptr(v_cache), _stream(k_cache.device)))

@@ -151,3 +151,19 @@ def test_binding_refuses_cpu_tensors():
     k = torch.zeros(1, 8, 1, 64)
     with pytest.raises(ValueError):
         hy.hysparse_full_attn_scores(q, k, k, 1)
+
+
+def test_append_kv_validation():
+    L = hy.lib()
+    d = _desc(Tkv=100)
+    assert L.hysparse_append_kv(None, FAKE, FAKE, 1, 0, FAKE, FAKE, None) == 1
+    assert L.hysparse_append_kv(ctypes.byref(d), FAKE, FAKE, 0, 0, FAKE, FAKE, None) == 2      # n_new < 1
+    assert L.hysparse_append_kv(ctypes.byref(d), FAKE, FAKE, 1, -1, FAKE, FAKE, None) == 2     # pos < 0
+    assert L.hysparse_append_kv(ctypes.byref(d), FAKE, FAKE, 5, 96, FAKE, FAKE, None) == 2     # past capacity
+    assert L.hysparse_append_kv(ctypes.byref(d), None, FAKE, 1, 0, FAKE, FAKE, None) == 1
+    assert L.hysparse_append_kv(ctypes.byref(d), FAKE, FAKE, 1, 0, FAKE_ODD, FAKE, None) == 4
+    bad = _desc(Tkv=100, D=96)
+    assert L.hysparse_append_kv(ctypes.byref(bad), FAKE, FAKE, 1, 0, FAKE, FAKE, None) == 3    # head_dim
+    # the query fields are not read: a query shape that the attention calls reject is fine here
+    q_bad = _desc(Tq=500, Tkv=100, Hq=3)
+    assert L.hysparse_append_kv(ctypes.byref(q_bad), FAKE, FAKE, 0, 0, FAKE, FAKE, None) == 2   # still n_new

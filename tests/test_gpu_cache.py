@@ -1,0 +1,128 @@
+"""GPU parity of the decode loop: KV-cache append, multi-step decode with the
+indices recomputed every step, and chunked prefill."""
+import numpy as np
+import pytest
+import torch
+
+from long_context_hybrid_amd import hysparse as hy
+from long_context_hybrid_amd import inputs as gen
+from oracle import hysparse_oracle as orc
+from tests.gpu_util import assert_attn_close, assert_scores_close, dev_tensor, eps_valid, host, say
+
+pytestmark = pytest.mark.gpu
+W = gen.WORKLOADS
+
+
+@pytest.fixture(autouse=True)
+def _lib():
+    hy.lib()
+
+
+def test_append_kv_writes_exactly_the_new_rows():
+    say("append kv")
+    torch.manual_seed(3)
+    B, cap, Hkv, D = 3, 500, 4, 128
+    for dt in (torch.bfloat16, torch.float32):
+        kc = torch.randn(B, cap, Hkv, D, device="cuda").to(dt)
+        vc = torch.randn(B, cap, Hkv, D, device="cuda").to(dt)
+        k0, v0 = kc.clone(), vc.clone()
+        kn = torch.randn(B, 7, Hkv, D, device="cuda").to(dt)
+        vn = torch.randn(B, 7, Hkv, D, device="cuda").to(dt)
+        hy.hysparse_append_kv(kn, vn, kc, vc, 493)      # the last 7 rows of the capacity
+        hy.hysparse_append_kv(kn[:, :1].contiguous(), vn[:, :1].contiguous(), kc, vc, 0)
+        torch.cuda.synchronize()
+        ek, ev = k0.clone(), v0.clone()
+        ek[:, 493:], ev[:, 493:] = kn, vn
+        ek[:, :1], ev[:, :1] = kn[:, :1], vn[:, :1]
+        assert torch.equal(kc, ek) and torch.equal(vc, ev)
+    # a strided (head-major) cache view
+    base = torch.randn(B, Hkv, cap, D, device="cuda").to(torch.bfloat16)
+    kc = base.permute(0, 2, 1, 3)
+    vc = base.clone().permute(0, 2, 1, 3)
+    kn = torch.randn(B, 2, Hkv, D, device="cuda").to(torch.bfloat16)
+    hy.hysparse_append_kv(kn, kn.clone(), kc, vc, 10)
+    torch.cuda.synchronize()
+    assert torch.equal(kc[:, 10:12], kn) and torch.equal(vc[:, 10:12], kn)
+
+
+def test_multi_step_decode_recomputes_indices_each_step():
+    """T decode steps after a prefix of L0 tokens: each step appends its
+    token's K/V to the cache and runs the hybrid block (full layer on the cache
+    of length L0 + t + 1, top-K, sparse layers).  Step t is query t of a
+    T-query prefill with per-query scores, which the oracle evaluates."""
+    L0, T = 3000, 6
+    wl = W["decode8k"].replace(batch=2, q_len=T, kv_len=L0 + T, k_top=256, n_sparse=2)
+    say(f"multi-step decode L0={L0} T={T}")
+    inp = gen.make_inputs(wl)
+    dt = wl.dtype
+    qf, k, v = dev_tensor(inp.q_full, dt), dev_tensor(inp.k, dt), dev_tensor(inp.v, dt)
+    qs = [dev_tensor(q, dt) for q in inp.q_sparse]
+    gates = torch.from_numpy(inp.gate_logits).cuda()
+    B, Hq, Hkv, D, K = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.k_top
+    kc = torch.zeros(B, L0 + T, Hkv, D, device="cuda", dtype=k.dtype)
+    vc = torch.zeros_like(kc)
+    hy.hysparse_append_kv(k[:, :L0].contiguous(), v[:, :L0].contiguous(), kc, vc, 0)
+    outs_full, scores, idxs, outs = [], [], [], [[] for _ in qs]
+    for t in range(T):
+        L = L0 + t + 1
+        hy.hysparse_append_kv(k[:, L - 1:L].contiguous(), v[:, L - 1:L].contiguous(), kc, vc, L - 1)
+        res = hy.hysparse_hybrid_block(qf[:, t:t + 1], kc[:, :L], vc[:, :L], [q[:, t:t + 1] for q in qs], gates,
+                                       K, 1, wl.window)
+        torch.cuda.synchronize()
+        outs_full.append(host(res["out_full"]))
+        scores.append(host(res["scores"]).astype(np.float32))
+        idxs.append(host(res["idx"]))
+        for l in range(len(qs)):
+            outs[l].append(host(res["out"][l]))
+    assert torch.equal(kc, k) and torch.equal(vc, v)
+    O_ref, _, S_ref = orc.full_layer(inp.q_full, inp.k, inp.v, 1)
+    idx_all = np.full((B, Hkv, T, K), -1, np.int32)
+    for t in range(T):
+        L = L0 + t + 1
+        assert_attn_close(torch.from_numpy(outs_full[t]), O_ref[:, t:t + 1], dt, f"O_full step {t}")
+        assert_scores_close(torch.from_numpy(scores[t][:, :, 0]), S_ref[:, :, t, :L])
+        for b in range(B):
+            for g in range(Hkv):
+                np.testing.assert_array_equal(idxs[t][b, g, 0], orc.topk_row(scores[t][b, g, 0], L, K))
+                assert eps_valid(idxs[t][b, g, 0], S_ref[b, g, t], L)
+        idx_all[:, :, t] = idxs[t][:, :, 0]
+    for l in range(len(qs)):
+        ref = orc.sparse_layer(inp.q_sparse[l], inp.k, inp.v, idx_all, 1, wl.window, inp.gate_logits[l])
+        got = np.concatenate(outs[l], axis=1)
+        assert_attn_close(torch.from_numpy(got), ref, dt, f"sparse layer {l}")
+
+
+def test_chunked_prefill_matches_one_shot():
+    """A prompt prefilled in chunks (multiples of the 64-query score block):
+    each chunk appends its K/V and runs the full layer with q_len = chunk,
+    kv_len = end of chunk; outputs and score rows equal the one-shot prefill's
+    (oracle), and the top-K on the chunk's scores is that of those rows."""
+    T, chunks = 640, (192, 256, 128, 64)
+    wl = W["prefill32k"].replace(q_len=T, kv_len=T, k_top=160, n_sparse=0)
+    say("chunked prefill")
+    inp = gen.make_inputs(wl)
+    dt = wl.dtype
+    qf, k, v = dev_tensor(inp.q_full, dt), dev_tensor(inp.k, dt), dev_tensor(inp.v, dt)
+    kc, vc = torch.zeros_like(k), torch.zeros_like(v)
+    O_ref, LSE_ref, S_ref = orc.full_layer(inp.q_full, inp.k, inp.v, 64)
+    s0 = 0
+    for c in chunks:
+        e = s0 + c
+        hy.hysparse_append_kv(k[:, s0:e].contiguous(), v[:, s0:e].contiguous(), kc, vc, s0)
+        out, lse, S = hy.hysparse_full_attn_scores(qf[:, s0:e], kc[:, :e], vc[:, :e], 64)
+        idx = hy.hysparse_topk(S.reshape(-1, e), wl.k_top,
+                               valid_len=torch.tensor([min(e, s0 + (n % (c // 64) + 1) * 64)
+                                                       for n in range(S.shape[0] * S.shape[1] * S.shape[2])],
+                                                      dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        n0, n1 = s0 // 64, e // 64
+        assert_attn_close(out, O_ref[:, s0:e], dt, f"O chunk {s0}:{e}")
+        np.testing.assert_allclose(host(lse), LSE_ref[:, :, s0:e], rtol=0, atol=2e-5)
+        Sg = host(S).astype(np.float32)
+        assert_scores_close(S, S_ref[:, :, n0:n1, :e])
+        ih = host(idx).reshape(S.shape[0], S.shape[1], S.shape[2], wl.k_top)
+        for g in range(wl.n_kv_heads):
+            for n in range(n1 - n0):
+                cand = orc.candidate_count(n0 + n, T, T, 64)
+                np.testing.assert_array_equal(ih[0, g, n], orc.topk_row(Sg[0, g, n], cand, wl.k_top))
+        s0 = e
