@@ -210,6 +210,10 @@ def sparse_layer_block(qs, k, v, idx_row, b: int, g: int, n: int, score_block: i
                        window: int, gate_logits, scale=None):
     """Sparse-layer output for the queries of block n and heads of group g.
 
+    gate_logits: [Hq] (one learnable logit per head) or [B, Tq, Hq] (one per
+    token and head: the input-dependent reading g = sigmoid(x . w_h) of the
+    intelliparadigm article's learnable sigmoid gate, section 2.2).
+
     Returns (out [nq, G, D], o_global, o_local) in float64.
     """
     B, Tq, Hq, D = qs.shape
@@ -246,7 +250,11 @@ def sparse_layer_block(qs, k, v, idx_row, b: int, g: int, n: int, score_block: i
     pw, _, _ = _softmax_masked(lw, mw)
     o_l = pw @ Vw
 
-    gate = sigmoid(np.asarray(gate_logits)[g * G:(g + 1) * G])[None, :, None]
+    gl = np.asarray(gate_logits)
+    if gl.ndim == 3:   # one logit per (batch, query, head): [B, Tq, Hq]
+        gate = sigmoid(gl[b, i0:i1, g * G:(g + 1) * G])[:, :, None]
+    else:              # one logit per head: [Hq]
+        gate = sigmoid(gl[g * G:(g + 1) * G])[None, :, None]
     out = gate * o_g + (1.0 - gate) * o_l
     return out, o_g, o_l
 

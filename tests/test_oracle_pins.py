@@ -403,3 +403,45 @@ def test_planted_block_outranks_the_rest():
     S = np.zeros((B, Hkv, 1, T))
     kept, _, _ = orc.hier_select(q, k, S, blk, 3, 8)
     assert 5 in kept[0, 0]
+
+
+# ------------------------------------------------- per-token (input-dependent) gate
+
+def _tok_gate_case():
+    wl = gen.WORKLOADS["prefill32k"].replace(q_len=150, kv_len=150, k_top=40, window=20, n_sparse=1)
+    inp = gen.make_inputs(wl)
+    _, _, S = orc.full_layer(inp.q_full, inp.k, inp.v, 64)
+    idx = orc.select_indices(S, wl.q_len, wl.kv_len, 64, wl.k_top)
+    return wl, inp, idx
+
+
+def test_token_gate_equal_per_token_is_the_head_gate():
+    wl, inp, idx = _tok_gate_case()
+    gh = inp.gate_logits[0]
+    gt = np.broadcast_to(gh, (wl.batch, wl.q_len, wl.n_q_heads)).copy()
+    a = orc.sparse_layer(inp.q_sparse[0], inp.k, inp.v, idx, 64, wl.window, gh)
+    b = orc.sparse_layer(inp.q_sparse[0], inp.k, inp.v, idx, 64, wl.window, gt)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_token_gate_is_local_and_selects_branches_per_token():
+    wl, inp, idx = _tok_gate_case()
+    G = wl.group
+    rng = np.random.default_rng(90)
+    gt = rng.standard_normal((wl.batch, wl.q_len, wl.n_q_heads))
+    base = orc.sparse_layer(inp.q_sparse[0], inp.k, inp.v, idx, 64, wl.window, gt)
+    gt2 = gt.copy()
+    gt2[0, 70, 5] += 1.5                      # one (token, head) logit
+    moved = orc.sparse_layer(inp.q_sparse[0], inp.k, inp.v, idx, 64, wl.window, gt2)
+    diff = np.abs(moved - base).max(axis=-1)[0]
+    assert diff[70, 5] > 0 and np.count_nonzero(diff) == 1
+    # +inf / -inf per token: that token's global / window output, exactly
+    gsel = np.where((np.arange(wl.q_len) % 2 == 0)[None, :, None], np.inf, -np.inf) * np.ones_like(gt)
+    out = orc.sparse_layer(inp.q_sparse[0], inp.k, inp.v, idx, 64, wl.window, gsel)
+    for n in range(wl.n_blocks):
+        i0, i1 = n * 64, min((n + 1) * 64, wl.q_len)
+        _, o_g, o_l = orc.sparse_layer_block(inp.q_sparse[0], inp.k, inp.v, idx[0, 1, n], 0, 1, n, 64, wl.window,
+                                             gsel)
+        rows = np.arange(i0, i1)
+        np.testing.assert_array_equal(out[0, rows[rows % 2 == 0], G:2 * G], o_g[(rows % 2 == 0)])
+        np.testing.assert_array_equal(out[0, rows[rows % 2 == 1], G:2 * G], o_l[(rows % 2 == 1)])
