@@ -141,6 +141,22 @@ hys_status hysparse_sparse_attn(const hys_attn_desc* desc, const void* q, const 
                                 void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Sparse layer with one gate logit per token and head (the input-dependent
+ * reading of the learnable sigmoid gate of intelliparadigm article 2.2,
+ * g = sigmoid(x . w_h) with the projection x . w_h computed by the caller).
+ * The logit of (batch b, query i, query head h) is
+ *   gate_logits[b * gate_stride_b + i * gate_stride_t + h];
+ * strides (Tq * Hq, Hq) read a contiguous [B, Tq, Hq] float32 tensor, strides
+ * (0, 0) one logit per head (exactly hysparse_sparse_attn).  Everything else
+ * as hysparse_sparse_attn.  Errors: negative strides -> HYS_ERR_BAD_SHAPE.
+ */
+hys_status hysparse_sparse_attn_token_gate(const hys_attn_desc* desc, const void* q, const void* k,
+                                           const void* v, const int32_t* idx, int32_t k_top,
+                                           int32_t score_block, int32_t window, const float* gate_logits,
+                                           int64_t gate_stride_b, int64_t gate_stride_t, void* out, void* ws,
+                                           size_t ws_bytes, hipStream_t stream);
+
+/*
  * One hybrid block (intelliparadigm article 2.1 and 3.1): the full layer on
  * q_full, top-K over its scores, then n_sparse sparse layers that reuse its
  * k, v and indices, each with its own queries and gate logits.

@@ -53,7 +53,7 @@ struct DecodeArgs {
   int ld;               // logit row pitch: kv_len rounded up to 4 (16-byte rows)
   float* part_o;
   float* part_ml;
-  const float* gate;    // sparse: [Hq] gate logits
+  GateRef gate;         // sparse: gate logits
   void* out;            // sparse: [B, Tq, Hq, D]
 };
 
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(D) void sparse_merge_kernel(DecodeArgs a) {
       lg += __shfl_xor(lg, off);
       lw += __shfl_xor(lw, off);
     }
-    const float gt = 1.f / (1.f + expf(-a.gate[g * a.G + h]));
+    const float gt = 1.f / (1.f + expf(-a.gate.p[(int64_t)b * a.gate.sb + (int64_t)i * a.gate.st + g * a.G + h]));
     const float L = win ? lw : lg;
     const float scale = (L > 0.f) ? (win ? (1.f - gt) : gt) / L : 0.f;
     if (in) wts[sp] = w * scale;
@@ -655,7 +655,7 @@ hipError_t launch_full_decode(const Geom& g, const void* q, const void* k, const
 
 hipError_t launch_sparse_rows(const Geom& g, const void* q, const void* k, const void* v,
                               const int32_t* idx, int k_top, int score_block, int window,
-                              const float* gate, void* out, void* ws, hipStream_t st) {
+                              const GateRef& gate, void* out, void* ws, hipStream_t st) {
   const DecodePlan p = plan_sparse_rows(g, k_top, window);
   const DecodeWs w = carve_decode_ws(g, p, ws, false);
   DecodeArgs a = make_args(g, p, q, k, v);

@@ -81,9 +81,16 @@ DecodeWs carve_decode_ws(const Geom& g, const DecodePlan& p, void* ws, bool full
 
 hipError_t launch_full_decode(const Geom& g, const void* q, const void* k, const void* v, void* out,
                               float* lse, float* scores, void* ws, hipStream_t st);
+// Gate logits of the sparse layer: the logit of (batch b, query i, query head
+// h) is p[b * sb + i * st + h]; sb = st = 0 is one logit per head.
+struct GateRef {
+  const float* p;
+  int64_t sb, st;
+};
+
 hipError_t launch_sparse_rows(const Geom& g, const void* q, const void* k, const void* v,
                               const int32_t* idx, int k_top, int score_block, int window,
-                              const float* gate, void* out, void* ws, hipStream_t st);
+                              const GateRef& gate, void* out, void* ws, hipStream_t st);
 
 // --------------------------------------------------------------- prefill path
 size_t prefill_full_ws_bytes(const Geom& g, int score_block);
@@ -93,7 +100,7 @@ hipError_t launch_full_prefill(const Geom& g, const void* q, const void* k, cons
 size_t sparse_block_ws_bytes(const Geom& g, int k_top, int window);
 hipError_t launch_sparse_block(const Geom& g, const void* q, const void* k, const void* v,
                                const int32_t* idx, int k_top, int score_block, int window,
-                               const float* gate, void* out, void* ws, hipStream_t st);
+                               const GateRef& gate, void* out, void* ws, hipStream_t st);
 
 // ---------------------------------------------------------------------- top-K
 size_t topk_ws_bytes(int64_t n_rows, int32_t row_len, int32_t k);

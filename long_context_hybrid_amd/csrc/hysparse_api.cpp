@@ -125,7 +125,7 @@ hipError_t run_full(const hys::Geom& g, const void* q, const void* k, const void
 }
 
 hipError_t run_sparse(const hys::Geom& g, const void* q, const void* k, const void* v, const int32_t* idx, int kt,
-                      int sb, int w, const float* gate, void* out, void* ws, hipStream_t st) {
+                      int sb, int w, const hys::GateRef& gate, void* out, void* ws, hipStream_t st) {
   if (sparse_by_rows(g, sb)) return hys::launch_sparse_rows(g, q, k, v, idx, kt, sb, w, gate, out, ws, st);
   return hys::launch_sparse_block(g, q, k, v, idx, kt, sb, w, gate, out, ws, st);
 }
@@ -182,9 +182,18 @@ hys_status hysparse_sparse_attn(const hys_attn_desc* desc, const void* q, const 
                                 const int32_t* idx, int32_t k_top, int32_t score_block, int32_t window,
                                 const float* gate_logits, void* out, void* ws, size_t ws_bytes,
                                 hipStream_t stream) {
+  return hysparse_sparse_attn_token_gate(desc, q, k, v, idx, k_top, score_block, window, gate_logits, 0, 0, out,
+                                         ws, ws_bytes, stream);
+}
+
+hys_status hysparse_sparse_attn_token_gate(const hys_attn_desc* desc, const void* q, const void* k, const void* v,
+                                           const int32_t* idx, int32_t k_top, int32_t score_block, int32_t window,
+                                           const float* gate_logits, int64_t gate_stride_b, int64_t gate_stride_t,
+                                           void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
   hys::Geom g;
   hys_status s;
   if ((s = check_desc(desc, &g))) return s;
+  if (gate_stride_b < 0 || gate_stride_t < 0) return fail(HYS_ERR_BAD_SHAPE, "gate strides must be >= 0");
   if ((s = check_sb(score_block))) return s;
   if (k_top < 1) return fail(HYS_ERR_BAD_SHAPE, "k_top must be >= 1");
   if (window < 1) return fail(HYS_ERR_BAD_SHAPE, "window must be >= 1");
@@ -193,7 +202,8 @@ hys_status hysparse_sparse_attn(const hys_attn_desc* desc, const void* q, const 
       (s = check_tensor(gate_logits, "gate_logits", 4)))
     return s;
   if ((s = check_ws(ws, ws_bytes, sparse_ws(g, score_block, k_top, window)))) return s;
-  return from_hip(run_sparse(g, q, k, v, idx, k_top, score_block, window, gate_logits, out, ws, stream));
+  const hys::GateRef gate{gate_logits, gate_stride_b, gate_stride_t};
+  return from_hip(run_sparse(g, q, k, v, idx, k_top, score_block, window, gate, out, ws, stream));
 }
 
 hys_status hysparse_hybrid_block(const hys_attn_desc* desc, const void* q_full, const void* k, const void* v,
@@ -247,8 +257,8 @@ hys_status hysparse_hybrid_block(const hys_attn_desc* desc, const void* q_full, 
   e = hys::launch_topk(scores, (int64_t)g.B * g.Hkv * NB, g.Tkv, g.Tkv, vl, k_top, idx, inner_ws, stream);
   if (e != hipSuccess) return from_hip(e);
   for (int l = 0; l < n_sparse; ++l) {
-    e = run_sparse(g, q_sparse[l], k, v, idx, k_top, score_block, window, gate_logits + (size_t)l * g.Hq,
-                   out_sparse[l], inner_ws, stream);
+    const hys::GateRef gate{gate_logits + (size_t)l * g.Hq, 0, 0};
+    e = run_sparse(g, q_sparse[l], k, v, idx, k_top, score_block, window, gate, out_sparse[l], inner_ws, stream);
     if (e != hipSuccess) return from_hip(e);
   }
   return ok();

@@ -64,7 +64,7 @@ struct PrefillArgs {
   // sparse
   const int32_t* idx;
   int k_top, window;
-  const float* gate;
+  GateRef gate;
   int nrc;                // row chunks per score block
 };
 
@@ -469,7 +469,6 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
 
   typename TR::frag qf[kRTW][KC];
   int rpos[kRTW];
-  float gt[kRTW];
   bool tile_ok[kRTW];
 #pragma unroll
   for (int x = 0; x < kRTW; ++x) {
@@ -480,7 +479,6 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
     const bool ok = tile_ok[x] && i < a.Tq;
     rpos[x] = ok ? a.Tkv - a.Tq + i : -1;
     load_q_frags<TR, D>(a, b, i, g * a.G + hl, ok, quad, qf[x]);
-    gt[x] = tile_ok[x] ? 1.f / (1.f + expf(-a.gate[g * a.G + hl])) : 0.f;
   }
   int pmin = 0x7fffffff;  // smallest position among the wave's rows
 #pragma unroll
@@ -530,12 +528,14 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
   RowState<kRTW, D> st;
   st.reset();
   // output row (b, i, head) of accumulator row 4 * quad + r of row tile x, or
-  // nullptr for padding rows
-  auto orow_of = [&](int x, int r) -> ST* {
+  // nullptr for padding rows; *gate_out = that row's sigmoid gate
+  auto orow_of = [&](int x, int r, float* gate_out) -> ST* {
     const int rt = rc * (kNW * kRTW) + wave * kRTW + x;
     const int hl = rt / 4, qoff = 16 * (rt % 4);
     const int i = i0 + qoff + 4 * quad + r;
     if (!tile_ok[x] || i >= a.Tq) return nullptr;
+    const float w = a.gate.p[(int64_t)b * a.gate.sb + (int64_t)i * a.gate.st + g * a.G + hl];
+    *gate_out = 1.f / (1.f + expf(-w));
     return (ST*)a.out + (((int64_t)b * a.Tq + i) * a.Hq + g * a.G + hl) * D;
   };
   const int ntiles = nwt + ngt;
@@ -571,8 +571,9 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float lr = __shfl(lt, 4 * quad + r);
-      const float sc = lr > 0.f ? (1.f - gt[x]) / lr : 0.f;
-      ST* orow = orow_of(x, r);
+      float gr = 0.f;
+      ST* orow = orow_of(x, r, &gr);
+      const float sc = lr > 0.f ? (1.f - gr) / lr : 0.f;
       if (orow) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) orow[16 * dt + col] = TR::from_float(st.o[x][dt][r] * sc);
@@ -591,9 +592,10 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float lr = __shfl(lt, 4 * quad + r);
-      ST* orow = orow_of(x, r);
+      float gr = 0.f;
+      ST* orow = orow_of(x, r, &gr);
       if (orow) {
-        const float sc = lr > 0.f ? gt[x] / lr : 0.f;
+        const float sc = lr > 0.f ? gr / lr : 0.f;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
           orow[16 * dt + col] = TR::from_float(st.o[x][dt][r] * sc + TR::to_float(orow[16 * dt + col]));
@@ -688,7 +690,7 @@ hipError_t launch_full_prefill(const Geom& g, const void* q, const void* k, cons
 size_t sparse_block_ws_bytes(const Geom&, int, int) { return 0; }
 
 hipError_t launch_sparse_block(const Geom& g, const void* q, const void* k, const void* v, const int32_t* idx,
-                               int k_top, int score_block, int window, const float* gate, void* out, void* /*ws*/,
+                               int k_top, int score_block, int window, const GateRef& gate, void* out, void* /*ws*/,
                                hipStream_t st) {
   (void)score_block;  // 64 (rows of one block share its index set)
   PrefillArgs a = base_args(g, q, k, v);

@@ -28,7 +28,8 @@ STATUS = {0: "HYS_OK", 1: "HYS_ERR_NULL_PTR", 2: "HYS_ERR_BAD_SHAPE", 3: "HYS_ER
 EXPORTS = ("hysparse_full_attn_scores", "hysparse_topk", "hysparse_sparse_attn", "hysparse_hybrid_block",
            "hysparse_workspace_bytes", "hysparse_topk_workspace_bytes", "hysparse_status_string",
            "hysparse_last_error", "hysparse_version", "hysparse_trace_begin", "hysparse_trace_end",
-           "hysparse_trace_name", "hysparse_hier_select", "hysparse_hier_workspace_bytes", "hysparse_append_kv")
+           "hysparse_trace_name", "hysparse_hier_select", "hysparse_hier_workspace_bytes", "hysparse_append_kv",
+           "hysparse_sparse_attn_token_gate")
 
 
 class HysAttnDesc(ctypes.Structure):
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.hysparse_hier_select.restype = i32
     L.hysparse_hier_workspace_bytes.argtypes = [D, i32, i32, i32]
     L.hysparse_append_kv.argtypes = [D, _P, _P, i32, i32, _P, _P, _P]
+    L.hysparse_sparse_attn_token_gate.argtypes = [D, _P, _P, _P, _P, i32, i32, i32, _P, i64, i64, _P, _P, sz, _P]
+    L.hysparse_sparse_attn_token_gate.restype = i32
     L.hysparse_append_kv.restype = i32
     L.hysparse_hier_workspace_bytes.restype = sz
     L.hysparse_trace_begin.argtypes = [_P, i32]
@@ -205,6 +208,28 @@ def hysparse_sparse_attn(q, k, v, idx, k_top: int, score_block: int, window: int
     _check(lib().hysparse_sparse_attn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), k_top, score_block,
                                       window, _ptr(gate_logits), _ptr(out), _ptr(ws),
                                       0 if ws is None else ws.numel(), _stream(dev)))
+    return out
+
+
+def hysparse_sparse_attn_token_gate(q, k, v, idx, k_top: int, score_block: int, window: int, gate_logits,
+                                    out=None, workspace=None, scale: float = 0.0):
+    """One sparse layer with one gate logit per token and head: gate_logits
+    float32 [B, Tq, Hq] (any strides on the batch and token axes, head axis
+    contiguous); returns out."""
+    dev = _same_device(q, k, v, idx, gate_logits)
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be contiguous int32 [B, Hkv, NB, k_top]")
+    B, Tq, Hq, _ = q.shape
+    if gate_logits.dtype != torch.float32 or gate_logits.dim() != 3 or tuple(gate_logits.shape) != (B, Tq, Hq) \
+            or gate_logits.stride(2) != 1:
+        raise ValueError("gate_logits must be float32 [B, Tq, Hq] with the head axis contiguous")
+    desc = make_desc(q, k, scale)
+    out = torch.empty(q.shape, dtype=q.dtype, device=dev) if out is None else out
+    ws = _workspace(hysparse_workspace_bytes(HYS_OP_SPARSE, desc, score_block, k_top, window), dev, workspace)
+    _check(lib().hysparse_sparse_attn_token_gate(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), k_top,
+                                                 score_block, window, _ptr(gate_logits), gate_logits.stride(0),
+                                                 gate_logits.stride(1), _ptr(out), _ptr(ws),
+                                                 0 if ws is None else ws.numel(), _stream(dev)))
     return out
 
 
