@@ -207,12 +207,15 @@ def sigmoid(w):
 
 
 def sparse_layer_block(qs, k, v, idx_row, b: int, g: int, n: int, score_block: int,
-                       window: int, gate_logits, scale=None):
+                       window: int, gate_logits, scale=None, k_win=None, v_win=None):
     """Sparse-layer output for the queries of block n and heads of group g.
 
     gate_logits: [Hq] (one learnable logit per head) or [B, Tq, Hq] (one per
     token and head: the input-dependent reading g = sigmoid(x . w_h) of the
     intelliparadigm article's learnable sigmoid gate, section 2.2).
+    k_win, v_win: [B, Tkv, Hkv, D] keys and values of the layer's own window
+    branch, by position (the reading in which each sparse layer maintains its
+    own 128-token window, section 2.2); None reads the shared k, v.
 
     Returns (out [nq, G, D], o_global, o_local) in float64.
     """
@@ -242,8 +245,10 @@ def sparse_layer_block(qs, k, v, idx_row, b: int, g: int, n: int, score_block: i
     lo = max(0, int(pos[0]) - window + 1)
     hi = int(pos[-1]) + 1
     wk = np.arange(lo, hi)
-    Kw = k[b, lo:hi, g].astype(F64)
-    Vw = v[b, lo:hi, g].astype(F64)
+    kwin = k if k_win is None else k_win
+    vwin = v if v_win is None else v_win
+    Kw = kwin[b, lo:hi, g].astype(F64)
+    Vw = vwin[b, lo:hi, g].astype(F64)
     lw = scale * (Qb @ Kw.T)
     mw = (wk[None, None, :] <= pos[:, None, None]) & (wk[None, None, :] > pos[:, None, None] - window)
     mw = np.broadcast_to(mw, lw.shape)
@@ -260,8 +265,9 @@ def sparse_layer_block(qs, k, v, idx_row, b: int, g: int, n: int, score_block: i
 
 
 def sparse_layer(qs, k, v, idx, score_block: int, window: int, gate_logits,
-                 scale=None, blocks=None):
-    """One sparse layer over all (or the listed) (b, g, n) units -> [B,Tq,Hq,D] f64."""
+                 scale=None, blocks=None, k_win=None, v_win=None):
+    """One sparse layer over all (or the listed) (b, g, n) units -> [B,Tq,Hq,D] f64
+    (k_win, v_win: the layer's own window keys/values by position, or None)."""
     B, Tq, Hq, D = qs.shape
     Hkv = k.shape[2]
     G = Hq // Hkv
@@ -272,7 +278,7 @@ def sparse_layer(qs, k, v, idx, score_block: int, window: int, gate_logits,
     for (b, g, n) in units:
         i0, i1 = block_query_range(n, Tq, score_block)
         o, _, _ = sparse_layer_block(qs, k, v, idx[b, g, n], b, g, n, score_block,
-                                     window, gate_logits, scale)
+                                     window, gate_logits, scale, k_win, v_win)
         out[b, i0:i1, g * G:(g + 1) * G] = o
     return out
 

@@ -445,3 +445,38 @@ def test_token_gate_is_local_and_selects_branches_per_token():
         rows = np.arange(i0, i1)
         np.testing.assert_array_equal(out[0, rows[rows % 2 == 0], G:2 * G], o_g[(rows % 2 == 0)])
         np.testing.assert_array_equal(out[0, rows[rows % 2 == 1], G:2 * G], o_l[(rows % 2 == 1)])
+
+
+# ------------------------------------------------- own window KV per sparse layer
+
+def test_own_window_kv_gate_zero_is_sliding_window_on_it():
+    """Gate 0: the output is W-key sliding-window attention over the layer's
+    own keys/values (torch SDPA with the band mask), the shared cache unused."""
+    B, T, Hq, Hkv, D, W = 1, 40, 4, 2, 16, 7
+    q, k, v = _rand(31, B, T, Hq, D), _rand(32, B, T, Hkv, D), _rand(33, B, T, Hkv, D)
+    kw, vw = _rand(34, B, T, Hkv, D), _rand(35, B, T, Hkv, D)
+    idx = np.tile(np.arange(8, dtype=np.int32), (B, Hkv, T, 1))
+    out = orc.sparse_layer(q, k, v, idx, 1, W, np.full(Hq, -np.inf), k_win=kw, v_win=vw)
+    i = np.arange(T)
+    band = (i[None, :] <= i[:, None]) & (i[None, :] > i[:, None] - W)
+    for h in range(Hq):
+        ref = _sdpa(q[0, :, h], kw[0, :, h // 2], vw[0, :, h // 2], band, 1.0 / math.sqrt(D))
+        np.testing.assert_allclose(out[0, :, h], ref, atol=1e-12)
+
+
+def test_own_window_kv_equal_to_cache_and_gate_one():
+    """Own window K/V equal to the shared cache give the shared-window result
+    exactly; with gate 1 the window K/V do not matter."""
+    B, T, Hq, Hkv, D, W = 2, 30, 4, 1, 16, 5
+    q, k, v = _rand(41, B, T, Hq, D), _rand(42, B, T, Hkv, D), _rand(43, B, T, Hkv, D)
+    idx = np.tile(np.arange(0, 24, 3, dtype=np.int32), (B, Hkv, T, 1))
+    gl = _rand(44, Hq)
+    a = orc.sparse_layer(q, k, v, idx, 1, W, gl)
+    b = orc.sparse_layer(q, k, v, idx, 1, W, gl, k_win=k.copy(), v_win=v.copy())
+    np.testing.assert_array_equal(a, b)
+    c = orc.sparse_layer(q, k, v, idx, 1, W, np.full(Hq, np.inf))
+    d = orc.sparse_layer(q, k, v, idx, 1, W, np.full(Hq, np.inf), k_win=_rand(45, B, T, Hkv, D),
+                         v_win=_rand(46, B, T, Hkv, D))
+    np.testing.assert_array_equal(c, d)
+    e = orc.sparse_layer(q, k, v, idx, 1, W, gl, k_win=_rand(45, B, T, Hkv, D), v_win=_rand(46, B, T, Hkv, D))
+    assert np.abs(e - a).max() > 1e-3
