@@ -157,6 +157,41 @@ hys_status hysparse_sparse_attn_token_gate(const hys_attn_desc* desc, const void
                                            size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Keys and values of a sparse layer's own window branch (the reading in which
+ * each sparse layer maintains its own 128-token window, intelliparadigm
+ * article 2.2), in desc.dtype with head_dim contiguous.  Position p of batch b
+ * and KV head h is row (ring > 0 ? p % ring : p) of the buffer:
+ *   k, v     16-byte aligned, caller-owned, read.
+ *   stride   element strides of the (batch, row, head) axes, multiples of 16 bytes.
+ *   ring     > 0: a ring of `ring` rows holding the most recent positions
+ *            (decode: ring >= window; prefill: ring >= window + q_len - 1 so
+ *            that every position a call reads has its own row); 0: rows are
+ *            positions (the buffer spans at least kv_len rows).
+ * The caller keeps the buffer current (hysparse_append_kv writes a row).
+ */
+typedef struct {
+  const void* k;
+  const void* v;
+  int64_t stride[3];
+  int32_t ring;
+} hys_window_kv;
+
+/*
+ * The general sparse layer: gate logits as in hysparse_sparse_attn_token_gate
+ * (strides 0, 0: one logit per head) and, when own_window is not NULL, the
+ * window branch over the layer's own window keys/values instead of the shared
+ * cache (the global branch always reads the shared cache at the indices).
+ * Everything else as hysparse_sparse_attn.  Errors: negative gate strides, a
+ * ring shorter than the positions one call reads -> HYS_ERR_BAD_SHAPE;
+ * misaligned window buffers or strides -> HYS_ERR_ALIGN.
+ */
+hys_status hysparse_sparse_attn_ex(const hys_attn_desc* desc, const void* q, const void* k, const void* v,
+                                   const int32_t* idx, int32_t k_top, int32_t score_block, int32_t window,
+                                   const float* gate_logits, int64_t gate_stride_b, int64_t gate_stride_t,
+                                   const hys_window_kv* own_window, void* out, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/*
  * One hybrid block (intelliparadigm article 2.1 and 3.1): the full layer on
  * q_full, top-K over its scores, then n_sparse sparse layers that reuse its
  * k, v and indices, each with its own queries and gate logits.

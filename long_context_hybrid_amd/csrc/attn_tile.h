@@ -52,9 +52,15 @@ struct TileStage {
   u32x4_t vr[NV > 0 ? NV : 1][2];
   int jk;
 
-  // key(t) -> key index of tile entry t, or -1 when the entry is invalid
+  // key(t) -> key index (position) of tile entry t, or -1 when the entry is
+  // invalid; the row read for key j is row(j) of kbase / vbase (identity
+  // unless the keys live in a ring of slots)
   template <class KeyFn>
   __device__ __forceinline__ void load(const ST* kbase, const ST* vbase, int64_t ks_t, KeyFn key) {
+    load(kbase, vbase, ks_t, key, [](int j) { return j; });
+  }
+  template <class KeyFn, class RowFn>
+  __device__ __forceinline__ void load(const ST* kbase, const ST* vbase, int64_t ks_t, KeyFn key, RowFn row) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int s = 0; s < NK; ++s) {
@@ -64,7 +70,7 @@ struct TileStage {
       if (kExactK || x < kTK * L::CPR) {
         const int t = x / L::CPR, c = x - (x / L::CPR) * L::CPR;
         const int j = key(t);
-        kr[s] = *reinterpret_cast<const u32x4_t*>(kbase + (int64_t)(j >= 0 ? j : 0) * ks_t + c * L::EPC);
+        kr[s] = *reinterpret_cast<const u32x4_t*>(kbase + (int64_t)(j >= 0 ? row(j) : 0) * ks_t + c * L::EPC);
       }
     }
     if constexpr (WITH_V) {
@@ -76,7 +82,7 @@ struct TileStage {
 #pragma unroll
           for (int r = 0; r < 2; ++r) {
             const int j = key(2 * kp + r);
-            vr[s][r] = *reinterpret_cast<const u32x4_t*>(vbase + (int64_t)(j >= 0 ? j : 0) * ks_t + c * L::EPC);
+            vr[s][r] = *reinterpret_cast<const u32x4_t*>(vbase + (int64_t)(j >= 0 ? row(j) : 0) * ks_t + c * L::EPC);
           }
         }
       }
@@ -192,13 +198,14 @@ __device__ __forceinline__ void qk_tile(f32x4_t (&sacc)[RTW][4], const typename 
   }
 }
 
-// softmax_tile: masks the logits when `mask` (wave-uniform) is set (valid(rt,
+// mask_vote_tile: masks the logits when `mask` (wave-uniform) is set (valid(rt,
 // j) says whether key j may be used by the lane's row of row tile rt; j < 0
-// marks an invalid tile entry), updates the running max / sum (rescaling O
-// when a max rises), and packs the probabilities as PV's A operand.
+// marks an invalid tile entry), then raises the running maxima that the tile
+// exceeds by more than the slack, rescaling O and l (one wave vote).  After
+// it, exp_pack_tile turns the logits into probabilities.
 template <typename TR, int D, int RTW, class Valid>
-__device__ __forceinline__ void softmax_tile(RowState<RTW, D>& st, f32x4_t (&sacc)[RTW][4], const int* kj,
-                                             float sl2, bool mask, Valid valid, typename TR::frag (&pa)[RTW][2]) {
+__device__ __forceinline__ void mask_vote_tile(RowState<RTW, D>& st, f32x4_t (&sacc)[RTW][4], const int* kj,
+                                               float sl2, bool mask, Valid valid) {
   constexpr int DT = D / 16;
   const int lane = threadIdx.x & 63, quad = lane >> 4;
   if (mask) {  // masked logits in place
@@ -241,6 +248,14 @@ __device__ __forceinline__ void softmax_tile(RowState<RTW, D>& st, f32x4_t (&sac
       }
     }
   }
+}
+
+// exp_pack_tile: probabilities 2^(logit * sl2 - m) of a tile whose maxima
+// mask_vote_tile has settled, added to the row sums and packed as PV's A
+// operand.
+template <typename TR, int D, int RTW>
+__device__ __forceinline__ void exp_pack_tile(RowState<RTW, D>& st, const f32x4_t (&sacc)[RTW][4], float sl2,
+                                              typename TR::frag (&pa)[RTW][2]) {
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
     const float nmu = (st.m[rt] == kNegInf) ? 0.f : -st.m[rt];
@@ -257,6 +272,14 @@ __device__ __forceinline__ void softmax_tile(RowState<RTW, D>& st, f32x4_t (&sac
     pa[rt][0] = TR::pack(p[0], p[1]);
     pa[rt][1] = TR::pack(p[2], p[3]);
   }
+}
+
+// softmax_tile: mask_vote_tile then exp_pack_tile.
+template <typename TR, int D, int RTW, class Valid>
+__device__ __forceinline__ void softmax_tile(RowState<RTW, D>& st, f32x4_t (&sacc)[RTW][4], const int* kj,
+                                             float sl2, bool mask, Valid valid, typename TR::frag (&pa)[RTW][2]) {
+  mask_vote_tile<TR, D, RTW>(st, sacc, kj, sl2, mask, valid);
+  exp_pack_tile<TR, D, RTW>(st, sacc, sl2, pa);
 }
 
 // pv_tile: O += P . V for the wave's row tiles.

@@ -54,6 +54,7 @@ struct DecodeArgs {
   float* part_o;
   float* part_ml;
   GateRef gate;         // sparse: gate logits
+  WinRef win;           // sparse: window branch keys/values (k == nullptr: the shared cache)
   void* out;            // sparse: [B, Tq, Hq, D]
 };
 
@@ -124,6 +125,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
   const ST* kbase = (const ST*)a.k + (int64_t)b * a.ks_b + (int64_t)g * a.ks_h;
   const ST* vbase = (const ST*)a.v + (int64_t)b * a.ks_b + (int64_t)g * a.ks_h;
+  int64_t kst = a.ks_t;  // token stride of the rows this split reads
+  int ring = 0;          // > 0: key j lives in row j % ring
+  if (!FULL && kind == 2 && a.win.k) {  // the layer's own window keys/values
+    kbase = (const ST*)a.win.k + (int64_t)b * a.win.sb + (int64_t)g * a.win.sh;
+    vbase = (const ST*)a.win.v + (int64_t)b * a.win.sb + (int64_t)g * a.win.sh;
+    kst = a.win.st;
+    ring = a.win.ring;
+  }
+  auto row_of = [&](int j) -> int64_t { return j < 0 ? 0 : (ring > 0 ? j % ring : j); };
 
   // B operand: Q^T, lane (head = col, group = quad) holds d = 32c + 8*quad + e
   frag qf[KC];
@@ -157,7 +167,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int j = kjb[16 * kt + col];
-      const ST* kr = kbase + (int64_t)(j >= 0 ? j : 0) * a.ks_t;
+      const ST* kr = kbase + row_of(j) * kst;
 #pragma unroll
       for (int c = 0; c < KC; ++c) kf[kt][c] = TR::template load8_stream<FULL>(kr + 32 * c + 8 * quad);
     }
@@ -168,7 +178,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = kjb[4 * kq + r];
-        vr[pp][r] = load16_stream<FULL>(vbase + (int64_t)(j >= 0 ? j : 0) * a.ks_t + tc * EPC);
+        vr[pp][r] = load16_stream<FULL>(vbase + row_of(j) * kst + tc * EPC);
       }
     }
   };
@@ -655,7 +665,7 @@ hipError_t launch_full_decode(const Geom& g, const void* q, const void* k, const
 
 hipError_t launch_sparse_rows(const Geom& g, const void* q, const void* k, const void* v,
                               const int32_t* idx, int k_top, int score_block, int window,
-                              const GateRef& gate, void* out, void* ws, hipStream_t st) {
+                              const GateRef& gate, const WinRef& win, void* out, void* ws, hipStream_t st) {
   const DecodePlan p = plan_sparse_rows(g, k_top, window);
   const DecodeWs w = carve_decode_ws(g, p, ws, false);
   DecodeArgs a = make_args(g, p, q, k, v);
@@ -667,6 +677,7 @@ hipError_t launch_sparse_rows(const Geom& g, const void* q, const void* k, const
   a.part_o = w.part_o;
   a.part_ml = w.part_ml;
   a.gate = gate;
+  a.win = win;
   a.out = out;
   HYS_DISPATCH(g, {
     {

@@ -88,9 +88,20 @@ struct GateRef {
   int64_t sb, st;
 };
 
+// Keys/values of the sparse layer's window branch: the shared cache (k ==
+// nullptr) or the layer's own window K/V, position j in row (ring > 0 ? j %
+// ring : j), strides in elements.
+struct WinRef {
+  const void* k;
+  const void* v;
+  int64_t sb, st, sh;
+  int ring;
+};
+
 hipError_t launch_sparse_rows(const Geom& g, const void* q, const void* k, const void* v,
                               const int32_t* idx, int k_top, int score_block, int window,
-                              const GateRef& gate, void* out, void* ws, hipStream_t st);
+                              const GateRef& gate, const WinRef& win, void* out, void* ws,
+                              hipStream_t st);
 
 // --------------------------------------------------------------- prefill path
 size_t prefill_full_ws_bytes(const Geom& g, int score_block);
@@ -100,7 +111,8 @@ hipError_t launch_full_prefill(const Geom& g, const void* q, const void* k, cons
 size_t sparse_block_ws_bytes(const Geom& g, int k_top, int window);
 hipError_t launch_sparse_block(const Geom& g, const void* q, const void* k, const void* v,
                                const int32_t* idx, int k_top, int score_block, int window,
-                               const GateRef& gate, void* out, void* ws, hipStream_t st);
+                               const GateRef& gate, const WinRef& win, void* out, void* ws,
+                              hipStream_t st);
 
 // ---------------------------------------------------------------------- top-K
 size_t topk_ws_bytes(int64_t n_rows, int32_t row_len, int32_t k);

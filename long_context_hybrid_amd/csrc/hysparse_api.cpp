@@ -125,9 +125,10 @@ hipError_t run_full(const hys::Geom& g, const void* q, const void* k, const void
 }
 
 hipError_t run_sparse(const hys::Geom& g, const void* q, const void* k, const void* v, const int32_t* idx, int kt,
-                      int sb, int w, const hys::GateRef& gate, void* out, void* ws, hipStream_t st) {
-  if (sparse_by_rows(g, sb)) return hys::launch_sparse_rows(g, q, k, v, idx, kt, sb, w, gate, out, ws, st);
-  return hys::launch_sparse_block(g, q, k, v, idx, kt, sb, w, gate, out, ws, st);
+                      int sb, int w, const hys::GateRef& gate, void* out, void* ws, hipStream_t st,
+                      const hys::WinRef& win = hys::WinRef{nullptr, nullptr, 0, 0, 0, 0}) {
+  if (sparse_by_rows(g, sb)) return hys::launch_sparse_rows(g, q, k, v, idx, kt, sb, w, gate, win, out, ws, st);
+  return hys::launch_sparse_block(g, q, k, v, idx, kt, sb, w, gate, win, out, ws, st);
 }
 
 }  // namespace
@@ -190,10 +191,33 @@ hys_status hysparse_sparse_attn_token_gate(const hys_attn_desc* desc, const void
                                            const int32_t* idx, int32_t k_top, int32_t score_block, int32_t window,
                                            const float* gate_logits, int64_t gate_stride_b, int64_t gate_stride_t,
                                            void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return hysparse_sparse_attn_ex(desc, q, k, v, idx, k_top, score_block, window, gate_logits, gate_stride_b,
+                                 gate_stride_t, nullptr, out, ws, ws_bytes, stream);
+}
+
+hys_status hysparse_sparse_attn_ex(const hys_attn_desc* desc, const void* q, const void* k, const void* v,
+                                   const int32_t* idx, int32_t k_top, int32_t score_block, int32_t window,
+                                   const float* gate_logits, int64_t gate_stride_b, int64_t gate_stride_t,
+                                   const hys_window_kv* own_window, void* out, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
   hys::Geom g;
   hys_status s;
   if ((s = check_desc(desc, &g))) return s;
   if (gate_stride_b < 0 || gate_stride_t < 0) return fail(HYS_ERR_BAD_SHAPE, "gate strides must be >= 0");
+  hys::WinRef win{nullptr, nullptr, 0, 0, 0, 0};
+  if (own_window) {
+    const hys_window_kv& w = *own_window;
+    if ((s = check_tensor(w.k, "own_window.k", 16)) || (s = check_tensor(w.v, "own_window.v", 16))) return s;
+    const int64_t esz = g.dtype == HYS_BF16 ? 2 : 4;
+    for (int x = 0; x < 3; ++x) {
+      if (w.stride[x] < 0) return fail(HYS_ERR_BAD_SHAPE, "negative own-window stride");
+      if ((w.stride[x] * esz) % 16 != 0) return fail(HYS_ERR_ALIGN, "own-window strides must be multiples of 16 bytes");
+    }
+    if (w.ring < 0) return fail(HYS_ERR_BAD_SHAPE, "own_window.ring must be >= 0");
+    if (w.ring > 0 && (int64_t)w.ring < (int64_t)window + g.Tq - 1)
+      return fail(HYS_ERR_BAD_SHAPE, "own_window.ring must be >= window + q_len - 1");
+    win = hys::WinRef{w.k, w.v, w.stride[0], w.stride[1], w.stride[2], w.ring};
+  }
   if ((s = check_sb(score_block))) return s;
   if (k_top < 1) return fail(HYS_ERR_BAD_SHAPE, "k_top must be >= 1");
   if (window < 1) return fail(HYS_ERR_BAD_SHAPE, "window must be >= 1");
@@ -203,7 +227,7 @@ hys_status hysparse_sparse_attn_token_gate(const hys_attn_desc* desc, const void
     return s;
   if ((s = check_ws(ws, ws_bytes, sparse_ws(g, score_block, k_top, window)))) return s;
   const hys::GateRef gate{gate_logits, gate_stride_b, gate_stride_t};
-  return from_hip(run_sparse(g, q, k, v, idx, k_top, score_block, window, gate, out, ws, stream));
+  return from_hip(run_sparse(g, q, k, v, idx, k_top, score_block, window, gate, out, ws, stream, win));
 }
 
 hys_status hysparse_hybrid_block(const hys_attn_desc* desc, const void* q_full, const void* k, const void* v,

@@ -65,6 +65,7 @@ struct PrefillArgs {
   const int32_t* idx;
   int k_top, window;
   GateRef gate;
+  WinRef win;             // window branch keys/values (k == nullptr: the shared cache)
   int nrc;                // row chunks per score block
 };
 
@@ -521,10 +522,21 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
     };
   };
 
+  // window tiles read the layer's own window keys/values when given
+  const ST* wkbase = a.win.k ? (const ST*)a.win.k + (int64_t)b * a.win.sb + (int64_t)g * a.win.sh : kbase;
+  const ST* wvbase = a.win.k ? (const ST*)a.win.v + (int64_t)b * a.win.sb + (int64_t)g * a.win.sh : vbase;
+  const int64_t wst = a.win.k ? a.win.st : a.ks_t;
+  const int ring = a.win.k ? a.win.ring : 0;
+  TileStage<TR, D, kNT, true> stg;
+  auto load_tile = [&](int tile) {
+    if (tile < nwt)
+      stg.load(wkbase, wvbase, wst, key_of(tile), [=](int j) { return ring > 0 ? j % ring : j; });
+    else
+      stg.load(kbase, vbase, a.ks_t, key_of(tile));
+  };
   refill(0);
   __syncthreads();
-  TileStage<TR, D, kNT, true> stg;
-  stg.load(kbase, vbase, a.ks_t, key_of(0));
+  load_tile(0);
   RowState<kRTW, D> st;
   st.reset();
   // output row (b, i, head) of accumulator row 4 * quad + r of row tile x, or
@@ -551,7 +563,7 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
         refill(e1);  // the previous chunk's last reader was load(it), before the barrier above
         __syncthreads();
       }
-      stg.load(kbase, vbase, a.ks_t, key_of(it + 1));
+      load_tile(it + 1);
     }
     return any;
   };
@@ -690,7 +702,8 @@ hipError_t launch_full_prefill(const Geom& g, const void* q, const void* k, cons
 size_t sparse_block_ws_bytes(const Geom&, int, int) { return 0; }
 
 hipError_t launch_sparse_block(const Geom& g, const void* q, const void* k, const void* v, const int32_t* idx,
-                               int k_top, int score_block, int window, const GateRef& gate, void* out, void* /*ws*/,
+                               int k_top, int score_block, int window, const GateRef& gate, const WinRef& win,
+                               void* out, void* /*ws*/,
                                hipStream_t st) {
   (void)score_block;  // 64 (rows of one block share its index set)
   PrefillArgs a = base_args(g, q, k, v);
@@ -699,6 +712,7 @@ hipError_t launch_sparse_block(const Geom& g, const void* q, const void* k, cons
   a.k_top = k_top;
   a.window = window;
   a.gate = gate;
+  a.win = win;
   a.out = out;
   a.nrc = (4 * g.G + kSpNW * kSpRTW - 1) / (kSpNW * kSpRTW);
   const int units = g.B * g.Hkv * a.NB;

@@ -29,7 +29,12 @@ EXPORTS = ("hysparse_full_attn_scores", "hysparse_topk", "hysparse_sparse_attn",
            "hysparse_workspace_bytes", "hysparse_topk_workspace_bytes", "hysparse_status_string",
            "hysparse_last_error", "hysparse_version", "hysparse_trace_begin", "hysparse_trace_end",
            "hysparse_trace_name", "hysparse_hier_select", "hysparse_hier_workspace_bytes", "hysparse_append_kv",
-           "hysparse_sparse_attn_token_gate")
+           "hysparse_sparse_attn_token_gate", "hysparse_sparse_attn_ex")
+
+
+class HysWindowKV(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("stride", ctypes.c_int64 * 3),
+                ("ring", ctypes.c_int32)]
 
 
 class HysAttnDesc(ctypes.Structure):
@@ -81,6 +86,9 @@ def lib() -> ctypes.CDLL:
     L.hysparse_append_kv.argtypes = [D, _P, _P, i32, i32, _P, _P, _P]
     L.hysparse_sparse_attn_token_gate.argtypes = [D, _P, _P, _P, _P, i32, i32, i32, _P, i64, i64, _P, _P, sz, _P]
     L.hysparse_sparse_attn_token_gate.restype = i32
+    L.hysparse_sparse_attn_ex.argtypes = [D, _P, _P, _P, _P, i32, i32, i32, _P, i64, i64,
+                                          ctypes.POINTER(HysWindowKV), _P, _P, sz, _P]
+    L.hysparse_sparse_attn_ex.restype = i32
     L.hysparse_append_kv.restype = i32
     L.hysparse_hier_workspace_bytes.restype = sz
     L.hysparse_trace_begin.argtypes = [_P, i32]
@@ -351,3 +359,43 @@ def hysparse_append_kv(k_new, v_new, k_cache, v_cache, pos: int):
     desc = make_desc(k_cache, k_cache)
     _check(lib().hysparse_append_kv(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), k_new.shape[1], pos,
                                     _ptr(k_cache), _ptr(v_cache), _stream(k_cache.device)))
+
+
+def hysparse_sparse_attn_ex(q, k, v, idx, k_top: int, score_block: int, window: int, gate_logits,
+                            own_k=None, own_v=None, ring: int = 0, out=None, workspace=None, scale: float = 0.0):
+    """The general sparse layer: gate_logits float32 [Hq] (one per head) or
+    [B, Tq, Hq] (one per token and head, head axis contiguous); own_k / own_v
+    [B, rows, Hkv, D] (head_dim contiguous) the layer's own window keys/values
+    (position p in row p % ring, or row p when ring == 0), or None for the
+    shared cache.  Returns out."""
+    dev = _same_device(q, k, v, idx, gate_logits)
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be contiguous int32 [B, Hkv, NB, k_top]")
+    B, Tq, Hq, _ = q.shape
+    if gate_logits.dtype != torch.float32 or gate_logits.stride(-1) != 1:
+        raise ValueError("gate_logits must be float32 with the head axis contiguous")
+    if gate_logits.dim() == 1 and gate_logits.shape[0] == Hq:
+        gsb, gst = 0, 0
+    elif gate_logits.dim() == 3 and tuple(gate_logits.shape) == (B, Tq, Hq):
+        gsb, gst = gate_logits.stride(0), gate_logits.stride(1)
+    else:
+        raise ValueError("gate_logits must be [Hq] or [B, Tq, Hq]")
+    win = None
+    if own_k is not None or own_v is not None:
+        _same_device(q, own_k, own_v)
+        if own_k.shape != own_v.shape or own_k.stride() != own_v.stride() or own_k.dtype != q.dtype \
+                or own_k.dim() != 4 or own_k.stride(3) != 1 or own_k.shape[0] != B or own_k.shape[2:] != k.shape[2:]:
+            raise ValueError("own_k / own_v must be matching [B, rows, Hkv, D] tensors of q's dtype")
+        win = HysWindowKV()
+        win.k, win.v = own_k.data_ptr(), own_v.data_ptr()
+        for x in range(3):
+            win.stride[x] = own_k.stride(x)
+        win.ring = int(ring)
+    desc = make_desc(q, k, scale)
+    out = torch.empty(q.shape, dtype=q.dtype, device=dev) if out is None else out
+    ws = _workspace(hysparse_workspace_bytes(HYS_OP_SPARSE, desc, score_block, k_top, window), dev, workspace)
+    _check(lib().hysparse_sparse_attn_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), k_top,
+                                         score_block, window, _ptr(gate_logits), gsb, gst,
+                                         ctypes.byref(win) if win is not None else None, _ptr(out), _ptr(ws),
+                                         0 if ws is None else ws.numel(), _stream(dev)))
+    return out

@@ -8,7 +8,8 @@ Recipe (one generator per tensor, so every tensor is reproducible alone):
 
 * ``numpy.random.Generator(PCG64(SeedSequence([config_id, tensor_id, layer])))``
   with tensor ids 0 = full-layer query, 1 = keys, 2 = values, 3 = sparse-layer
-  query (``layer`` = 0..N-1), 4 = gate logits, 5 = planted positions.
+  query (``layer`` = 0..N-1), 4 = gate logits, 5 = planted positions, 6 / 7 =
+  a sparse layer's own window keys / values (``own_window_kv``).
 * Values are drawn in float64, cast to float32 (round to nearest even), and for
   bf16 workloads rounded once more to bf16 (round to nearest even).  The arrays
   returned are float32 whose values are exactly the stored ones, so every
@@ -49,7 +50,7 @@ from typing import Optional
 
 import numpy as np
 
-T_QFULL, T_K, T_V, T_QSPARSE, T_GATE, T_PLANT = 0, 1, 2, 3, 4, 5
+T_QFULL, T_K, T_V, T_QSPARSE, T_GATE, T_PLANT, T_KWIN, T_VWIN = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -238,3 +239,12 @@ def make_device_inputs(wl: Workload, device, n_sparse: Optional[int] = None):
     grng = _rng(wl.config_id, T_GATE)
     gates = grng.uniform(-2.0, 2.0, size=(N, Hq)) if wl.gate_dist == "uniform2" else grng.standard_normal(size=(N, Hq))
     return q_full, k, v, q_sparse, torch.from_numpy(gates.astype(np.float32)).to(device)
+
+
+def own_window_kv(wl: Workload, layer: int = 0):
+    """Keys and values of sparse layer ``layer``'s own window branch, by
+    position: [B, Tkv, Hkv, D] each, same distribution and rounding as k, v."""
+    shape = (wl.batch, wl.kv_len, wl.n_kv_heads, wl.head_dim)
+    kw = _store(_normal(_rng(wl.config_id, T_KWIN, layer), shape, wl.std), wl.dtype)
+    vw = _store(_normal(_rng(wl.config_id, T_VWIN, layer), shape, wl.std), wl.dtype)
+    return kw, vw

@@ -167,3 +167,25 @@ def test_append_kv_validation():
     # the query fields are not read: a query shape that the attention calls reject is fine here
     q_bad = _desc(Tq=500, Tkv=100, Hq=3)
     assert L.hysparse_append_kv(ctypes.byref(q_bad), FAKE, FAKE, 0, 0, FAKE, FAKE, None) == 2   # still n_new
+
+
+def test_sparse_ex_validation():
+    L = hy.lib()
+    d = _desc(Tq=1, Tkv=256)
+    w = hy.HysWindowKV()
+    w.k, w.v = 0x10000, 0x20000
+    for x, s in enumerate((128 * 2 * 128, 2 * 128, 128)):
+        w.stride[x] = s
+    w.ring = 100                                     # window 128 needs ring >= 128
+    args = lambda win, gsb=0: (ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, 1, 128, FAKE, gsb, 0, win, FAKE, FAKE,
+                               1 << 30, None)
+    assert L.hysparse_sparse_attn_ex(*args(ctypes.byref(w))) == 2
+    assert L.hysparse_sparse_attn_ex(*args(None, gsb=-1)) == 2
+    w.ring = 0
+    w.stride[1] = 129                                # not a multiple of 16 bytes
+    assert L.hysparse_sparse_attn_ex(*args(ctypes.byref(w))) == 4
+    w.stride[1] = 2 * 128
+    w.k = 0x10004                                    # misaligned buffer
+    assert L.hysparse_sparse_attn_ex(*args(ctypes.byref(w))) == 4
+    w.k = None
+    assert L.hysparse_sparse_attn_ex(*args(ctypes.byref(w))) == 1
