@@ -4,8 +4,9 @@
 // one query row of one KV group with all of that group's query heads
 // (G <= 16 heads padded to the 16 rows of a 16x16 MFMA tile):
 //   * full layer (decode):  key list = the whole cache 0..Tkv-1; the scaled
-//     logits are also written (base 2) so that the importance scores can be
-//     formed once the log-sum-exp of every head is known;
+//     logits are also written (base 2, key-major: the group's heads of one
+//     key side by side) so that the importance scores can be formed once the
+//     log-sum-exp of every head is known;
 //   * sparse layer (one query row per score row): key list = the row's top-K
 //     indices (global branch) followed by the W window keys (local branch);
 //     a split covers either global or window entries, never both.
@@ -49,8 +50,9 @@ struct DecodeArgs {
   const int32_t* idx;
   int k_top, score_block, NB, window;
   int chunk, wchunk, nsplit, nsg;
-  float* logits;        // full decode: base-2 logits, rows of ld floats
-  int ld;               // logit row pitch: kv_len rounded up to 4 (16-byte rows)
+  float* logits;        // full decode: base-2 logits, key-major (see logit_slots)
+  int lgp;              // logit slots per key: G rounded up to 4, 8 or 16
+  int64_t lus;          // floats per unit of the logit scratch
   float* part_o;
   float* part_ml;
   GateRef gate;         // sparse: gate logits
@@ -151,8 +153,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
   ST* vt = reinterpret_cast<ST*>(smem) + (size_t)wave * D * VP;
   int* kj = kj_s[wave];
-  float* lg_row = nullptr;
-  if (FULL && col < a.G) lg_row = a.logits + ((int64_t)b * a.Hq + g * a.G + col) * a.ld;
+  // full layer: this unit's logits, key-major [key][lgp] (heads of a key
+  // contiguous, so a wave writes each step's logits as whole 1 KB runs)
+  float* lg_unit = FULL ? a.logits + (int64_t)unit * a.lus : nullptr;
 
   // key index of list entry t (-1: past the list, negative index or after pos)
   auto key_at = [&](int t) -> int {
@@ -223,24 +226,21 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     float mt = kNegInf;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      bool all_valid = true;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = kjc[16 * kt + 4 * quad + r];
         s[kt][r] = (j >= 0) ? sacc[kt][r] * a.sl2 : kNegInf;
-        all_valid = all_valid && (j >= 0);
         mt = fmaxf(mt, s[kt][r]);
       }
-      if (FULL && lg_row != nullptr) {
-        // full layer: list entry t is key t, so the four keys are consecutive
-        const int j0 = t0 + 16 * kt + 4 * quad;
-        if (all_valid) {
-          *reinterpret_cast<float4*>(lg_row + j0) = make_float4(s[kt][0], s[kt][1], s[kt][2], s[kt][3]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (j0 + r < t_end) lg_row[j0 + r] = s[kt][r];
-        }
+      if constexpr (FULL) {
+        // lane (head col, quad) holds keys 4*quad + r; after the transpose
+        // inside each lane quad it holds heads (col & ~3) + e of key
+        // 4*quad + (col & 3).  List entry t is key t in the full layer.
+        float w[4] = {s[kt][0], s[kt][1], s[kt][2], s[kt][3]};
+        quad_transpose4(w);
+        const int j = t0 + 16 * kt + 4 * quad + (col & 3);
+        if (col < a.lgp && j < t_end)
+          *reinterpret_cast<float4*>(lg_unit + (int64_t)j * a.lgp + (col & ~3)) = make_float4(w[0], w[1], w[2], w[3]);
       }
     }
     mt = wave_max16x4(mt);
@@ -417,8 +417,9 @@ __global__ __launch_bounds__(D) void sparse_merge_kernel(DecodeArgs a) {
 struct FinishArgs {
   const float* part_o;
   const float* part_ml;
-  const float* logits;
-  int ld;               // logit row pitch (multiple of 4)
+  const float* logits;  // key-major [unit][key][lgp]
+  int lgp;              // logit slots per key (4, 8 or 16)
+  int64_t lus;          // floats per unit of the logit scratch
   int nsplit, G, Hkv, Tkv, nchunk, units;
   void* out;
   float* lse;
@@ -426,34 +427,93 @@ struct FinishArgs {
 };
 
 // Base-2 log-sum-exp of every head of a unit from its split states, into
-// lse_s[0..G).  All 256 threads take part; the reduction order is fixed, so
-// every workgroup of the finish kernel computes bit-identical values.
+// lse_s[0..G).  16 threads per head each fold a strided subset of the
+// splits' (m, l) pairs in one pass (eight loads in flight), then a 16-lane
+// butterfly folds the threads; the order is fixed, so every workgroup of the
+// finish kernel computes bit-identical values.
+__device__ __forceinline__ void fold_ml(float& M, float& L, float m, float l) {
+  const float Mn = fmaxf(M, m);
+  const float mu = (Mn == kNegInf) ? 0.f : Mn;
+  L = L * exp2f(M - mu) + l * exp2f(m - mu);
+  M = Mn;
+}
 __device__ __forceinline__ void unit_lse2(const float* pml, int nsplit, int G, float* lse_s) {
-  // 16 threads per head, each over a strided subset of splits, then a
-  // 16-lane butterfly
   const int tid = threadIdx.x, h = tid >> 4, t = tid & 15;
-  float M = kNegInf;
-  if (h < G)
-    for (int sp = t; sp < nsplit; sp += 16) M = fmaxf(M, pml[(sp * G + h) * 2]);
+  float M = kNegInf, L = 0.f;
+  if (h < G) {
+    for (int base = t; base < nsplit; base += 16 * 8) {
+      float2 v[8];
 #pragma unroll
-  for (int off = 8; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
-  const float mu = (M == kNegInf) ? 0.f : M;
-  float L = 0.f;
-  if (h < G)
-    for (int sp = t; sp < nsplit; sp += 16) L += pml[(sp * G + h) * 2 + 1] * exp2f(pml[(sp * G + h) * 2] - mu);
+      for (int u = 0; u < 8; ++u) {
+        const int sp = base + 16 * u;
+        v[u] = sp < nsplit ? *reinterpret_cast<const float2*>(pml + (sp * G + h) * 2) : make_float2(kNegInf, 0.f);
+      }
 #pragma unroll
-  for (int off = 8; off > 0; off >>= 1) L += __shfl_xor(L, off, 16);
-  if (h < G && t == 0) lse_s[h] = (L > 0.f) ? mu + log2f(L) : kNegInf;
+      for (int u = 0; u < 8; ++u) fold_ml(M, L, v[u].x, v[u].y);
+    }
+  }
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) {
+    const float m2 = __shfl_xor(M, off, 16), l2 = __shfl_xor(L, off, 16);
+    fold_ml(M, L, m2, l2);
+  }
+  if (h < G && t == 0) lse_s[h] = (L > 0.f) ? M + log2f(L) : kNegInf;
   __syncthreads();
 }
 
-// Blocks [0, units*G): output row of one (unit, head): O = sum_s 2^(m_s - lse2) O_s.
-// Blocks [units*G, ...): importance scores of one chunk of keys of a unit:
+// Importance scores of a wave's 256 keys (4 groups of 64) from the
+// key-major logits, Q = lgp / 4 lanes per key.  The wave reads the logits
+// as whole 1 KB runs: in run xi of a group, lane l holds heads 4*(l % Q) ..
+// +3 of key (64/Q)*xi + l/Q; a DPP sum over the key's Q lanes gives its S.
+// (The scratch holds nchunk * kScoreChunk keys per unit, so every run is in
+// it; keys past kv_len are read but not stored.)
+template <int Q>
+__device__ __forceinline__ void score_runs(const FinishArgs& f, int unit, int key0, const float* lse_s) {
+  constexpr int NR = 4 * Q;   // 1 KB runs
+  constexpr int KPR = 64 / Q; // keys per run
+  const int lane = threadIdx.x & 63, hg = lane % Q;
+  float L[4];
+  bool hv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hv[e] = 4 * hg + e < f.G;
+    L[e] = hv[e] ? lse_s[4 * hg + e] : 0.f;
+  }
+  const float* lg = f.logits + (int64_t)unit * f.lus + (int64_t)key0 * (4 * Q);
+  float4 x[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) x[r] = *reinterpret_cast<const float4*>(lg + r * 256 + 4 * lane);
+  float* srow = f.scores + (int64_t)unit * f.Tkv;
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) {
+    float mine = 0.f;
+#pragma unroll
+    for (int xi = 0; xi < Q; ++xi) {
+      const float4 v = x[grp * Q + xi];
+      float p = 0.f;
+      p += hv[0] ? fast_exp2(v.x - L[0]) : 0.f;
+      p += hv[1] ? fast_exp2(v.y - L[1]) : 0.f;
+      p += hv[2] ? fast_exp2(v.z - L[2]) : 0.f;
+      p += hv[3] ? fast_exp2(v.w - L[3]) : 0.f;
+      if constexpr (Q >= 2) p += dpp_quad<0xB1>(p);
+      if constexpr (Q == 4) p += dpp_quad<0x4E>(p);
+      mine = (xi == hg) ? p : mine;
+    }
+    const int j = key0 + 64 * grp + KPR * hg + lane / Q;
+    if (j < f.Tkv) srow[j] = mine;
+  }
+}
+
+// Blocks [0, units*G): output row of one (unit, head): O = sum_s 2^(m_s - lse2) O_s,
+//   256 threads = D/4 float4 columns x NPH split phases, eight splits in flight.
+// Blocks [units*G, ...): importance scores of one chunk of kScoreChunk keys of a unit:
 //   S[b, g, 0, j] = sum over the group's heads of 2^(logit2[h, j] - lse2[h]).
 template <typename TR, int D>
 __global__ __launch_bounds__(256) void decode_full_finish_kernel(FinishArgs f) {
+  constexpr int DV = D / 4;      // float4 columns of a row
+  constexpr int NPH = 256 / DV;  // split phases of the row merge
   __shared__ float lse_s[16];
-  __shared__ float red[256 / D][D];
+  __shared__ __align__(16) float red[NPH][D];
   const int tid = threadIdx.x;
   const int nrow = f.units * f.G;
   const int Hq = f.Hkv * f.G;
@@ -464,55 +524,49 @@ __global__ __launch_bounds__(256) void decode_full_finish_kernel(FinishArgs f) {
     const float* po = f.part_o + (int64_t)unit * f.nsplit * f.G * D;
     unit_lse2(pml, f.nsplit, f.G, lse_s);
     const float l2 = lse_s[h];
-    constexpr int NS = 256 / D;  // split phases
-    const int d = tid % D, ph = tid / D;
-    float acc = 0.f;
-#pragma unroll 4
-    for (int sp = ph; sp < f.nsplit; sp += NS) acc += exp2f(pml[(sp * f.G + h) * 2] - l2) * po[((int64_t)sp * f.G + h) * D + d];
-    red[ph][d] = acc;
+    const int d4 = tid % DV, ph = tid / DV;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int base = ph; base < f.nsplit; base += NPH * 8) {
+      float m[8];
+      float4 o[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int sp = base + NPH * u;
+        const bool in = sp < f.nsplit;
+        m[u] = in ? pml[(sp * f.G + h) * 2] : kNegInf;
+        o[u] = in ? *reinterpret_cast<const float4*>(po + ((int64_t)sp * f.G + h) * D + 4 * d4)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = exp2f(m[u] - l2);
+        acc.x += w * o[u].x;
+        acc.y += w * o[u].y;
+        acc.z += w * o[u].z;
+        acc.w += w * o[u].w;
+      }
+    }
+    *reinterpret_cast<float4*>(&red[ph][4 * d4]) = acc;
     __syncthreads();
-    if (ph == 0) {
-      for (int x = 1; x < NS; ++x) acc += red[x][d];
+    if (tid < D) {
+      float sum = 0.f;
+      for (int x = 0; x < NPH; ++x) sum += red[x][tid];
       const int hq = g * f.G + h;
-      reinterpret_cast<typename TR::storage*>(f.out)[((int64_t)b * Hq + hq) * D + d] = TR::from_float(acc);
-      if (d == 0 && f.lse) f.lse[(int64_t)b * Hq + hq] = l2 * kLn2;
+      reinterpret_cast<typename TR::storage*>(f.out)[((int64_t)b * Hq + hq) * D + tid] = TR::from_float(sum);
+      if (tid == 0 && f.lse) f.lse[(int64_t)b * Hq + hq] = l2 * kLn2;
     }
     return;
   }
   const int bid = blockIdx.x - nrow;
   const int unit = bid / f.nchunk, c = bid - (bid / f.nchunk) * f.nchunk;
-  const int b = unit / f.Hkv, g = unit - b * f.Hkv;
   unit_lse2(f.part_ml + (int64_t)unit * f.nsplit * f.G * 2, f.nsplit, f.G, lse_s);
-  float* srow = f.scores + (int64_t)unit * f.Tkv;
-  const bool vec_out = (f.Tkv & 3) == 0;  // the score row itself has pitch Tkv
-  for (int sub = 0; sub < kScoreChunk / 1024; ++sub) {
-    const int j0 = c * kScoreChunk + sub * 1024 + 4 * tid;
-    if (j0 >= f.Tkv) break;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    const float* row0 = f.logits + ((int64_t)b * Hq + g * f.G) * f.ld;
-    // all the group's rows in flight at once, then the exponentials (the
-    // logit rows are padded to a multiple of 4: the lanes past Tkv read
-    // padding and are not stored)
-    float4 x[16];
-#pragma unroll
-    for (int h = 0; h < 16; ++h)
-      if (h < f.G) x[h] = *reinterpret_cast<const float4*>(row0 + (int64_t)h * f.ld + j0);
-#pragma unroll
-    for (int h = 0; h < 16; ++h)
-      if (h < f.G) {
-        const float L = lse_s[h];
-        acc[0] += fast_exp2(x[h].x - L);
-        acc[1] += fast_exp2(x[h].y - L);
-        acc[2] += fast_exp2(x[h].z - L);
-        acc[3] += fast_exp2(x[h].w - L);
-      }
-    if (vec_out && j0 + 3 < f.Tkv) {
-      *reinterpret_cast<float4*>(srow + j0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    } else {
-      for (int e = 0; e < 4; ++e)
-        if (j0 + e < f.Tkv) srow[j0 + e] = acc[e];
-    }
-  }
+  const int key0 = c * kScoreChunk + (tid >> 6) * (kScoreChunk / 4);  // the wave's 256 keys
+  if (f.lgp == 4)
+    score_runs<1>(f, unit, key0, lse_s);
+  else if (f.lgp == 8)
+    score_runs<2>(f, unit, key0, lse_s);
+  else
+    score_runs<4>(f, unit, key0, lse_s);
 }
 
 DecodeArgs make_args(const Geom& g, const DecodePlan& p, const void* q, const void* k, const void* v) {
@@ -602,12 +656,19 @@ DecodePlan plan_sparse_rows(const Geom& g, int k_top, int window) {
   return p;
 }
 
-static int logit_pitch(const Geom& g) { return (g.Tkv + 3) & ~3; }
+// Full-decode logit scratch: per unit (b, g), key-major rows of lgp slots
+// (the group's G heads, padded to 4, 8 or 16), for kv_len rounded up to
+// whole score chunks.
+static int logit_slots(const Geom& g) { return g.G <= 4 ? 4 : (g.G <= 8 ? 8 : 16); }
+static int64_t logit_unit_floats(const Geom& g) {
+  const int64_t keys = (int64_t)(g.Tkv + kScoreChunk - 1) / kScoreChunk * kScoreChunk;
+  return keys * logit_slots(g);
+}
 
 static size_t decode_ws(const Geom& g, const DecodePlan& p, bool full) {
   size_t n = align_up((size_t)p.units * p.nsplit * g.G * g.D * sizeof(float));
   n += align_up((size_t)p.units * p.nsplit * g.G * 2 * sizeof(float));
-  if (full) n += align_up((size_t)g.B * g.Hq * logit_pitch(g) * sizeof(float));
+  if (full) n += align_up((size_t)p.units * logit_unit_floats(g) * sizeof(float));
   return n;
 }
 
@@ -633,14 +694,16 @@ hipError_t launch_full_decode(const Geom& g, const void* q, const void* k, const
   const DecodeWs w = carve_decode_ws(g, p, ws, true);
   DecodeArgs a = make_args(g, p, q, k, v);
   a.logits = w.logits;
-  a.ld = logit_pitch(g);
+  a.lgp = logit_slots(g);
+  a.lus = logit_unit_floats(g);
   a.part_o = w.part_o;
   a.part_ml = w.part_ml;
   FinishArgs f{};
   f.part_o = w.part_o;
   f.part_ml = w.part_ml;
   f.logits = w.logits;
-  f.ld = logit_pitch(g);
+  f.lgp = logit_slots(g);
+  f.lus = logit_unit_floats(g);
   f.nsplit = p.nsplit;
   f.G = g.G;
   f.Hkv = g.Hkv;

@@ -173,4 +173,35 @@ __device__ __forceinline__ float wave_sum16x4(float x) {
   return a + b;
 }
 
+// DPP quad_perm move inside each group of four lanes: CTRL 0xB1 = lanes
+// [1,0,3,2] (partner l ^ 1), 0x4E = [2,3,0,1] (partner l ^ 2).
+template <int CTRL>
+__device__ __forceinline__ float dpp_quad(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// 4 x 4 transpose inside each group of four lanes: lane i (= l & 3) holds
+// v[0..3] on entry and, on exit, v[k] = the entry v[i] of the group's lane k.
+// Two exchange stages (lane bit 0 with value bit 0, then lane bit 1 with
+// value bit 1), each two DPP moves.
+__device__ __forceinline__ void quad_transpose4(float (&v)[4]) {
+  const bool b0 = threadIdx.x & 1, b1 = threadIdx.x & 2;
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) {
+    const float recv = dpp_quad<0xB1>(b0 ? v[2 * hi] : v[2 * hi + 1]);
+    if (b0)
+      v[2 * hi] = recv;
+    else
+      v[2 * hi + 1] = recv;
+  }
+#pragma unroll
+  for (int lo = 0; lo < 2; ++lo) {
+    const float recv = dpp_quad<0x4E>(b1 ? v[lo] : v[2 + lo]);
+    if (b1)
+      v[lo] = recv;
+    else
+      v[2 + lo] = recv;
+  }
+}
+
 }  // namespace hys

@@ -73,7 +73,7 @@ DecodePlan plan_sparse_rows(const Geom& g, int k_top, int window);
 struct DecodeWs {
   float* part_o;   // [units, nsplit, G, D]
   float* part_ml;  // [units, nsplit, G, 2]
-  float* logits;   // full only: [B, Hq, Tkv] base-2 scaled logits
+  float* logits;   // full only: base-2 scaled logits, [B, Hkv, keys, slots] (key-major)
 };
 size_t decode_full_ws_bytes(const Geom& g);
 size_t decode_sparse_ws_bytes(const Geom& g, int k_top, int window);
