@@ -203,9 +203,9 @@ __device__ __forceinline__ void qk_tile(f32x4_t (&sacc)[RTW][4], const typename 
 // marks an invalid tile entry), then raises the running maxima that the tile
 // exceeds by more than the slack, rescaling O and l (one wave vote).  After
 // it, exp_pack_tile turns the logits into probabilities.
-template <typename TR, int D, int RTW, class Valid>
-__device__ __forceinline__ void mask_vote_tile(RowState<RTW, D>& st, f32x4_t (&sacc)[RTW][4], const int* kj,
-                                               float sl2, bool mask, Valid valid) {
+template <typename TR, int D, int RTW, class Keys, class Valid>
+__device__ __forceinline__ void mask_vote_tile_k(RowState<RTW, D>& st, f32x4_t (&sacc)[RTW][4], Keys keys,
+                                                 float sl2, bool mask, Valid valid) {
   constexpr int DT = D / 16;
   const int lane = threadIdx.x & 63, quad = lane >> 4;
   if (mask) {  // masked logits in place
@@ -213,7 +213,7 @@ __device__ __forceinline__ void mask_vote_tile(RowState<RTW, D>& st, f32x4_t (&s
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = kj[16 * kt + 4 * quad + r];
+        const int j = keys(16 * kt + 4 * quad + r);
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt)
           if (!(j >= 0 && valid(rt, j))) sacc[rt][kt][r] = kNegInf;
@@ -248,6 +248,13 @@ __device__ __forceinline__ void mask_vote_tile(RowState<RTW, D>& st, f32x4_t (&s
       }
     }
   }
+}
+
+// The staged-tile form: tile entry e's key index is kj[e].
+template <typename TR, int D, int RTW, class Valid>
+__device__ __forceinline__ void mask_vote_tile(RowState<RTW, D>& st, f32x4_t (&sacc)[RTW][4], const int* kj,
+                                               float sl2, bool mask, Valid valid) {
+  mask_vote_tile_k<TR, D, RTW>(st, sacc, [kj](int e) { return kj[e]; }, sl2, mask, valid);
 }
 
 // exp_pack_tile: probabilities 2^(logit * sl2 - m) of a tile whose maxima
@@ -310,6 +317,109 @@ __device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename
   typename TR::frag pa[RTW][2];
   softmax_tile<TR, D, RTW>(st, sacc, kj, sl2, mask, valid, pa);
   pv_tile<TR, D, RTW>(st, pa, sm);
+}
+
+// ------------------------------------------------------ LDS-DMA staged tiles
+// bf16, head_dim 128.  A stage holds one 64-key tile, K then V, each as 64
+// unpadded 256-byte rows written by global_load_lds_dwordx4: one instruction
+// fills 1 KB (four rows, lane l -> bytes 16 l .. 16 l + 15), and the lane ->
+// global address mapping decides which 16-byte chunk lands in which slot.
+// Chunk c (elements 8c .. 8c + 7) of key k sits in slot
+//   K: c ^ (k & 15)      the 16 lanes of an A-fragment read (16 keys, one
+//                        chunk) hit 16 different slots;
+//   V: c ^ 2 (k & 7)     a transposed read (4 keys x 2 chunks per 16 lanes)
+//                        hits 8 different slots, and lane groups 0 / 1 use
+//                        the two halves of the banks.
+// The DMA needs no staging registers and no LDS store instructions; the
+// caller keeps several stages in flight and waits with vmcnt.
+#define HYS_LDS __attribute__((address_space(3)))
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+struct DmaTile {
+  static constexpr int kRow = 256;           // bytes per key row (128 bf16)
+  static constexpr int kHalf = kTK * kRow;   // 16 KB: K, then V
+  static constexpr int kBytes = 2 * kHalf;
+};
+
+// Issue the DMA of tile keys t0 .. t0 + 63 into `stage`; keys past `last`
+// (kv_len - 1) are loaded from row `last` and must be masked by the caller.
+// The NW waves share the 32 one-kilobyte instructions (32 / NW each).
+template <int NW>
+__device__ __forceinline__ void dma_tile(unsigned char* stage, const uint16_t* kbase, const uint16_t* vbase,
+                                         int64_t ks_t, int t0, int last) {
+  static_assert(16 % NW == 0, "waves must divide the 16 instructions per tensor");
+  constexpr int IPW = 16 / NW;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, slot = lane & 15;
+#pragma unroll
+  for (int x = 0; x < IPW; ++x) {
+    const int m = wave * IPW + x;  // rows 4m .. 4m + 3
+    const int row = 4 * m + (lane >> 4);
+    const int64_t j = min(t0 + row, last);
+    __builtin_amdgcn_global_load_lds(kbase + j * ks_t + 8 * (slot ^ (row & 15)),
+                                     (HYS_LDS void*)(stage + 1024 * m), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vbase + j * ks_t + 8 * (slot ^ (2 * (row & 7))),
+                                     (HYS_LDS void*)(stage + DmaTile::kHalf + 1024 * m), 16, 0, 0);
+  }
+}
+
+// K fragment (same lanes and k order as lds_k_frag) from a DMA stage.
+__device__ __forceinline__ bf16x8_t dma_k_frag(const unsigned char* stage, int kt, int c, int col, int quad) {
+  const int row = 16 * kt + col;  // row & 15 == col
+  return __builtin_bit_cast(bf16x8_t,
+                            *reinterpret_cast<const u32x4_t*>(stage + row * DmaTile::kRow + (((4 * c + quad) ^ col) << 4)));
+}
+
+// V fragment for P.V (same lanes and key order as lds_v_frag) from a DMA
+// stage, with the gfx950 transposed LDS read: in each group of 16 lanes,
+// lane L receives element L & 3 of the 8-byte read of lane 4e + (L >> 2) as
+// its element e.  Lane s of the group reads key r0 + (s >> 2), columns
+// d0 + 4 (s & 3) .. +3, so lane L receives keys r0 .. r0 + 3 of column
+// d0 + L.
+__device__ __forceinline__ bf16x8_t dma_v_frag(const unsigned char* stage, int dt, int kk, int col, int quad) {
+  const unsigned char* vs = stage + DmaTile::kHalf;
+  const int d = 16 * dt + 4 * (col & 3);
+  const int r0 = 32 * kk + 4 * quad + (col >> 2);
+  auto rd = [&](int row) {
+    const int off = row * DmaTile::kRow + (((d >> 3) ^ (2 * (row & 7))) << 4) + 8 * (col & 1);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((HYS_LDS i16x4_t*)(vs + off));
+  };
+  const i16x4_t lo = rd(r0), hi = rd(r0 + 16);
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, both);
+}
+
+// The attention step on a DMA stage whose tile starts at key j0 (tile entry
+// e is key j0 + e).
+template <int RTW, class Valid>
+__device__ __forceinline__ void attend_tile_dma(RowState<RTW, 128>& st, const bf16x8_t (&qf)[RTW][4],
+                                                const unsigned char* stage, int j0, float sl2, bool mask,
+                                                Valid valid) {
+  const int lane = threadIdx.x & 63, col = lane & 15, quad = lane >> 4;
+  f32x4_t sacc[RTW][4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    bf16x8_t kf[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kf[c] = dma_k_frag(stage, kt, c, col, quad);
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      sacc[rt][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) BF16::mma(sacc[rt][kt], kf[c], qf[rt][c]);
+    }
+  }
+  bf16x8_t pa[RTW][2];
+  mask_vote_tile_k<BF16, 128, RTW>(st, sacc, [j0](int e) { return j0 + e; }, sl2, mask, valid);
+  exp_pack_tile<BF16, 128, RTW>(st, sacc, sl2, pa);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const bf16x8_t vb = dma_v_frag(stage, dt, kk, col, quad);
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt) BF16::mma(st.o[rt][dt], pa[rt][kk], vb);
+    }
 }
 
 // Whether a wave must mask a staged tile: some entry is invalid (j < 0) or

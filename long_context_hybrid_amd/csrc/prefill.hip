@@ -46,6 +46,19 @@ constexpr int kFwdNW = kFwdShape[0], kFwdRTW = kFwdShape[1], kFwdWPE = kFwdShape
 constexpr int kScNW = kScShape[0], kScRTW = kScShape[1];
 constexpr int kSpNW = kSpShape[0], kSpRTW = kSpShape[1];
 constexpr int kIdxCh = 1024;                // sparse layer: selected indices staged in LDS per refill
+// Forward sweep, bf16 with head_dim 128: tiles staged by LDS DMA into a ring
+// of kDmaStages stages (the next two tiles in flight while one is used).
+#ifndef HYS_FWD_DMA
+#define HYS_FWD_DMA 1
+#endif
+constexpr int kDmaStages = 3;
+
+// wait until at most N of this wave's vector-memory operations are
+// outstanding (they complete in issue order) and its LDS reads are done
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
 
 struct PrefillArgs {
   const void* q;
@@ -85,14 +98,17 @@ __device__ __forceinline__ void load_q_frags(const PrefillArgs& a, int b, int i,
 }
 
 // ------------------------------------------------------------- sweep 1: fwd
-template <typename TR, int D, int kNW, int kRTW, int kWPE>
+// DMA: tiles come into a ring of LDS stages by global_load_lds (bf16,
+// head_dim 128); otherwise through registers into one LDS tile.
+template <typename TR, int D, int kNW, int kRTW, int kWPE, bool DMA>
 __global__ __launch_bounds__(kNW * 64, kWPE) void prefill_fwd_kernel(PrefillArgs a) {
   constexpr int kNT = kNW * 64;
   using ST = typename TR::storage;
   using L = TileLayout<TR, D>;
   constexpr int KC = D / 32, DT = D / 16;
-  __shared__ __align__(16) unsigned char sm[L::kBytes];
-  __shared__ int kj[kTK];
+  static_assert(!DMA || (TR::kBytes == 2 && D == 128), "DMA staging is for bf16, head_dim 128");
+  __shared__ __align__(16) unsigned char sm[DMA ? kDmaStages * DmaTile::kBytes : L::kBytes];
+  __shared__ int kj[DMA ? 1 : kTK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, quad = lane >> 4;
   const int per_qt = a.B * a.Hkv * a.NHC;
   const int qt = a.nqt - 1 - (int)(blockIdx.x / per_qt);  // longest causal prefixes first
@@ -124,20 +140,56 @@ __global__ __launch_bounds__(kNW * 64, kWPE) void prefill_fwd_kernel(PrefillArgs
   const ST* vbase = (const ST*)a.v + (int64_t)b * a.ks_b + (int64_t)g * a.ks_h;
   const int Tkv = a.Tkv;
 
-  TileStage<TR, D, kNT, true> stg;
-  stg.load(kbase, vbase, a.ks_t, [=](int t) { return t < Tkv ? t : -1; });
   RowState<kRTW, D> st;
   st.reset();
-  for (int it = 0; it < nkt; ++it) {
-    __syncthreads();
-    stg.store(sm, kj);
-    __syncthreads();
-    if (it + 1 < nkt) {
-      const int t0 = (it + 1) * kTK;
-      stg.load(kbase, vbase, a.ks_t, [=](int t) { return t0 + t < Tkv ? t0 + t : -1; });
+  if constexpr (DMA) {
+    // Ring of kDmaStages stages: at step it, tile it is used while tiles
+    // it + 1 and it + 2 are in flight.  Each wave waits for its own DMA of
+    // tile it (at most the 2 * 16 / kNW instructions of tile it + 1 may remain
+    // outstanding); the barrier then makes every wave's part visible and
+    // frees the stage of tile it - 1 for tile it + 2.  Keys past kv_len are
+    // loaded from row kv_len - 1 and masked (they lie after every position).
+    constexpr int kDmaPerTile = 2 * 16 / kNW;
+    const uint16_t* kb = reinterpret_cast<const uint16_t*>(kbase);
+    const uint16_t* vb = reinterpret_cast<const uint16_t*>(vbase);
+    const int last = Tkv - 1;
+    dma_tile<kNW>(sm, kb, vb, a.ks_t, 0, last);
+    if (nkt > 1) dma_tile<kNW>(sm + DmaTile::kBytes, kb, vb, a.ks_t, kTK, last);
+    // The Q fragments must be resident before the loop: the compiler cannot
+    // count the ring's loads across steps and would otherwise wait for all
+    // of them (vmcnt 0) at the first MFMA of every step.
+#pragma unroll
+    for (int rt = 0; rt < kRTW; ++rt)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) asm volatile("" ::"v"(qf[rt][c]));
+    int cur = 0;  // stage of tile it; tile it + 2 goes to the stage of tile it - 1
+    for (int it = 0; it < nkt; ++it) {
+      if (it + 1 < nkt)
+        wait_vm_lgkm<kDmaPerTile>();
+      else
+        wait_vm_lgkm<0>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const int nxt = cur == 0 ? kDmaStages - 1 : cur - 1;
+      if (it + 2 < nkt) dma_tile<kNW>(sm + nxt * DmaTile::kBytes, kb, vb, a.ks_t, (it + 2) * kTK, last);
+      attend_tile_dma<kRTW>(st, qf, sm + cur * DmaTile::kBytes, it * kTK, a.sl2, (it + 1) * kTK - 1 > pmin,
+                            [&](int rt, int j) { return j <= rpos[rt]; });
+      cur = cur == kDmaStages - 1 ? 0 : cur + 1;
     }
-    attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, (it + 1) * kTK - 1 > pmin,
-                             [&](int rt, int j) { return j <= rpos[rt]; });
+  } else {
+    TileStage<TR, D, kNT, true> stg;
+    stg.load(kbase, vbase, a.ks_t, [=](int t) { return t < Tkv ? t : -1; });
+    for (int it = 0; it < nkt; ++it) {
+      __syncthreads();
+      stg.store(sm, kj);
+      __syncthreads();
+      if (it + 1 < nkt) {
+        const int t0 = (it + 1) * kTK;
+        stg.load(kbase, vbase, a.ks_t, [=](int t) { return t0 + t < Tkv ? t0 + t : -1; });
+      }
+      attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, (it + 1) * kTK - 1 > pmin,
+                               [&](int rt, int j) { return j <= rpos[rt]; });
+    }
   }
 
 #pragma unroll
@@ -684,7 +736,8 @@ hipError_t launch_full_prefill(const Geom& g, const void* q, const void* k, cons
   HYS_PF_DISPATCH(g, {
     {
       TraceScope ts(st, "full_prefill_fwd");
-      prefill_fwd_kernel<TR, DD, kFwdNW, kFwdRTW, kFwdWPE><<<a.nqt * g.B * g.Hkv * a.NHC, kFwdNW * 64, 0, st>>>(a);
+      constexpr bool kDma = HYS_FWD_DMA && TR::kBytes == 2 && DD == 128;
+      prefill_fwd_kernel<TR, DD, kFwdNW, kFwdRTW, kFwdWPE, kDma><<<a.nqt * g.B * g.Hkv * a.NHC, kFwdNW * 64, 0, st>>>(a);
     }
     if (score_block == 64) {
       TraceScope ts(st, "full_prefill_scores");
