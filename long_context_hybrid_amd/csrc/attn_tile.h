@@ -362,6 +362,23 @@ __device__ __forceinline__ void dma_tile(unsigned char* stage, const uint16_t* k
   }
 }
 
+// K only (16 KB stage): the NW waves share the 16 one-kilobyte instructions.
+template <int NW>
+__device__ __forceinline__ void dma_tile_k(unsigned char* stage, const uint16_t* kbase, int64_t ks_t, int t0,
+                                           int last) {
+  static_assert(16 % NW == 0, "waves must divide the 16 instructions per tensor");
+  constexpr int IPW = 16 / NW;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, slot = lane & 15;
+#pragma unroll
+  for (int x = 0; x < IPW; ++x) {
+    const int m = wave * IPW + x;
+    const int row = 4 * m + (lane >> 4);
+    const int64_t j = min(t0 + row, last);
+    __builtin_amdgcn_global_load_lds(kbase + j * ks_t + 8 * (slot ^ (row & 15)),
+                                     (HYS_LDS void*)(stage + 1024 * m), 16, 0, 0);
+  }
+}
+
 // K fragment (same lanes and k order as lds_k_frag) from a DMA stage.
 __device__ __forceinline__ bf16x8_t dma_k_frag(const unsigned char* stage, int kt, int c, int col, int quad) {
   const int row = 16 * kt + col;  // row & 15 == col

@@ -51,6 +51,9 @@ constexpr int kIdxCh = 1024;                // sparse layer: selected indices st
 #ifndef HYS_FWD_DMA
 #define HYS_FWD_DMA 1
 #endif
+#ifndef HYS_SC_DMA
+#define HYS_SC_DMA 1
+#endif
 constexpr int kDmaStages = 3;
 
 // wait until at most N of this wave's vector-memory operations are
@@ -224,18 +227,20 @@ __global__ __launch_bounds__(kNW * 64, kWPE) void prefill_fwd_kernel(PrefillArgs
 // ---------------------------------------------------------- sweep 2: scores
 // One staged tile for the streaming score sweep: per key, the sum of P over
 // the wave's RTW row tiles, written to wred[key] (lanes of quad 0).
-template <typename TR, int D, int RTW, bool MASK>
+// kfrag(ct, c): K fragment of key sub-tile ct, k-step c; keys(e): key index
+// of tile entry e (-1: invalid).
+template <typename TR, int D, int RTW, bool MASK, class KFrag, class Keys>
 __device__ __forceinline__ void block_score_tile(const typename TR::frag (&qf)[RTW][D / 32],
                                                  const float (&nl)[RTW][4], const int (&rowpos)[RTW][4],
-                                                 const unsigned char* sm, const int* kj, float sl2, float* wred) {
+                                                 KFrag kfrag, Keys keys, float sl2, float* wred) {
   constexpr int KC = D / 32;
   const int lane = threadIdx.x & 63, col = lane & 15, quad = lane >> 4;
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     typename TR::frag kf[KC];
 #pragma unroll
-    for (int c = 0; c < KC; ++c) kf[c] = lds_k_frag<TR, D>(sm, ct, c, col, quad);
-    const int j = MASK ? kj[16 * ct + col] : 0;
+    for (int c = 0; c < KC; ++c) kf[c] = kfrag(ct, c);
+    const int j = MASK ? keys(16 * ct + col) : 0;
     float pr[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int x = 0; x < RTW; ++x) {
@@ -304,16 +309,22 @@ __device__ __forceinline__ void score_tile(const typename TR::frag (&qf)[RTW][D 
 // 16 * (rt % 4) ..); every pass streams keys [0, last(n)] through LDS.  Per
 // tile each wave sums P over its rows per key into red[wave][key]; the
 // workgroup adds the wave sums in a fixed order and writes S (first pass) or
-// adds to it (later passes; the same thread owns the same key in every pass).
-template <typename TR, int D, int kNW, int kRTW>
-__global__ __launch_bounds__(kNW * 64) void prefill_block_scores_kernel(PrefillArgs a) {
+// adds to it (later passes; the same thread owns the same key in every pass,
+// so the order of the additions is fixed).
+// DMA (bf16, head_dim 128): K tiles come into a ring of three LDS stages by
+// global_load_lds, one barrier per tile, the wave sums double-buffered; the
+// later passes add with a no-return atomic so that no load waits inside the
+// ring.  Otherwise: global -> registers -> one LDS tile.
+template <typename TR, int D, int kNW, int kRTW, bool DMA>
+__global__ __launch_bounds__(kNW * 64, 2) void prefill_block_scores_kernel(PrefillArgs a) {
   constexpr int kNT = kNW * 64;
   using ST = typename TR::storage;
   using L = TileLayout<TR, D>;
   constexpr int KC = D / 32;
-  __shared__ __align__(16) unsigned char sm[L::kKBytes];
-  __shared__ int kj[kTK];
-  __shared__ float red[kNW * kTK];
+  static_assert(!DMA || (TR::kBytes == 2 && D == 128), "DMA staging is for bf16, head_dim 128");
+  __shared__ __align__(16) unsigned char sm[DMA ? kDmaStages * DmaTile::kHalf : L::kKBytes];
+  __shared__ int kj[DMA ? 1 : kTK];
+  __shared__ float red[DMA ? 2 : 1][kNW * kTK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, quad = lane >> 4;
   const int per_n = a.B * a.Hkv;
   const int n = a.NB - 1 - (int)(blockIdx.x / per_n);
@@ -344,43 +355,97 @@ __global__ __launch_bounds__(kNW * 64) void prefill_block_scores_kernel(PrefillA
         const int i = i0 + qoff + col;
         load_q_frags<TR, D>(a, b, i, g * a.G + hl, rt < RT && i < a.Tq, quad, qf[x]);
       }
+      // the LSE of the lane's four rows, loaded unconditionally (clamped
+      // index) so the loads are in flight together
+      const float* l2row = a.lse2 + ((int64_t)b * a.Hq + g * a.G + min(hl, a.G - 1)) * a.Tq;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + qoff + 4 * quad + r;
         const bool ok = rt < RT && i < a.Tq;
         rowpos[x][r] = ok ? a.Tkv - a.Tq + i : -1;
-        nl[x][r] = ok ? -a.lse2[((int64_t)b * a.Hq + g * a.G + hl) * a.Tq + i] : kNegInf;
+        const float l2 = l2row[min(i, a.Tq - 1)];
+        nl[x][r] = ok ? -l2 : kNegInf;
         pmin = ok ? min(pmin, rowpos[x][r]) : pmin;
       }
     }
     pmin = wave_min_int(pmin);
-    auto flush = [&](int t) {  // tile t's key sums -> S (threads 0..63)
+    // tile t's key sums (red buffer rb) -> S (threads 0..63)
+    auto flush = [&](int t, int rb) {
       const int j = t * kTK + tid;
       if (j < Tkv) {
         float v = 0.f;
 #pragma unroll
-        for (int w = 0; w < kNW; ++w) v += red[w * kTK + tid];
-        srow[j] = ps == 0 ? v : srow[j] + v;
+        for (int w = 0; w < kNW; ++w) v += red[rb][w * kTK + tid];
+        if (ps == 0)
+          srow[j] = v;
+        else if (DMA)
+          atomicAddNoRet(srow + j, v);
+        else
+          srow[j] += v;
       }
     };
-    TileStage<TR, D, kNT, false> stg;
-    stg.load(kbase, kbase, a.ks_t, [=](int t) { return t < Tkv ? t : -1; });
-    for (int it = 0; it < nkt; ++it) {
+    if constexpr (DMA) {
+      constexpr int kDmaPerTile = 16 / kNW;
+      const uint16_t* kb = reinterpret_cast<const uint16_t*>(kbase);
+      const int last = Tkv - 1;
+      // every wave is done with the previous pass's stages and sums
       __syncthreads();
-      if (it > 0 && tid < kTK) flush(it - 1);
-      stg.store(sm, kj);
-      __syncthreads();
-      if (it + 1 < nkt) {
-        const int t0 = (it + 1) * kTK;
-        stg.load(kbase, kbase, a.ks_t, [=](int t) { return t0 + t < Tkv ? t0 + t : -1; });
+      dma_tile_k<kNW>(sm, kb, a.ks_t, 0, last);
+      if (nkt > 1) dma_tile_k<kNW>(sm + DmaTile::kHalf, kb, a.ks_t, kTK, last);
+      // resident Q / LSE before the ring (see the forward sweep)
+#pragma unroll
+      for (int x = 0; x < kRTW; ++x) {
+#pragma unroll
+        for (int c = 0; c < KC; ++c) asm volatile("" ::"v"(qf[x][c]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) asm volatile("" ::"v"(nl[x][r]));
       }
-      if (tile_needs_mask(kj, pmin))
-        block_score_tile<TR, D, kRTW, true>(qf, nl, rowpos, sm, kj, a.sl2, red + wave * kTK);
-      else
-        block_score_tile<TR, D, kRTW, false>(qf, nl, rowpos, sm, kj, a.sl2, red + wave * kTK);
+      int cur = 0;
+      for (int it = 0; it < nkt; ++it) {
+        if (it + 1 < nkt)
+          wait_vm_lgkm<kDmaPerTile>();
+        else
+          wait_vm_lgkm<0>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (it > 0 && tid < kTK) flush(it - 1, (it - 1) & 1);
+        const int nxt = cur == 0 ? kDmaStages - 1 : cur - 1;
+        if (it + 2 < nkt) dma_tile_k<kNW>(sm + nxt * DmaTile::kHalf, kb, a.ks_t, (it + 2) * kTK, last);
+        const unsigned char* stage = sm + cur * DmaTile::kHalf;
+        const int j0 = it * kTK;
+        auto kfrag = [&](int ct, int c) { return dma_k_frag(stage, ct, c, col, quad); };
+        auto keys = [&](int e) { return j0 + e < Tkv ? j0 + e : -1; };
+        float* wred = red[it & 1] + wave * kTK;
+        if ((it + 1) * kTK - 1 > pmin)
+          block_score_tile<TR, D, kRTW, true>(qf, nl, rowpos, kfrag, keys, a.sl2, wred);
+        else
+          block_score_tile<TR, D, kRTW, false>(qf, nl, rowpos, kfrag, keys, a.sl2, wred);
+        cur = cur == kDmaStages - 1 ? 0 : cur + 1;
+      }
+      __syncthreads();
+      if (tid < kTK) flush(nkt - 1, (nkt - 1) & 1);
+    } else {
+      TileStage<TR, D, kNT, false> stg;
+      stg.load(kbase, kbase, a.ks_t, [=](int t) { return t < Tkv ? t : -1; });
+      auto kfrag = [&](int ct, int c) { return lds_k_frag<TR, D>(sm, ct, c, col, quad); };
+      auto keys = [&](int e) { return kj[e]; };
+      for (int it = 0; it < nkt; ++it) {
+        __syncthreads();
+        if (it > 0 && tid < kTK) flush(it - 1, 0);
+        stg.store(sm, kj);
+        __syncthreads();
+        if (it + 1 < nkt) {
+          const int t0 = (it + 1) * kTK;
+          stg.load(kbase, kbase, a.ks_t, [=](int t) { return t0 + t < Tkv ? t0 + t : -1; });
+        }
+        if (tile_needs_mask(kj, pmin))
+          block_score_tile<TR, D, kRTW, true>(qf, nl, rowpos, kfrag, keys, a.sl2, red[0] + wave * kTK);
+        else
+          block_score_tile<TR, D, kRTW, false>(qf, nl, rowpos, kfrag, keys, a.sl2, red[0] + wave * kTK);
+      }
+      __syncthreads();
+      if (tid < kTK) flush(nkt - 1, 0);
     }
-    __syncthreads();
-    if (tid < kTK) flush(nkt - 1);
   }
 }
 
@@ -741,7 +806,8 @@ hipError_t launch_full_prefill(const Geom& g, const void* q, const void* k, cons
     }
     if (score_block == 64) {
       TraceScope ts(st, "full_prefill_scores");
-      prefill_block_scores_kernel<TR, DD, kScNW, kScRTW><<<a.NB * g.B * g.Hkv, kScNW * 64, 0, st>>>(a);
+      constexpr bool kDma = HYS_SC_DMA && TR::kBytes == 2 && DD == 128;
+      prefill_block_scores_kernel<TR, DD, kScNW, kScRTW, kDma><<<a.NB * g.B * g.Hkv, kScNW * 64, 0, st>>>(a);
     } else {
       a.nqb = (g.Tq + 15) / 16;
       a.nkr = (g.Tkv + 127) / 128;
