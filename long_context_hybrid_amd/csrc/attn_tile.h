@@ -335,6 +335,28 @@ __device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename
 #define HYS_LDS __attribute__((address_space(3)))
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
+// One 16-byte-per-lane LDS DMA: lane l's 16 bytes at `gaddr` go to LDS
+// address lds + 16 l (lds must be the same in every lane: it is M0).  Written
+// as inline asm so that the compiler's own wait insertion, which cannot tell
+// the ring's stages apart, does not drain the DMA before every LDS read; the
+// callers wait with explicit vmcnt counts (these loads complete in issue
+// order, so loads unknown to the compiler only make its waits stricter).
+// M0 is saved and restored around the load (the compiler owns it), and one
+// wait state separates the M0 write from the LDS DMA that reads it.
+__device__ __forceinline__ void lds_dma16(const void* gaddr, HYS_LDS void* lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gaddr), "s"(m0v)
+      : "memory");
+}
+
 struct DmaTile {
   static constexpr int kRow = 256;           // bytes per key row (128 bf16)
   static constexpr int kHalf = kTK * kRow;   // 16 KB: K, then V
@@ -355,10 +377,8 @@ __device__ __forceinline__ void dma_tile(unsigned char* stage, const uint16_t* k
     const int m = wave * IPW + x;  // rows 4m .. 4m + 3
     const int row = 4 * m + (lane >> 4);
     const int64_t j = min(t0 + row, last);
-    __builtin_amdgcn_global_load_lds(kbase + j * ks_t + 8 * (slot ^ (row & 15)),
-                                     (HYS_LDS void*)(stage + 1024 * m), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vbase + j * ks_t + 8 * (slot ^ (2 * (row & 7))),
-                                     (HYS_LDS void*)(stage + DmaTile::kHalf + 1024 * m), 16, 0, 0);
+    lds_dma16(kbase + j * ks_t + 8 * (slot ^ (row & 15)), (HYS_LDS void*)(stage + 1024 * m));
+    lds_dma16(vbase + j * ks_t + 8 * (slot ^ (2 * (row & 7))), (HYS_LDS void*)(stage + DmaTile::kHalf + 1024 * m));
   }
 }
 
@@ -374,8 +394,7 @@ __device__ __forceinline__ void dma_tile_k(unsigned char* stage, const uint16_t*
     const int m = wave * IPW + x;
     const int row = 4 * m + (lane >> 4);
     const int64_t j = min(t0 + row, last);
-    __builtin_amdgcn_global_load_lds(kbase + j * ks_t + 8 * (slot ^ (row & 15)),
-                                     (HYS_LDS void*)(stage + 1024 * m), 16, 0, 0);
+    lds_dma16(kbase + j * ks_t + 8 * (slot ^ (row & 15)), (HYS_LDS void*)(stage + 1024 * m));
   }
 }
 
@@ -406,11 +425,11 @@ __device__ __forceinline__ bf16x8_t dma_v_frag(const unsigned char* stage, int d
   return __builtin_bit_cast(bf16x8_t, both);
 }
 
-// The attention step on a DMA stage whose tile starts at key j0 (tile entry
-// e is key j0 + e).
-template <int RTW, class Valid>
+// The attention step on a DMA stage; keys(e) is the key index of tile entry
+// e (-1: invalid), evaluated only when the tile is masked.
+template <int RTW, class Keys, class Valid>
 __device__ __forceinline__ void attend_tile_dma(RowState<RTW, 128>& st, const bf16x8_t (&qf)[RTW][4],
-                                                const unsigned char* stage, int j0, float sl2, bool mask,
+                                                const unsigned char* stage, Keys keys, float sl2, bool mask,
                                                 Valid valid) {
   const int lane = threadIdx.x & 63, col = lane & 15, quad = lane >> 4;
   f32x4_t sacc[RTW][4];
@@ -427,7 +446,7 @@ __device__ __forceinline__ void attend_tile_dma(RowState<RTW, 128>& st, const bf
     }
   }
   bf16x8_t pa[RTW][2];
-  mask_vote_tile_k<BF16, 128, RTW>(st, sacc, [j0](int e) { return j0 + e; }, sl2, mask, valid);
+  mask_vote_tile_k<BF16, 128, RTW>(st, sacc, keys, sl2, mask, valid);
   exp_pack_tile<BF16, 128, RTW>(st, sacc, sl2, pa);
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)

@@ -175,8 +175,9 @@ __global__ __launch_bounds__(kNW * 64, kWPE) void prefill_fwd_kernel(PrefillArgs
       asm volatile("" ::: "memory");
       const int nxt = cur == 0 ? kDmaStages - 1 : cur - 1;
       if (it + 2 < nkt) dma_tile<kNW>(sm + nxt * DmaTile::kBytes, kb, vb, a.ks_t, (it + 2) * kTK, last);
-      attend_tile_dma<kRTW>(st, qf, sm + cur * DmaTile::kBytes, it * kTK, a.sl2, (it + 1) * kTK - 1 > pmin,
-                            [&](int rt, int j) { return j <= rpos[rt]; });
+      const int j0 = it * kTK;
+      attend_tile_dma<kRTW>(st, qf, sm + cur * DmaTile::kBytes, [j0](int e) { return j0 + e; }, a.sl2,
+                            (it + 1) * kTK - 1 > pmin, [&](int rt, int j) { return j <= rpos[rt]; });
       cur = cur == kDmaStages - 1 ? 0 : cur + 1;
     }
   } else {
@@ -379,7 +380,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void prefill_block_scores_kernel(Prefi
         if (ps == 0)
           srow[j] = v;
         else if (DMA)
-          atomicAddNoRet(srow + j, v);
+          unsafeAtomicAdd(srow + j, v);  // no-return hardware fp32 add
         else
           srow[j] += v;
       }
@@ -558,6 +559,9 @@ __global__ __launch_bounds__(kNW * 64) void prefill_scores_kernel(PrefillArgs a)
 }
 
 // ------------------------------------------------------------ sparse block
+// Indices staged kIdxCh at a time, tiles global -> registers -> one LDS tile,
+// empty tiles skipped.  (The LDS-DMA ring of the full layer's sweeps made
+// this kernel slower: it is not bound by the latency of its loads.)
 template <typename TR, int D, int kNW, int kRTW>
 __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
   constexpr int kNT = kNW * 64;
@@ -607,53 +611,14 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
   const int W = a.window;
   const int wlo = max(0, pos_first - W + 1);
   const int nwt = (pos_last - wlo) / kTK + 1;
-  const int ngt = (a.k_top + kTK - 1) / kTK;
   const int32_t* idx_row = a.idx + ((int64_t)(b * a.Hkv + g) * a.NB + n) * a.k_top;
   const int ktop = a.k_top;
-  // The selected indices are staged in LDS kIdxCh at a time (validated: -1
-  // for padding and for keys after the block), so a gathered tile's row loads
-  // do not wait on an index load from global memory.
-  int* idx_s = idx_stage;
-  auto refill = [&](int e0) {
-    constexpr int kPer = (kIdxCh + kNT - 1) / kNT;  // fixed count: the loads are in flight together
-    int jv[kPer];
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      const int x = tid + r * kNT, e = e0 + x;
-      jv[r] = (x < kIdxCh && e < ktop) ? idx_row[e] : -1;
-    }
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      const int x = tid + r * kNT;
-      if (x < kIdxCh) idx_s[x] = (jv[r] >= 0 && jv[r] <= pos_last) ? jv[r] : -1;
-    }
-  };
-  auto key_of = [=](int tile) {
-    return [=](int t) -> int {
-      if (tile < nwt) {
-        const int j = wlo + tile * kTK + t;
-        return j <= pos_last ? j : -1;
-      }
-      const int e = (tile - nwt) * kTK + t;
-      return e < ktop ? idx_s[e & (kIdxCh - 1)] : -1;
-    };
-  };
-
   // window tiles read the layer's own window keys/values when given
   const ST* wkbase = a.win.k ? (const ST*)a.win.k + (int64_t)b * a.win.sb + (int64_t)g * a.win.sh : kbase;
   const ST* wvbase = a.win.k ? (const ST*)a.win.v + (int64_t)b * a.win.sb + (int64_t)g * a.win.sh : vbase;
   const int64_t wst = a.win.k ? a.win.st : a.ks_t;
   const int ring = a.win.k ? a.win.ring : 0;
-  TileStage<TR, D, kNT, true> stg;
-  auto load_tile = [&](int tile) {
-    if (tile < nwt)
-      stg.load(wkbase, wvbase, wst, key_of(tile), [=](int j) { return ring > 0 ? j % ring : j; });
-    else
-      stg.load(kbase, vbase, a.ks_t, key_of(tile));
-  };
-  refill(0);
-  __syncthreads();
-  load_tile(0);
+
   RowState<kRTW, D> st;
   st.reset();
   // output row (b, i, head) of accumulator row 4 * quad + r of row tile x, or
@@ -667,53 +632,96 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
     *gate_out = 1.f / (1.f + expf(-w));
     return (ST*)a.out + (((int64_t)b * a.Tq + i) * a.Hq + g * a.G + hl) * D;
   };
-  const int ntiles = nwt + ngt;
-  // stage the current tile, prefetch the next one; returns whether any entry
-  // of the staged tile is a key
-  auto stage = [&](int it) -> int {
-    __syncthreads();
-    stg.store(sm, kj);
-    const int any = __syncthreads_or(tid < kTK && stg.jk >= 0);
-    if (it + 1 < ntiles) {
-      const int e1 = (it + 1 - nwt) * kTK;  // first list entry of the next tile
-      if (e1 > 0 && (e1 & (kIdxCh - 1)) == 0) {
-        refill(e1);  // the previous chunk's last reader was load(it), before the barrier above
-        __syncthreads();
-      }
-      load_tile(it + 1);
-    }
-    return any;
-  };
-  // The two branches run as two loops (one live output state; separate loops
-  // keep the register pressure of one attention step each).
-  for (int it = 0; it < nwt; ++it) {
-    if (stage(it))
-      attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, true,
-                               [&](int rt, int j) { return j <= rpos[rt] && j > rpos[rt] - W; });
-  }
   // window branch done: its share (1 - g) * o_window goes to the output now
   // (read back by the same lanes in the epilogue); restart for the global
-  // branch
+  // branch (two live output states would not fit the registers)
+  auto window_share = [&]() {
 #pragma unroll
-  for (int x = 0; x < kRTW; ++x) {
-    const float lt = wave_sum16x4(st.l[x]);
+    for (int x = 0; x < kRTW; ++x) {
+      const float lt = wave_sum16x4(st.l[x]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float lr = __shfl(lt, 4 * quad + r);
-      float gr = 0.f;
-      ST* orow = orow_of(x, r, &gr);
-      const float sc = lr > 0.f ? (1.f - gr) / lr : 0.f;
-      if (orow) {
+      for (int r = 0; r < 4; ++r) {
+        const float lr = __shfl(lt, 4 * quad + r);
+        float gr = 0.f;
+        ST* orow = orow_of(x, r, &gr);
+        const float sc = lr > 0.f ? (1.f - gr) / lr : 0.f;
+        if (orow) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) orow[16 * dt + col] = TR::from_float(st.o[x][dt][r] * sc);
+          for (int dt = 0; dt < DT; ++dt) orow[16 * dt + col] = TR::from_float(st.o[x][dt][r] * sc);
+        }
       }
     }
-  }
-  st.reset();
-  for (int it = nwt; it < ntiles; ++it) {
-    if (stage(it))
-      attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, tile_needs_mask(kj, pmin),
-                               [&](int rt, int j) { return j <= rpos[rt]; });
+    st.reset();
+  };
+  auto window_valid = [&](int rt, int j) { return j <= rpos[rt] && j > rpos[rt] - W; };
+  auto causal_valid = [&](int rt, int j) { return j <= rpos[rt]; };
+
+  {
+    const int ngt = (ktop + kTK - 1) / kTK;
+    // The selected indices are staged in LDS kIdxCh at a time (validated: -1
+    // for padding and for keys after the block), so a gathered tile's row loads
+    // do not wait on an index load from global memory.
+    int* idx_s = idx_stage;
+    auto refill = [&](int e0) {
+      constexpr int kPer = (kIdxCh + kNT - 1) / kNT;  // fixed count: the loads are in flight together
+      int jv[kPer];
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const int x = tid + r * kNT, e = e0 + x;
+        jv[r] = (x < kIdxCh && e < ktop) ? idx_row[e] : -1;
+      }
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const int x = tid + r * kNT;
+        if (x < kIdxCh) idx_s[x] = (jv[r] >= 0 && jv[r] <= pos_last) ? jv[r] : -1;
+      }
+    };
+    auto key_of = [=](int tile) {
+      return [=](int t) -> int {
+        if (tile < nwt) {
+          const int j = wlo + tile * kTK + t;
+          return j <= pos_last ? j : -1;
+        }
+        const int e = (tile - nwt) * kTK + t;
+        return e < ktop ? idx_s[e & (kIdxCh - 1)] : -1;
+      };
+    };
+    TileStage<TR, D, kNT, true> stg;
+    auto load_tile = [&](int tile) {
+      if (tile < nwt)
+        stg.load(wkbase, wvbase, wst, key_of(tile), [=](int j) { return ring > 0 ? j % ring : j; });
+      else
+        stg.load(kbase, vbase, a.ks_t, key_of(tile));
+    };
+    refill(0);
+    __syncthreads();
+    load_tile(0);
+    const int ntiles = nwt + ngt;
+    // stage the current tile, prefetch the next one; returns whether any entry
+    // of the staged tile is a key
+    auto stage = [&](int it) -> int {
+      __syncthreads();
+      stg.store(sm, kj);
+      const int any = __syncthreads_or(tid < kTK && stg.jk >= 0);
+      if (it + 1 < ntiles) {
+        const int e1 = (it + 1 - nwt) * kTK;  // first list entry of the next tile
+        if (e1 > 0 && (e1 & (kIdxCh - 1)) == 0) {
+          refill(e1);  // the previous chunk's last reader was load(it), before the barrier above
+          __syncthreads();
+        }
+        load_tile(it + 1);
+      }
+      return any;
+    };
+    // The two branches run as two loops (one live output state; separate loops
+    // keep the register pressure of one attention step each).
+    for (int it = 0; it < nwt; ++it) {
+      if (stage(it)) attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, true, window_valid);
+    }
+    window_share();
+    for (int it = nwt; it < ntiles; ++it) {
+      if (stage(it)) attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, tile_needs_mask(kj, pmin), causal_valid);
+    }
   }
 #pragma unroll
   for (int x = 0; x < kRTW; ++x) {
