@@ -229,11 +229,13 @@ __global__ __launch_bounds__(kNW * 64, kWPE) void prefill_fwd_kernel(PrefillArgs
 // One staged tile for the streaming score sweep: per key, the sum of P over
 // the wave's RTW row tiles, written to wred[key] (lanes of quad 0).
 // kfrag(ct, c): K fragment of key sub-tile ct, k-step c; keys(e): key index
-// of tile entry e (-1: invalid).
+// of tile entry e (-1: invalid).  Row tile x holds queries 16 (x % 4) .. of
+// the block, so the position of the lane's row r is pos0 + 16 (x % 4) + r
+// (padding rows have nl = -inf and add exactly 0 whatever the mask says).
 template <typename TR, int D, int RTW, bool MASK, class KFrag, class Keys>
 __device__ __forceinline__ void block_score_tile(const typename TR::frag (&qf)[RTW][D / 32],
-                                                 const float (&nl)[RTW][4], const int (&rowpos)[RTW][4],
-                                                 KFrag kfrag, Keys keys, float sl2, float* wred) {
+                                                 const float (&nl)[RTW][4], int pos0, KFrag kfrag, Keys keys,
+                                                 float sl2, float* wred) {
   constexpr int KC = D / 32;
   const int lane = threadIdx.x & 63, col = lane & 15, quad = lane >> 4;
 #pragma unroll
@@ -252,7 +254,7 @@ __device__ __forceinline__ void block_score_tile(const typename TR::frag (&qf)[R
       for (int r = 0; r < 4; ++r) {
         const float p = fast_exp2(fmaf(s[r], sl2, nl[x][r]));
         if constexpr (MASK)
-          pr[r] += (j >= 0 && j <= rowpos[x][r]) ? p : 0.f;
+          pr[r] += (j >= 0 && j <= pos0 + 16 * (x & 3) + r) ? p : 0.f;
         else
           pr[r] += p;
       }
@@ -317,12 +319,13 @@ __device__ __forceinline__ void score_tile(const typename TR::frag (&qf)[RTW][D 
 // later passes add with a no-return atomic so that no load waits inside the
 // ring.  Otherwise: global -> registers -> one LDS tile.
 template <typename TR, int D, int kNW, int kRTW, bool DMA>
-__global__ __launch_bounds__(kNW * 64, 2) void prefill_block_scores_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kNW * 64, DMA ? 2 : 1) void prefill_block_scores_kernel(PrefillArgs a) {
   constexpr int kNT = kNW * 64;
   using ST = typename TR::storage;
   using L = TileLayout<TR, D>;
   constexpr int KC = D / 32;
   static_assert(!DMA || (TR::kBytes == 2 && D == 128), "DMA staging is for bf16, head_dim 128");
+  static_assert(kRTW % 4 == 0, "a wave's row tiles cover whole groups of the block's 64 queries");
   __shared__ __align__(16) unsigned char sm[DMA ? kDmaStages * DmaTile::kHalf : L::kKBytes];
   __shared__ int kj[DMA ? 1 : kTK];
   __shared__ float red[DMA ? 2 : 1][kNW * kTK];
@@ -346,7 +349,6 @@ __global__ __launch_bounds__(kNW * 64, 2) void prefill_block_scores_kernel(Prefi
   for (int ps = 0; ps < npass; ++ps) {
     typename TR::frag qf[kRTW][KC];
     float nl[kRTW][4];
-    int rowpos[kRTW][4];
     int pmin = 0x7fffffff;
 #pragma unroll
     for (int x = 0; x < kRTW; ++x) {
@@ -363,13 +365,13 @@ __global__ __launch_bounds__(kNW * 64, 2) void prefill_block_scores_kernel(Prefi
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + qoff + 4 * quad + r;
         const bool ok = rt < RT && i < a.Tq;
-        rowpos[x][r] = ok ? a.Tkv - a.Tq + i : -1;
         const float l2 = l2row[min(i, a.Tq - 1)];
         nl[x][r] = ok ? -l2 : kNegInf;
-        pmin = ok ? min(pmin, rowpos[x][r]) : pmin;
+        pmin = ok ? min(pmin, a.Tkv - a.Tq + i) : pmin;
       }
     }
     pmin = wave_min_int(pmin);
+    const int pos0 = a.Tkv - a.Tq + i0 + 4 * quad;  // row r of row tile x: pos0 + 16 (x % 4) + r
     // tile t's key sums (red buffer rb) -> S (threads 0..63)
     auto flush = [&](int t, int rb) {
       const int j = t * kTK + tid;
@@ -418,9 +420,9 @@ __global__ __launch_bounds__(kNW * 64, 2) void prefill_block_scores_kernel(Prefi
         auto keys = [&](int e) { return j0 + e < Tkv ? j0 + e : -1; };
         float* wred = red[it & 1] + wave * kTK;
         if ((it + 1) * kTK - 1 > pmin)
-          block_score_tile<TR, D, kRTW, true>(qf, nl, rowpos, kfrag, keys, a.sl2, wred);
+          block_score_tile<TR, D, kRTW, true>(qf, nl, pos0, kfrag, keys, a.sl2, wred);
         else
-          block_score_tile<TR, D, kRTW, false>(qf, nl, rowpos, kfrag, keys, a.sl2, wred);
+          block_score_tile<TR, D, kRTW, false>(qf, nl, pos0, kfrag, keys, a.sl2, wred);
         cur = cur == kDmaStages - 1 ? 0 : cur + 1;
       }
       __syncthreads();
@@ -440,9 +442,9 @@ __global__ __launch_bounds__(kNW * 64, 2) void prefill_block_scores_kernel(Prefi
           stg.load(kbase, kbase, a.ks_t, [=](int t) { return t0 + t < Tkv ? t0 + t : -1; });
         }
         if (tile_needs_mask(kj, pmin))
-          block_score_tile<TR, D, kRTW, true>(qf, nl, rowpos, kfrag, keys, a.sl2, red[0] + wave * kTK);
+          block_score_tile<TR, D, kRTW, true>(qf, nl, pos0, kfrag, keys, a.sl2, red[0] + wave * kTK);
         else
-          block_score_tile<TR, D, kRTW, false>(qf, nl, rowpos, kfrag, keys, a.sl2, red[0] + wave * kTK);
+          block_score_tile<TR, D, kRTW, false>(qf, nl, pos0, kfrag, keys, a.sl2, red[0] + wave * kTK);
       }
       __syncthreads();
       if (tid < kTK) flush(nkt - 1, 0);
