@@ -573,6 +573,13 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
   __shared__ __align__(16) unsigned char sm[L::kBytes];
   __shared__ int kj[kTK];
   __shared__ int idx_stage[kIdxCh];
+  // the window branch's gated share of each output row, kept in LDS until
+  // the global branch is done (when it fits beside the tile; otherwise in
+  // the output itself); rows of SP elements (pitch D + 8: conflict-free)
+  constexpr int SP = D + 8;
+  constexpr size_t kStash = (size_t)kNW * kRTW * 16 * SP * sizeof(ST);
+  constexpr bool kLdsStash = L::kBytes + kStash + (kTK + kIdxCh) * sizeof(int) <= 160 * 1024;
+  __shared__ __align__(16) ST wstash[kLdsStash ? kNW * kRTW * 16 * SP : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, quad = lane >> 4;
 
   // the row chunks of one block share their gathered rows: keep them on one
@@ -623,33 +630,60 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
 
   RowState<kRTW, D> st;
   st.reset();
+  // the sigmoid gate of each accumulator row 4 * quad + r of row tile x
+  // (clamped indices, so all the loads are in flight together)
+  auto load_gates = [&](float (&gsig)[kRTW][4]) {
+    float w[kRTW][4];
+#pragma unroll
+    for (int x = 0; x < kRTW; ++x) {
+      const int rt = rc * (kNW * kRTW) + wave * kRTW + x;
+      const int hl = min(rt / 4, a.G - 1), qoff = 16 * (rt % 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = min(i0 + qoff + 4 * quad + r, a.Tq - 1);
+        w[x][r] = a.gate.p[(int64_t)b * a.gate.sb + (int64_t)i * a.gate.st + g * a.G + hl];
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < kRTW; ++x)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gsig[x][r] = 1.f / (1.f + expf(-w[x][r]));
+  };
   // output row (b, i, head) of accumulator row 4 * quad + r of row tile x, or
-  // nullptr for padding rows; *gate_out = that row's sigmoid gate
-  auto orow_of = [&](int x, int r, float* gate_out) -> ST* {
+  // nullptr for padding rows
+  auto orow_of = [&](int x, int r) -> ST* {
     const int rt = rc * (kNW * kRTW) + wave * kRTW + x;
     const int hl = rt / 4, qoff = 16 * (rt % 4);
     const int i = i0 + qoff + 4 * quad + r;
     if (!tile_ok[x] || i >= a.Tq) return nullptr;
-    const float w = a.gate.p[(int64_t)b * a.gate.sb + (int64_t)i * a.gate.st + g * a.G + hl];
-    *gate_out = 1.f / (1.f + expf(-w));
     return (ST*)a.out + (((int64_t)b * a.Tq + i) * a.Hq + g * a.G + hl) * D;
   };
-  // window branch done: its share (1 - g) * o_window goes to the output now
-  // (read back by the same lanes in the epilogue); restart for the global
-  // branch (two live output states would not fit the registers)
+  // where the window share of that row lives (same lane writes and reads it)
+  auto stash_of = [&](int x, int r, ST* orow) -> ST* {
+    if constexpr (kLdsStash)
+      return wstash + ((wave * kRTW + x) * 16 + 4 * quad + r) * SP;
+    else
+      return orow;
+  };
+  // window branch done: its share (1 - g) * o_window is stashed (rounded to
+  // the output type, read back by the same lane in the epilogue); restart
+  // for the global branch (two live output states would not fit the
+  // registers)
   auto window_share = [&]() {
+    float gsig[kRTW][4];
+    load_gates(gsig);
 #pragma unroll
     for (int x = 0; x < kRTW; ++x) {
       const float lt = wave_sum16x4(st.l[x]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float lr = __shfl(lt, 4 * quad + r);
-        float gr = 0.f;
-        ST* orow = orow_of(x, r, &gr);
-        const float sc = lr > 0.f ? (1.f - gr) / lr : 0.f;
+        const float sc = lr > 0.f ? (1.f - gsig[x][r]) / lr : 0.f;
+        ST* orow = orow_of(x, r);
         if (orow) {
+          ST* w = stash_of(x, r, orow);
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) orow[16 * dt + col] = TR::from_float(st.o[x][dt][r] * sc);
+          for (int dt = 0; dt < DT; ++dt) w[16 * dt + col] = TR::from_float(st.o[x][dt][r] * sc);
         }
       }
     }
@@ -725,19 +759,21 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
       if (stage(it)) attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, tile_needs_mask(kj, pmin), causal_valid);
     }
   }
+  float gsig[kRTW][4];
+  load_gates(gsig);
 #pragma unroll
   for (int x = 0; x < kRTW; ++x) {
     const float lt = wave_sum16x4(st.l[x]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float lr = __shfl(lt, 4 * quad + r);
-      float gr = 0.f;
-      ST* orow = orow_of(x, r, &gr);
+      ST* orow = orow_of(x, r);
       if (orow) {
-        const float sc = lr > 0.f ? gr / lr : 0.f;
+        const float sc = lr > 0.f ? gsig[x][r] / lr : 0.f;
+        const ST* w = stash_of(x, r, orow);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          orow[16 * dt + col] = TR::from_float(st.o[x][dt][r] * sc + TR::to_float(orow[16 * dt + col]));
+          orow[16 * dt + col] = TR::from_float(st.o[x][dt][r] * sc + TR::to_float(w[16 * dt + col]));
       }
     }
   }
