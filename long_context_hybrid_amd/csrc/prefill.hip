@@ -729,9 +729,11 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
       else
         stg.load(kbase, vbase, a.ks_t, key_of(tile));
     };
+    // tile 0 is a window tile (nwt >= 1) and needs no index: its loads fly
+    // together with the first index chunk's
+    load_tile(0);
     refill(0);
     __syncthreads();
-    load_tile(0);
     const int ntiles = nwt + ngt;
     // stage the current tile, prefetch the next one; returns whether any entry
     // of the staged tile is a key
