@@ -73,7 +73,7 @@ struct DecodeSmem {
 };
 
 template <typename TR, int D, bool FULL>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, FULL ? 1 : 2) void decode_split_kernel(DecodeArgs a) {
   using ST = typename TR::storage;
   using frag = typename TR::frag;
   using quad_t = typename TR::quad_t;
