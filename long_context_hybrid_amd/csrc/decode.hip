@@ -371,6 +371,8 @@ __global__ __launch_bounds__(D) void sparse_merge_kernel(DecodeArgs a) {
   const int i = unit % a.Tq, bg = unit / a.Tq;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const float* pml = a.part_ml + (int64_t)unit * a.nsplit * a.G * 2;
+  // the head's gate logit, first so that its load overlaps the others
+  const float gw = a.gate.p[(int64_t)b * a.gate.sb + (int64_t)i * a.gate.st + g * a.G + h];
   // this thread's output element of every split, loaded before the weights
   // are known so that both reads are in flight together
   const float* po = a.part_o + (int64_t)unit * a.nsplit * a.G * D + (int64_t)h * D + tid;
@@ -400,7 +402,7 @@ __global__ __launch_bounds__(D) void sparse_merge_kernel(DecodeArgs a) {
       lg += __shfl_xor(lg, off);
       lw += __shfl_xor(lw, off);
     }
-    const float gt = 1.f / (1.f + expf(-a.gate.p[(int64_t)b * a.gate.sb + (int64_t)i * a.gate.st + g * a.G + h]));
+    const float gt = 1.f / (1.f + expf(-gw));
     const float L = win ? lw : lg;
     const float scale = (L > 0.f) ? (win ? (1.f - gt) : gt) / L : 0.f;
     if (in) wts[sp] = w * scale;
@@ -466,12 +468,18 @@ __device__ __forceinline__ void unit_lse2(const float* pml, int nsplit, int G, f
 // as whole 1 KB runs: in run xi of a group, lane l holds heads 4*(l % Q) ..
 // +3 of key (64/Q)*xi + l/Q; a DPP sum over the key's Q lanes gives its S.
 // (The scratch holds nchunk * kScoreChunk keys per unit, so every run is in
-// it; keys past kv_len are read but not stored.)
+// it; keys past kv_len are read but not stored.)  The logit loads are issued
+// before the unit's LSE is formed (they do not depend on it).
 template <int Q>
-__device__ __forceinline__ void score_runs(const FinishArgs& f, int unit, int key0, const float* lse_s) {
+__device__ __forceinline__ void score_runs(const FinishArgs& f, int unit, int key0, float* lse_s) {
   constexpr int NR = 4 * Q;   // 1 KB runs
   constexpr int KPR = 64 / Q; // keys per run
   const int lane = threadIdx.x & 63, hg = lane % Q;
+  const float* lg = f.logits + (int64_t)unit * f.lus + (int64_t)key0 * (4 * Q);
+  float4 x[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) x[r] = *reinterpret_cast<const float4*>(lg + r * 256 + 4 * lane);
+  unit_lse2(f.part_ml + (int64_t)unit * f.nsplit * f.G * 2, f.nsplit, f.G, lse_s);
   float L[4];
   bool hv[4];
 #pragma unroll
@@ -479,10 +487,6 @@ __device__ __forceinline__ void score_runs(const FinishArgs& f, int unit, int ke
     hv[e] = 4 * hg + e < f.G;
     L[e] = hv[e] ? lse_s[4 * hg + e] : 0.f;
   }
-  const float* lg = f.logits + (int64_t)unit * f.lus + (int64_t)key0 * (4 * Q);
-  float4 x[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) x[r] = *reinterpret_cast<const float4*>(lg + r * 256 + 4 * lane);
   float* srow = f.scores + (int64_t)unit * f.Tkv;
 #pragma unroll
   for (int grp = 0; grp < 4; ++grp) {
@@ -559,7 +563,6 @@ __global__ __launch_bounds__(256) void decode_full_finish_kernel(FinishArgs f) {
   }
   const int bid = blockIdx.x - nrow;
   const int unit = bid / f.nchunk, c = bid - (bid / f.nchunk) * f.nchunk;
-  unit_lse2(f.part_ml + (int64_t)unit * f.nsplit * f.G * 2, f.nsplit, f.G, lse_s);
   const int key0 = c * kScoreChunk + (tid >> 6) * (kScoreChunk / 4);  // the wave's 256 keys
   if (f.lgp == 4)
     score_runs<1>(f, unit, key0, lse_s);
