@@ -740,7 +740,9 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
     auto stage = [&](int it) -> int {
       __syncthreads();
       stg.store(sm, kj);
-      const int any = __syncthreads_or(tid < kTK && stg.jk >= 0);
+      __syncthreads();
+      // whether any entry of the staged tile is a key (the same in every wave)
+      const int any = __builtin_amdgcn_ballot_w64(kj[lane] >= 0) != 0;
       if (it + 1 < ntiles) {
         const int e1 = (it + 1 - nwt) * kTK;  // first list entry of the next tile
         if (e1 > 0 && (e1 & (kIdxCh - 1)) == 0) {
