@@ -276,6 +276,25 @@ def main():
     print(f"[bench] {args.steps} steps: {ms:.4f} ms/step (wall {1e3 * wall / args.steps:.4f})", file=sys.stderr,
           flush=True)
 
+    # decode: the sparse layers' share of the untraced step, from the same block
+    # without sparse layers (full layer + top-K), timed the same way
+    sparse_b2b_us = None
+    if Tq == 1 and not loop and not hier and qs:
+        def step0():
+            hy.hysparse_hybrid_block(qf, k, v, [], gates, wl.k_top, wl.score_block, wl.window, out_full=out_full,
+                                     lse=lse, scores=scores, idx=idx, workspace=ws)
+
+        for _ in range(args.warmup):
+            step0()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            step0()
+        e1.record()
+        torch.cuda.synchronize()
+        ms0 = e0.elapsed_time(e1) / args.steps
+        sparse_b2b_us = 1e3 * (ms - ms0) / len(qs)
+
     # per-kernel durations: second pass with the library's event trace
     trace = hy.KernelTrace(capacity_kernels=64 * (args.steps + 1))
     trace.begin()
@@ -329,8 +348,14 @@ def main():
         result["roofline_full"] = rf
         result["roofline_sparse"] = rs
         if rs:
-            layer_us = rs["avg_us"] + kernels.get("sparse_merge", {"avg_us": 0.0})["avg_us"]
+            traced_us = rs["avg_us"] + kernels.get("sparse_merge", {"avg_us": 0.0})["avg_us"]
+            # per layer: the untraced share of the step when it was measured
+            # (back to back, launch gaps included), else the two traced kernels
+            layer_us = sparse_b2b_us if sparse_b2b_us else traced_us
             result["sparse_layer"] = {"tokens_per_s": tokens_per_step / (layer_us * 1e-6), "us_per_layer": layer_us,
+                                      "method": "step minus the block without sparse layers, per layer"
+                                      if sparse_b2b_us else "traced split + merge kernels",
+                                      "us_per_layer_traced": traced_us,
                                       "GB_per_s": sb / (layer_us * 1e-6) / 1e9,
                                       "frac_hbm": sb / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "alg_bytes": sb,
                                       "split_kernel_us": rs["avg_us"]}
