@@ -129,6 +129,27 @@ def test_hybrid_prefill_deterministic():
                 assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("name", ["prefill32k_small", "g16_chunk_q70_kv333"])
+def test_hybrid_prefill_head_major_cache_bit_identical(name):
+    """A head-major cache ([B, Hkv, T, D] storage passed as a [B, T, Hkv, D]
+    view) changes only the row addresses the tile loads use: every output
+    must equal the token-major run bit for bit."""
+    wl = PREFILL_CASES[name]
+    say(f"head-major cache {name}")
+    inp = gen.make_inputs(wl)
+    qf, k, v, qs, gates = _dev(inp)
+    khm = k.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    vhm = v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    assert khm.stride(1) == wl.head_dim and torch.equal(khm, k)
+    a = hy.hysparse_hybrid_block(qf, k, v, qs, gates, wl.k_top, wl.score_block, wl.window)
+    b = hy.hysparse_hybrid_block(qf, khm, vhm, qs, gates, wl.k_top, wl.score_block, wl.window)
+    torch.cuda.synchronize()
+    for key in ("out_full", "scores", "idx"):
+        assert torch.equal(a[key], b[key]), key
+    for oa, ob in zip(a["out"], b["out"]):
+        assert torch.equal(oa, ob)
+
+
 def test_hybrid_block_prefill32k_full_size_sampled():
     """The 32K prefill workload at full size; the oracle checks a sample of
     (KV group, score block) units including the first and last blocks."""
