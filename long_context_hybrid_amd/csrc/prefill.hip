@@ -45,7 +45,7 @@ constexpr int kSpShape[2] = {HYS_SP_SHAPE};    // sparse layer (two output state
 constexpr int kFwdNW = kFwdShape[0], kFwdRTW = kFwdShape[1], kFwdWPE = kFwdShape[2];
 constexpr int kScNW = kScShape[0], kScRTW = kScShape[1];
 constexpr int kSpNW = kSpShape[0], kSpRTW = kSpShape[1];
-constexpr int kIdxCh = 1024;                // sparse layer: selected indices staged in LDS per refill
+constexpr int kIdxCh = 2048;                // sparse layer: selected indices staged in LDS per refill
 // Forward sweep, bf16 with head_dim 128: tiles staged by LDS DMA into a ring
 // of kDmaStages stages (the next two tiles in flight while one is used).
 #ifndef HYS_FWD_DMA

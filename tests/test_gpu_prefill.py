@@ -24,6 +24,9 @@ PREFILL_CASES = {
     "f32_sb64_g2": W["tiny"].replace(q_len=200, kv_len=200, n_q_heads=4, n_kv_heads=2, score_block=64,
                                      k_top=40, window=16, n_sparse=1),
     "window_over_ctx": W["prefill32k"].replace(q_len=100, kv_len=100, k_top=500, window=300, n_sparse=1),
+    # more selected keys than one LDS index stage holds (the refill path)
+    "ktop_over_stage": W["prefill32k"].replace(q_len=2600, kv_len=2600, n_q_heads=4, n_kv_heads=1, k_top=2300,
+                                               n_sparse=1),
     # shorter than one 64-key tile: every tile row past the cache is clamped and masked
     "short_ctx_40": W["prefill32k"].replace(q_len=40, kv_len=40, k_top=16, window=8, n_sparse=1),
     # G = 16 with queries after a cached prefix: several score passes, ragged tiles
