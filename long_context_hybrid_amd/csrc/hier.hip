@@ -20,25 +20,61 @@ namespace {
 
 constexpr int kMaxBlocks = 1 << 20;  // pooled blocks per row
 
+// Pooled keys: one workgroup per (b, block m, g); 16-byte loads, a group of
+// LPR lanes per key row, RG rows in flight per pass (four passes' loads at
+// once), the RG partial sums added through LDS.
 template <typename TR, int D>
-__global__ __launch_bounds__(D) void pool_keys_kernel(const void* k, int64_t ks_b, int64_t ks_t, int64_t ks_h, int Tkv,
-                                                      int Hkv, int M, int block, float* kbar) {
+__global__ __launch_bounds__(256) void pool_keys_kernel(const void* k, int64_t ks_b, int64_t ks_t, int64_t ks_h, int Tkv,
+                                                        int Hkv, int M, int block, float* kbar) {
+  constexpr int EPC = 16 / TR::kBytes;  // elements per 16-byte load
+  constexpr int LPR = D / EPC;          // lanes per key row
+  constexpr int RG = 256 / LPR;         // key rows per pass
+  __shared__ float part[RG][D];
   const int id = blockIdx.x;  // (b, m, g)
   const int g = id % Hkv, m = (id / Hkv) % M, b = id / (Hkv * M);
-  const int d = threadIdx.x;
+  const int t = threadIdx.x, rg = t / LPR, ln = t - (t / LPR) * LPR;
   const int j0 = m * block, j1 = min(j0 + block, Tkv);
-  const typename TR::storage* base = (const typename TR::storage*)k + (int64_t)b * ks_b + (int64_t)g * ks_h + d;
-  float s = 0.f;
-#pragma unroll 8
-  for (int j = j0; j < j1; ++j) s += TR::to_float(base[(int64_t)j * ks_t]);
-  kbar[(((int64_t)b * M + m) * Hkv + g) * D + d] = s / (float)(j1 - j0);
+  const typename TR::storage* base =
+      (const typename TR::storage*)k + (int64_t)b * ks_b + (int64_t)g * ks_h + ln * EPC;
+  float acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+  for (int j = j0 + rg; j < j1; j += 4 * RG) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int jj = j + u * RG;
+      v[u] = jj < j1 ? *reinterpret_cast<const u32x4_t*>(base + (int64_t)jj * ks_t) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        if constexpr (TR::kBytes == 2)
+          acc[e] += bf16_to_f32((uint16_t)((e & 1) ? (v[u][e >> 1] >> 16) : (v[u][e >> 1] & 0xFFFFu)));
+        else
+          acc[e] += __uint_as_float(v[u][e]);
+      }
+  }
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) part[rg][ln * EPC + e] = acc[e];
+  __syncthreads();
+  for (int d = t; d < D; d += 256) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) s += part[r][d];
+    kbar[(((int64_t)b * M + m) * Hkv + g) * D + d] = s / (float)(j1 - j0);
+  }
 }
 
 // Block logits: one workgroup per (b, g, run of 64 pooled blocks); thread
 // (block m, head h) computes logit2[b, g, h, m] = tau * log2(e) * q_h . kbar_m.
+// The staging loads have fixed counts, so they are in flight together.
 template <typename TR, int D>
 __global__ __launch_bounds__(256) void block_logits_kernel(const void* q, int64_t qs_b, int64_t qs_h, const float* kbar,
                                                            int Hkv, int G, int M, float sl2, float* logit2) {
+  constexpr int QN = 16 * D / 256;  // G <= 16 query rows
+  constexpr int KN = 64 * D / 256;  // 64 pooled rows
   __shared__ float qs[16 * D];
   __shared__ float ks[64 * (D + 1)];
   const int nchunk = (M + 63) / 64;
@@ -46,13 +82,24 @@ __global__ __launch_bounds__(256) void block_logits_kernel(const void* q, int64_
   const int b = bg / Hkv, g = bg - (bg / Hkv) * Hkv;
   const int t = threadIdx.x;
   const int m0 = ch * 64;
-  for (int x = t; x < G * D; x += 256) {
-    const int h = x / D, d = x - h * D;
-    qs[x] = TR::to_float(((const typename TR::storage*)q)[(int64_t)b * qs_b + (int64_t)(g * G + h) * qs_h + d]);
+  float qv[QN], kv[KN];
+#pragma unroll
+  for (int r = 0; r < QN; ++r) {
+    const int x = t + 256 * r, h = x / D, d = x - (x / D) * D;
+    qv[r] = x < G * D ? TR::to_float(((const typename TR::storage*)q)[(int64_t)b * qs_b + (int64_t)(g * G + h) * qs_h + d])
+                      : 0.f;
   }
-  for (int x = t; x < 64 * D; x += 256) {
-    const int mm = x / D, d = x - mm * D;
-    ks[mm * (D + 1) + d] = (m0 + mm < M) ? kbar[(((int64_t)b * M + m0 + mm) * Hkv + g) * D + d] : 0.f;
+#pragma unroll
+  for (int r = 0; r < KN; ++r) {
+    const int x = t + 256 * r, mm = x / D, d = x - (x / D) * D;
+    kv[r] = (m0 + mm < M) ? kbar[(((int64_t)b * M + m0 + mm) * Hkv + g) * D + d] : 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r < QN; ++r) qs[t + 256 * r] = qv[r];
+#pragma unroll
+  for (int r = 0; r < KN; ++r) {
+    const int x = t + 256 * r, mm = x / D, d = x - (x / D) * D;
+    ks[mm * (D + 1) + d] = kv[r];
   }
   __syncthreads();
   for (int x = t; x < 64 * G; x += 256) {
@@ -64,35 +111,62 @@ __global__ __launch_bounds__(256) void block_logits_kernel(const void* q, int64_
 }
 
 // Block scores: one workgroup per (b, g): per head the softmax over the
-// pooled blocks (16 threads per head, fixed order), summed over heads.
+// pooled blocks (16 threads per head, an online (max, sum) over batches of
+// 16 loads in flight, folded in a fixed order), summed over heads.
 __global__ __launch_bounds__(256) void block_softmax_kernel(const float* logit2, int G, int M, float* bscore) {
   __shared__ float lse[16];
   const int bg = blockIdx.x, t = threadIdx.x;
   const int h = t >> 4, s = t & 15;
   const float* lg = logit2 + (int64_t)bg * G * M;
-  float mx = kNegInf;
-  if (h < G)
-    for (int m = s; m < M; m += 16) mx = fmaxf(mx, lg[(int64_t)h * M + m]);
+  float mx = kNegInf, sum = 0.f;
+  for (int m0 = s; m0 < M; m0 += 16 * 16) {
+    float v[16];
 #pragma unroll
-  for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
-  float sum = 0.f;
-  if (h < G)
-    for (int m = s; m < M; m += 16) sum += exp2f(lg[(int64_t)h * M + m] - mx);
+    for (int u = 0; u < 16; ++u) {
+      const int m = m0 + 16 * u;
+      v[u] = (h < G && m < M) ? lg[(int64_t)h * M + m] : kNegInf;
+    }
+    float bm = v[0];
 #pragma unroll
-  for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
+    for (int u = 1; u < 16; ++u) bm = fmaxf(bm, v[u]);
+    const float nm = fmaxf(mx, bm);
+    if (nm != kNegInf) {
+      float add = 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) add += exp2f(v[u] - nm);
+      sum = sum * exp2f(mx - nm) + add;
+      mx = nm;
+    }
+  }
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) {
+    const float om = __shfl_xor(mx, off, 16), os = __shfl_xor(sum, off, 16);
+    const float nm = fmaxf(mx, om);
+    if (nm != kNegInf) {
+      sum = sum * exp2f(mx - nm) + os * exp2f(om - nm);
+      mx = nm;
+    }
+  }
   if (s == 0 && h < G) lse[h] = mx + log2f(sum);
   __syncthreads();
   for (int m = t; m < M; m += 256) {
+    float e[16];
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh) e[hh] = hh < G ? lg[(int64_t)hh * M + m] : 0.f;
     float v = 0.f;
-    for (int hh = 0; hh < G; ++hh) v += exp2f(lg[(int64_t)hh * M + m] - lse[hh]);
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh)
+      if (hh < G) v += exp2f(e[hh] - lse[hh]);
     bscore[(int64_t)bg * M + m] = v;
   }
 }
 
 // cand[row][c] = S[row][token(c)], token(c) = blk[c / block] * block + c % block,
-// for the kept blocks in ascending order; valid[row] = number of candidates.
+// for the kept blocks in ascending order; valid[row] = number of candidates
+// (the kept list is ascending with -1 padding at its end).
 __global__ __launch_bounds__(256) void gather_candidates_kernel(const float* S, int Tkv, const int32_t* blk, int n_keep,
                                                                 int block, float* cand, int32_t* valid) {
+  __shared__ int wsum[4];
   const int row = blockIdx.y;
   const int64_t ncand = (int64_t)n_keep * block;
   const int32_t* br = blk + (int64_t)row * n_keep;
@@ -102,14 +176,17 @@ __global__ __launch_bounds__(256) void gather_candidates_kernel(const float* S, 
     const int64_t j = (int64_t)m * block + o;
     cand[(int64_t)row * ncand + c] = (m >= 0 && j < Tkv) ? S[(int64_t)row * Tkv + j] : 0.f;
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
+  if (blockIdx.x == 0) {
     int nv = 0;
-    for (int bi = 0; bi < n_keep; ++bi) {
+    for (int bi = threadIdx.x; bi < n_keep; bi += 256) {
       const int m = br[bi];
-      if (m < 0) break;
-      nv += min(block, Tkv - m * block);
+      nv += m < 0 ? 0 : min(block, Tkv - m * block);
     }
-    valid[row] = nv;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) nv += __shfl_xor(nv, off);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = nv;
+    __syncthreads();
+    if (threadIdx.x == 0) valid[row] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
   }
 }
 
@@ -197,8 +274,8 @@ hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const
   HIER_DT({
     {
       TraceScope ts(st, "hier_pool_keys");
-      pool_keys_kernel<TR, DD><<<g.B * M * g.Hkv, DD, 0, st>>>(k, g.ks_b, g.ks_t, g.ks_h, g.Tkv, g.Hkv, M, block,
-                                                               w.kbar);
+      pool_keys_kernel<TR, DD><<<g.B * M * g.Hkv, 256, 0, st>>>(k, g.ks_b, g.ks_t, g.ks_h, g.Tkv, g.Hkv, M, block,
+                                                                w.kbar);
     }
     {
       TraceScope ts(st, "hier_block_logits");
