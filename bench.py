@@ -250,11 +250,17 @@ def main():
         ws_h = torch.empty(hy.hysparse_hier_workspace_bytes(desc, HB, HKEEP, wl.k_top), dtype=torch.uint8, device=dev)
         bsc = torch.empty((B, Hkv, -(-Tkv // HB)), dtype=torch.float32, device=dev)
         blk = torch.empty((B, Hkv, HKEEP), dtype=torch.int32, device=dev)
+        # pooled keys kept beside the cache: pooled once here; a decode step
+        # refreshes only the block that holds the newest token
+        kbar = torch.empty((B, -(-Tkv // HB), Hkv, D), dtype=torch.float32, device=dev)
+        hy.hysparse_hier_pool(k, HB, kbar)
+        m_last = (Tkv - 1) // HB
 
         def step():
             hy.hysparse_full_attn_scores(qf, k, v, 1, out=out_full, lse=lse, scores=scores, workspace=ws_full)
-            hy.hysparse_hier_select(qf, k, scores, HB, HKEEP, wl.k_top, idx=idx, block_scores=bsc, blocks=blk,
-                                    workspace=ws_h)
+            hy.hysparse_hier_pool(k, HB, kbar, m_last, m_last + 1)
+            hy.hysparse_hier_select_pooled(qf, k, kbar, scores, HB, HKEEP, wl.k_top, idx=idx, block_scores=bsc,
+                                           blocks=blk, workspace=ws_h)
             for l in range(len(qs)):
                 hy.hysparse_sparse_attn(qs[l], k, v, idx, wl.k_top, 1, wl.window, gates[l], out=outs[l],
                                         workspace=ws_sp)

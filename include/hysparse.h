@@ -237,6 +237,41 @@ hys_status hysparse_hier_select(const hys_attn_desc* desc, const void* q, const 
                                 size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Pooled keys kept beside the cache, for hierarchical selection in a decode
+ * loop.  The pooled key of a complete block does not change as the cache
+ * grows (intelliparadigm article section 3.1: only the full layers update the
+ * cache), so a caller pools every block once and, after each
+ * hysparse_append_kv, refreshes only the blocks the new tokens touch.
+ *
+ * hysparse_hier_pool writes, for blocks m in [m_begin, m_end),
+ *   kbar[b, m, g, :] = mean of keys [m * block, min((m + 1) * block, kv_len))
+ * of KV group g, in fp32.  desc's kv fields describe the cache as for
+ * hysparse_append_kv (kv_len: the tokens it holds now); its query fields are
+ * not read.
+ *
+ *   k             the cache's keys, 16-byte aligned, read.
+ *   kbar          float32 [B, kbar_blocks, Hkv, D] (batch stride kbar_blocks
+ *                 * Hkv * D floats), 16-byte aligned, caller-owned, written
+ *                 for the given blocks only.
+ *   kbar_blocks   blocks held per batch entry: >= ceil(kv_len / block) (the
+ *                 cache capacity in blocks, so the array outlives growth).
+ *   Errors: block < 1, m_begin < 0, m_end < m_begin, m_end > ceil(kv_len /
+ *   block) or kbar_blocks too small -> HYS_ERR_BAD_SHAPE; no workspace.
+ *
+ * hysparse_hier_select_pooled is hysparse_hier_select with step 1 replaced by
+ * the given pooled keys (all ceil(kv_len / block) blocks valid); its other
+ * arguments, outputs and workspace are those of hysparse_hier_select, and
+ * with kbar from hysparse_hier_pool over every block its outputs equal
+ * hysparse_hier_select's bit for bit.
+ */
+hys_status hysparse_hier_pool(const hys_attn_desc* desc, const void* k, int32_t block, int32_t m_begin, int32_t m_end,
+                              float* kbar, int32_t kbar_blocks, hipStream_t stream);
+hys_status hysparse_hier_select_pooled(const hys_attn_desc* desc, const void* q, const float* kbar,
+                                       int32_t kbar_blocks, const float* scores, int32_t block, int32_t n_keep,
+                                       int32_t k_top, float* block_scores, int32_t* blocks, int32_t* idx, void* ws,
+                                       size_t ws_bytes, hipStream_t stream);
+
+/*
  * KV-cache append (intelliparadigm article section 3.1: only the full layers
  * update the cache; the sparse layers read it).  Copies n_new new rows of keys
  * and values, each [B, n_new, Hkv, D] contiguous in desc.dtype, into the cache

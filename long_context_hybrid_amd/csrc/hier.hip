@@ -20,18 +20,20 @@ namespace {
 
 constexpr int kMaxBlocks = 1 << 20;  // pooled blocks per row
 
-// Pooled keys: one workgroup per (b, block m, g); 16-byte loads, a group of
-// LPR lanes per key row, RG rows in flight per pass (four passes' loads at
-// once), the RG partial sums added through LDS.
+// Pooled keys of blocks [m_begin, m_begin + nm): one workgroup per (b, block
+// m, g); 16-byte loads, a group of LPR lanes per key row, RG rows in flight
+// per pass (four passes' loads at once), the RG partial sums added through
+// LDS.  kbar[b * kbs + (m * Hkv + g) * D + d] (kbs: floats per batch entry).
 template <typename TR, int D>
 __global__ __launch_bounds__(256) void pool_keys_kernel(const void* k, int64_t ks_b, int64_t ks_t, int64_t ks_h, int Tkv,
-                                                        int Hkv, int M, int block, float* kbar) {
+                                                        int Hkv, int m_begin, int nm, int block, float* kbar,
+                                                        int64_t kbs) {
   constexpr int EPC = 16 / TR::kBytes;  // elements per 16-byte load
   constexpr int LPR = D / EPC;          // lanes per key row
   constexpr int RG = 256 / LPR;         // key rows per pass
   __shared__ float part[RG][D];
-  const int id = blockIdx.x;  // (b, m, g)
-  const int g = id % Hkv, m = (id / Hkv) % M, b = id / (Hkv * M);
+  const int id = blockIdx.x;  // (b, m - m_begin, g)
+  const int g = id % Hkv, m = m_begin + (id / Hkv) % nm, b = id / (Hkv * nm);
   const int t = threadIdx.x, rg = t / LPR, ln = t - (t / LPR) * LPR;
   const int j0 = m * block, j1 = min(j0 + block, Tkv);
   const typename TR::storage* base =
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const void* k, int64_t k
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < RG; ++r) s += part[r][d];
-    kbar[(((int64_t)b * M + m) * Hkv + g) * D + d] = s / (float)(j1 - j0);
+    kbar[(int64_t)b * kbs + ((int64_t)m * Hkv + g) * D + d] = s / (float)(j1 - j0);
   }
 }
 
@@ -72,7 +74,8 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const void* k, int64_t k
 // The staging loads have fixed counts, so they are in flight together.
 template <typename TR, int D>
 __global__ __launch_bounds__(256) void block_logits_kernel(const void* q, int64_t qs_b, int64_t qs_h, const float* kbar,
-                                                           int Hkv, int G, int M, float sl2, float* logit2) {
+                                                           int64_t kbs, int Hkv, int G, int M, float sl2,
+                                                           float* logit2) {
   constexpr int QN = 16 * D / 256;  // G <= 16 query rows
   constexpr int KN = 64 * D / 256;  // 64 pooled rows
   __shared__ float qs[16 * D];
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(256) void block_logits_kernel(const void* q, int64_
 #pragma unroll
   for (int r = 0; r < KN; ++r) {
     const int x = t + 256 * r, mm = x / D, d = x - (x / D) * D;
-    kv[r] = (m0 + mm < M) ? kbar[(((int64_t)b * M + m0 + mm) * Hkv + g) * D + d] : 0.f;
+    kv[r] = (m0 + mm < M) ? kbar[(int64_t)b * kbs + ((int64_t)(m0 + mm) * Hkv + g) * D + d] : 0.f;
   }
 #pragma unroll
   for (int r = 0; r < QN; ++r) qs[t + 256 * r] = qv[r];
@@ -255,15 +258,6 @@ size_t hier_ws_bytes(const Geom& g, int block, int n_keep, int k_top) {
          hier_topk_ws(g, block, n_keep, k_top);
 }
 
-hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const float* scores, int block, int n_keep,
-                              int k_top, float* bscore_out, int32_t* blk_out, int32_t* idx, void* ws, hipStream_t st) {
-  const int M = (g.Tkv + block - 1) / block;
-  const int rows = g.B * g.Hkv;
-  HierWs w = carve(g, block, n_keep, k_top, ws);
-  float* bscore = bscore_out ? bscore_out : w.bscore;
-  int32_t* blk = blk_out ? blk_out : w.blk;
-  const float sl2 = g.scale * kLog2e;
-  hipError_t e;
 #define HIER_DT(...)                                                     \
   do {                                                                   \
     if (g.dtype == 1 && g.D == 128) { using TR = BF16; constexpr int DD = 128; __VA_ARGS__; } \
@@ -271,23 +265,49 @@ hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const
     else if (g.D == 128) { using TR = F32; constexpr int DD = 128; __VA_ARGS__; }            \
     else { using TR = F32; constexpr int DD = 64; __VA_ARGS__; }                              \
   } while (0)
+
+hipError_t launch_hier_pool(const Geom& g, const void* k, int block, int m_begin, int m_end, float* kbar,
+                            int64_t kbar_blocks, hipStream_t st) {
+  if (m_end <= m_begin) return hipSuccess;
+  const int nm = m_end - m_begin;
+  const int64_t kbs = kbar_blocks * g.Hkv * g.D;
+  HIER_DT({
+    TraceScope ts(st, "hier_pool_keys");
+    pool_keys_kernel<TR, DD><<<g.B * nm * g.Hkv, 256, 0, st>>>(k, g.ks_b, g.ks_t, g.ks_h, g.Tkv, g.Hkv, m_begin, nm,
+                                                               block, kbar, kbs);
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const float* kbar_in, int64_t kbar_blocks,
+                              const float* scores, int block, int n_keep, int k_top, float* bscore_out,
+                              int32_t* blk_out, int32_t* idx, void* ws, hipStream_t st) {
+  const int M = (g.Tkv + block - 1) / block;
+  const int rows = g.B * g.Hkv;
+  HierWs w = carve(g, block, n_keep, k_top, ws);
+  float* bscore = bscore_out ? bscore_out : w.bscore;
+  int32_t* blk = blk_out ? blk_out : w.blk;
+  const float sl2 = g.scale * kLog2e;
+  hipError_t e;
+  // pooled keys: the caller's, or all blocks pooled into the workspace now
+  const float* kbar = kbar_in;
+  int64_t kbs = kbar_blocks * g.Hkv * g.D;
+  if (!kbar) {
+    if ((e = launch_hier_pool(g, k, block, 0, M, w.kbar, M, st)) != hipSuccess) return e;
+    kbar = w.kbar;
+    kbs = (int64_t)M * g.Hkv * g.D;
+  }
   HIER_DT({
     {
-      TraceScope ts(st, "hier_pool_keys");
-      pool_keys_kernel<TR, DD><<<g.B * M * g.Hkv, 256, 0, st>>>(k, g.ks_b, g.ks_t, g.ks_h, g.Tkv, g.Hkv, M, block,
-                                                                w.kbar);
-    }
-    {
       TraceScope ts(st, "hier_block_logits");
-      block_logits_kernel<TR, DD><<<rows * ((M + 63) / 64), 256, 0, st>>>(q, g.qs_b, g.qs_h, w.kbar, g.Hkv, g.G, M,
-                                                                            sl2, w.logit2);
+      block_logits_kernel<TR, DD><<<rows * ((M + 63) / 64), 256, 0, st>>>(q, g.qs_b, g.qs_h, kbar, kbs, g.Hkv, g.G,
+                                                                            M, sl2, w.logit2);
     }
     {
       TraceScope ts(st, "hier_block_softmax");
       block_softmax_kernel<<<rows, 256, 0, st>>>(w.logit2, g.G, M, bscore);
     }
   });
-#undef HIER_DT
   ValidLen all{nullptr, M, 0, 1, 1, 1, 1};
   if ((e = launch_topk(bscore, rows, M, M, all, n_keep, blk, w.topk_ws, st)) != hipSuccess) return e;
   const int64_t ncand = (int64_t)n_keep * block;
@@ -308,5 +328,7 @@ hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const
   }
   return hipGetLastError();
 }
+
+#undef HIER_DT
 
 }  // namespace hys

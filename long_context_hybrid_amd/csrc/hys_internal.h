@@ -126,7 +126,13 @@ size_t hier_ws_bytes(const Geom& g, int block, int n_keep, int k_top);
 // KV-cache append (cache.hip)
 hipError_t launch_append_kv(const Geom& g, const void* k_new, const void* v_new, int n_new, int pos, void* k_cache,
                             void* v_cache, hipStream_t st);
-hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const float* scores, int block, int n_keep,
-                              int k_top, float* bscore_out, int32_t* blk_out, int32_t* idx, void* ws, hipStream_t st);
+// kbar_in: pooled keys [B, kbar_blocks, Hkv, D] fp32 from hysparse_hier_pool,
+// or nullptr (all blocks pooled from k into the workspace first)
+hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const float* kbar_in, int64_t kbar_blocks,
+                              const float* scores, int block, int n_keep, int k_top, float* bscore_out,
+                              int32_t* blk_out, int32_t* idx, void* ws, hipStream_t st);
+// pooled keys of blocks [m_begin, m_end) of k into kbar [B, kbar_blocks, Hkv, D] fp32
+hipError_t launch_hier_pool(const Geom& g, const void* k, int block, int m_begin, int m_end, float* kbar,
+                            int64_t kbar_blocks, hipStream_t st);
 
 }  // namespace hys

@@ -338,7 +338,50 @@ hys_status hysparse_hier_select(const hys_attn_desc* desc, const void* q, const 
   if (block_scores && !aligned(block_scores, 4)) return fail(HYS_ERR_ALIGN, "block_scores is not 4-byte aligned");
   if (blocks && !aligned(blocks, 4)) return fail(HYS_ERR_ALIGN, "blocks is not 4-byte aligned");
   if ((s = check_ws(ws, ws_bytes, hys::hier_ws_bytes(g, block, n_keep, k_top)))) return s;
-  return from_hip(hys::launch_hier_select(g, q, k, scores, block, n_keep, k_top, block_scores, blocks, idx, ws, stream));
+  return from_hip(hys::launch_hier_select(g, q, k, nullptr, 0, scores, block, n_keep, k_top, block_scores, blocks, idx,
+                                          ws, stream));
+}
+
+hys_status hysparse_hier_pool(const hys_attn_desc* desc, const void* k, int32_t block, int32_t m_begin, int32_t m_end,
+                              float* kbar, int32_t kbar_blocks, hipStream_t stream) {
+  if (!desc) return fail(HYS_ERR_NULL_PTR, "desc is NULL");
+  // only the cache (kv) fields are used: validate them with a stand-in query
+  hys_attn_desc d = *desc;
+  d.q_len = 1;
+  d.n_q_heads = d.n_kv_heads;
+  for (int x = 0; x < 3; ++x) d.q_stride[x] = d.kv_stride[x];
+  hys::Geom g;
+  hys_status s;
+  if ((s = check_desc(&d, &g))) return s;
+  if (block < 1) return fail(HYS_ERR_BAD_SHAPE, "block must be >= 1");
+  const int64_t M = ((int64_t)g.Tkv + block - 1) / block;
+  if (M > hys::hier_max_blocks())
+    return fail(HYS_ERR_UNSUPPORTED, "more than " + std::to_string(hys::hier_max_blocks()) + " pooled blocks per row");
+  if (kbar_blocks < M || kbar_blocks > hys::hier_max_blocks())
+    return fail(HYS_ERR_BAD_SHAPE, "kbar_blocks must cover ceil(kv_len / block) blocks");
+  if (m_begin < 0 || m_end < m_begin || m_end > M)
+    return fail(HYS_ERR_BAD_SHAPE, "need 0 <= m_begin <= m_end <= ceil(kv_len / block)");
+  if ((s = check_tensor(k, "k", 16)) || (s = check_tensor(kbar, "kbar", 16))) return s;
+  return from_hip(hys::launch_hier_pool(g, k, block, m_begin, m_end, kbar, kbar_blocks, stream));
+}
+
+hys_status hysparse_hier_select_pooled(const hys_attn_desc* desc, const void* q, const float* kbar, int32_t kbar_blocks,
+                                       const float* scores, int32_t block, int32_t n_keep, int32_t k_top,
+                                       float* block_scores, int32_t* blocks, int32_t* idx, void* ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  hys::Geom g;
+  hys_status s;
+  if ((s = check_hier(desc, block, n_keep, k_top, &g))) return s;
+  if (kbar_blocks < (g.Tkv + block - 1) / block || kbar_blocks > hys::hier_max_blocks())
+    return fail(HYS_ERR_BAD_SHAPE, "kbar_blocks must cover ceil(kv_len / block) blocks");
+  if ((s = check_tensor(q, "q", 16)) || (s = check_tensor(kbar, "kbar", 16)) ||
+      (s = check_tensor(scores, "scores", 16)) || (s = check_tensor(idx, "idx", 4)))
+    return s;
+  if (block_scores && !aligned(block_scores, 4)) return fail(HYS_ERR_ALIGN, "block_scores is not 4-byte aligned");
+  if (blocks && !aligned(blocks, 4)) return fail(HYS_ERR_ALIGN, "blocks is not 4-byte aligned");
+  if ((s = check_ws(ws, ws_bytes, hys::hier_ws_bytes(g, block, n_keep, k_top)))) return s;
+  return from_hip(hys::launch_hier_select(g, q, nullptr, kbar, kbar_blocks, scores, block, n_keep, k_top, block_scores,
+                                          blocks, idx, ws, stream));
 }
 
 hys_status hysparse_append_kv(const hys_attn_desc* desc, const void* k_new, const void* v_new, int32_t n_new,

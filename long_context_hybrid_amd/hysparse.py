@@ -29,7 +29,8 @@ EXPORTS = ("hysparse_full_attn_scores", "hysparse_topk", "hysparse_sparse_attn",
            "hysparse_workspace_bytes", "hysparse_topk_workspace_bytes", "hysparse_status_string",
            "hysparse_last_error", "hysparse_version", "hysparse_trace_begin", "hysparse_trace_end",
            "hysparse_trace_name", "hysparse_hier_select", "hysparse_hier_workspace_bytes", "hysparse_append_kv",
-           "hysparse_sparse_attn_token_gate", "hysparse_sparse_attn_ex")
+           "hysparse_sparse_attn_token_gate", "hysparse_sparse_attn_ex", "hysparse_hier_pool",
+           "hysparse_hier_select_pooled")
 
 
 class HysWindowKV(ctypes.Structure):
@@ -82,6 +83,10 @@ def lib() -> ctypes.CDLL:
     L.hysparse_version.restype = i32
     L.hysparse_hier_select.argtypes = [D, _P, _P, _P, i32, i32, i32, _P, _P, _P, _P, sz, _P]
     L.hysparse_hier_select.restype = i32
+    L.hysparse_hier_pool.argtypes = [D, _P, i32, i32, i32, _P, i32, _P]
+    L.hysparse_hier_pool.restype = i32
+    L.hysparse_hier_select_pooled.argtypes = [D, _P, _P, i32, _P, i32, i32, i32, _P, _P, _P, _P, sz, _P]
+    L.hysparse_hier_select_pooled.restype = i32
     L.hysparse_hier_workspace_bytes.argtypes = [D, i32, i32, i32]
     L.hysparse_append_kv.argtypes = [D, _P, _P, i32, i32, _P, _P, _P]
     L.hysparse_sparse_attn_token_gate.argtypes = [D, _P, _P, _P, _P, i32, i32, i32, _P, i64, i64, _P, _P, sz, _P]
@@ -294,6 +299,43 @@ def hysparse_hier_select(q, k, scores, block: int, n_keep: int, k_top: int, idx=
     _check(lib().hysparse_hier_select(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(scores), block, n_keep, k_top,
                                       _ptr(block_scores), _ptr(blocks), _ptr(idx), _ptr(ws),
                                       0 if ws is None else ws.numel(), _stream(dev)))
+    return idx, block_scores, blocks
+
+
+def hysparse_hier_pool(k, block: int, kbar, m_begin: int = 0, m_end=None):
+    """Pooled keys of blocks [m_begin, m_end) of the cache k [B, kv_len, Hkv, D]
+    (a view of the tokens it holds now) into kbar [B, kbar_blocks, Hkv, D]
+    float32 (contiguous); m_end defaults to ceil(kv_len / block)."""
+    _same_device(k, kbar)
+    if (kbar.dtype != torch.float32 or not kbar.is_contiguous() or kbar.dim() != 4 or kbar.shape[0] != k.shape[0]
+            or kbar.shape[2:] != k.shape[2:]):
+        raise ValueError("kbar must be contiguous float32 [B, kbar_blocks, Hkv, D]")
+    m_end = -(-k.shape[1] // block) if m_end is None else m_end
+    desc = make_desc(k, k)
+    _check(lib().hysparse_hier_pool(ctypes.byref(desc), _ptr(k), block, m_begin, m_end, _ptr(kbar), kbar.shape[1],
+                                    _stream(k.device)))
+    return kbar
+
+
+def hysparse_hier_select_pooled(q, k, kbar, scores, block: int, n_keep: int, k_top: int, idx=None, block_scores=None,
+                                blocks=None, want_blocks: bool = True, workspace=None, scale: float = 0.0):
+    """hysparse_hier_select with the pooled keys kbar [B, kbar_blocks, Hkv, D]
+    float32 from hysparse_hier_pool; k (the cache view) supplies only the
+    shape and strides of the call and is not read."""
+    dev = _same_device(q, kbar, scores)
+    if kbar.dtype != torch.float32 or not kbar.is_contiguous() or kbar.dim() != 4:
+        raise ValueError("kbar must be contiguous float32 [B, kbar_blocks, Hkv, D]")
+    desc = make_desc(q, k, scale)
+    B, Hkv, Tkv = q.shape[0], k.shape[2], k.shape[1]
+    M = -(-Tkv // block)
+    idx = torch.empty((B, Hkv, 1, k_top), dtype=torch.int32, device=dev) if idx is None else idx
+    if want_blocks:
+        block_scores = torch.empty((B, Hkv, M), dtype=torch.float32, device=dev) if block_scores is None else block_scores
+        blocks = torch.empty((B, Hkv, n_keep), dtype=torch.int32, device=dev) if blocks is None else blocks
+    ws = _workspace(hysparse_hier_workspace_bytes(desc, block, n_keep, k_top), dev, workspace)
+    _check(lib().hysparse_hier_select_pooled(ctypes.byref(desc), _ptr(q), _ptr(kbar), kbar.shape[1], _ptr(scores),
+                                             block, n_keep, k_top, _ptr(block_scores), _ptr(blocks), _ptr(idx),
+                                             _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)))
     return idx, block_scores, blocks
 
 

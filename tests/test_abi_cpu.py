@@ -135,6 +135,26 @@ def test_hier_validation():
     assert L.hysparse_hier_workspace_bytes(ctypes.byref(d), 128, 8, 64) > 0
 
 
+def test_hier_pool_and_pooled_select_validation():
+    L = hy.lib()
+    d = _desc(Tq=1, Tkv=1000)                                   # 8 blocks of 128
+    pool = lambda dd, blk, m0, m1, kb, kbar=FAKE, k=FAKE: L.hysparse_hier_pool(ctypes.byref(dd) if dd else None, k,
+                                                                               blk, m0, m1, kbar, kb, None)
+    assert pool(None, 128, 0, 8, 8) == 1
+    assert pool(d, 0, 0, 8, 8) == 2                             # block < 1
+    assert pool(d, 128, -1, 8, 8) == 2                          # m_begin < 0
+    assert pool(d, 128, 5, 4, 8) == 2                           # m_end < m_begin
+    assert pool(d, 128, 0, 9, 9) == 2                           # past ceil(kv_len / block)
+    assert pool(d, 128, 0, 8, 7) == 2                           # kbar_blocks too small
+    assert pool(d, 128, 0, 8, 8, kbar=None) == 1
+    assert pool(d, 128, 0, 8, 8, kbar=FAKE_ODD) == 4
+    sel = lambda dd, kb, kbar=FAKE: L.hysparse_hier_select_pooled(ctypes.byref(dd), FAKE, kbar, kb, FAKE, 128, 4, 64,
+                                                                  None, None, FAKE, FAKE, 1 << 40, None)
+    assert sel(d, 7) == 2                                       # kbar_blocks too small
+    assert sel(d, 8, kbar=None) == 1
+    assert sel(_desc(Tq=4, Tkv=1000), 8) == 3                   # decode only
+
+
 def test_workspace_query_grows_with_problem():
     L = hy.lib()
     small = L.hysparse_workspace_bytes(hy.HYS_OP_HYBRID, ctypes.byref(_desc(Tkv=1024)), 1, 64, 128)

@@ -75,3 +75,55 @@ def test_hier128k_full_size_iou_and_sparse_output():
     say(f"  mean IoU vs flat {np.mean(ious):.4f}; planted recall hier {rec_h:.3f} flat {rec_f:.3f}; "
         f"sparse output rel-l2 vs flat {rel:.4f}")
     assert rec_f == 1.0
+
+
+def test_hier_pooled_select_equals_hier_select():
+    """Pooled keys from hysparse_hier_pool (into an array with spare blocks)
+    give hysparse_hier_select's outputs bit for bit, and match the oracle's
+    block means."""
+    wl = W["hier128k"].replace(batch=2, kv_len=3000, k_top=300, n_sparse=1, n_planted=8)
+    block, n_keep = 128, 6
+    say("hier pooled select vs hier select")
+    inp = gen.make_inputs(wl)
+    qf, k = dev_tensor(inp.q_full, wl.dtype), dev_tensor(inp.k, wl.dtype)
+    _, _, S = hy.hysparse_full_attn_scores(qf, k, dev_tensor(inp.v, wl.dtype), 1)
+    M = -(-wl.kv_len // block)
+    kbar = torch.full((wl.batch, M + 5, wl.n_kv_heads, wl.head_dim), float("nan"), device="cuda")
+    hy.hysparse_hier_pool(k, block, kbar)
+    ref = hy.hysparse_hier_select(qf, k, S, block, n_keep, wl.k_top)
+    got = hy.hysparse_hier_select_pooled(qf, k, kbar, S, block, n_keep, wl.k_top)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+    np.testing.assert_allclose(host(kbar[:, :M]), orc.pooled_keys(inp.k, block), rtol=1e-6, atol=1e-6)
+    assert torch.isnan(kbar[:, M:]).all()          # blocks past the cache are not written
+
+
+def test_hier_pool_refresh_in_decode_loop():
+    """Decode loop: append one token per step and refresh only the block that
+    holds it; the pooled keys stay equal (bit for bit) to pooling the grown
+    cache from scratch, and the selection equals hysparse_hier_select."""
+    wl = W["hier128k"].replace(batch=1, kv_len=1400, k_top=128, n_sparse=1, n_planted=4)
+    block, n_keep, L0, steps = 100, 4, 1195, 9          # crosses the block boundary at 1200
+    say("hier pool refresh over a decode loop")
+    inp = gen.make_inputs(wl)
+    qf, k_all, v_all = (dev_tensor(x, wl.dtype) for x in (inp.q_full, inp.k, inp.v))
+    kc, vc = k_all.clone(), v_all.clone()
+    cap_blocks = -(-wl.kv_len // block)
+    kbar = torch.zeros((1, cap_blocks, wl.n_kv_heads, wl.head_dim), device="cuda")
+    hy.hysparse_hier_pool(kc[:, :L0], block, kbar)
+    for s in range(steps):
+        L = L0 + s + 1
+        hy.hysparse_append_kv(k_all[:, L - 1:L].contiguous(), v_all[:, L - 1:L].contiguous(), kc, vc, L - 1)
+        m = (L - 1) // block
+        hy.hysparse_hier_pool(kc[:, :L], block, kbar, m, m + 1)
+        fresh = torch.zeros_like(kbar)
+        hy.hysparse_hier_pool(kc[:, :L], block, fresh)
+        M = -(-L // block)
+        _, _, S = hy.hysparse_full_attn_scores(qf, kc[:, :L], vc[:, :L], 1)
+        ref = hy.hysparse_hier_select(qf, kc[:, :L], S, block, n_keep, wl.k_top)
+        got = hy.hysparse_hier_select_pooled(qf, kc[:, :L], kbar, S, block, n_keep, wl.k_top)
+        torch.cuda.synchronize()
+        assert torch.equal(kbar[:, :M], fresh[:, :M]), f"step {s}"
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b), f"step {s}"
