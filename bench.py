@@ -382,12 +382,16 @@ def main():
                                     "us": t_full * 1e6, "alg_flops": ff,
                                     "note": "two sweeps: the score sweep recomputes QK^T after the final LSE"}
     if hier:
-        from oracle import hysparse_oracle as orc  # set-overlap and recall helpers only (reporting)
         flat = hy.hysparse_topk(scores.view(B * Hkv, Tkv), wl.k_top).view(B, Hkv, 1, wl.k_top)
         o_flat = hy.hysparse_sparse_attn(qs[0], k, v, flat, wl.k_top, 1, wl.window, gates[0])
         torch.cuda.synchronize()
         fl, hi = flat.cpu().numpy(), idx_np
-        ious = [orc.selection_iou(hi[b, g], fl[b, g]) for b in range(B) for g in range(Hkv)]
+        def iou(a, b):  # set overlap of two index lists, padding (-1) ignored
+            sa, sb = np.unique(a[a >= 0]), np.unique(b[b >= 0])
+            union = np.union1d(sa, sb).size
+            return np.intersect1d(sa, sb).size / union if union else 1.0
+
+        ious = [iou(hi[b, g], fl[b, g]) for b in range(B) for g in range(Hkv)]
         rec = lambda sel: float(np.mean([np.isin(inp.planted[b], sel[b, g]).mean() for b in range(B)
                                           for g in range(Hkv)]))
         oh, of = outs[0].float().cpu().numpy(), o_flat.float().cpu().numpy()

@@ -31,6 +31,11 @@ KERNELS = {  # symbol fragment -> name used by the library's trace hook
     "prefill_scores_kernel": "full_prefill_scores",
     "prefill_block_scores_kernel": "full_prefill_scores",
     "sparse_block_kernel": "sparse_prefill",
+    "pool_keys_kernel": "hier_pool_keys",
+    "block_logits_kernel": "hier_block_logits",
+    "block_softmax_kernel": "hier_block_softmax",
+    "gather_candidates_kernel": "hier_gather",
+    "map_positions_kernel": "hier_map",
 }
 
 
