@@ -32,6 +32,12 @@ PREFILL_CASES = {
     # G = 16 with queries after a cached prefix: several score passes, ragged tiles
     "g16_chunk_q70_kv333": W["decode128k"].replace(q_len=70, kv_len=333, score_block=64, k_top=64, n_sparse=1,
                                                    n_planted=0, std=1.0),
+    # fp32 with head_dim 128, and bf16 with head_dim 64 and grouped heads
+    "f32_d128_g4_sb64": W["tiny"].replace(q_len=150, kv_len=150, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                          std=1.0 / np.sqrt(128.0), score_block=64, k_top=48, window=20,
+                                          n_sparse=1),
+    "bf16_d64_g8_sb64": W["prefill32k"].replace(q_len=260, kv_len=260, n_q_heads=16, n_kv_heads=2, head_dim=64,
+                                                k_top=80, window=32, n_sparse=1),
 }
 
 
