@@ -398,6 +398,51 @@ __device__ __forceinline__ void dma_tile_k(unsigned char* stage, const uint16_t*
   }
 }
 
+// A tile staged through registers into the DMA stage layout (bf16, head_dim
+// 128), for gathered rows: each thread loads whole 16-byte chunks of a key's
+// K and V rows (chunk x & 15 of tile entry x >> 4) and stores them at their
+// swizzled slots, so the tile is read with dma_k_frag / dma_v_frag and V
+// needs no transposition on the way in.  Same interface as TileStage; a row
+// whose entry is invalid is loaded from key 0 and masked with index -1.
+template <int NT>
+struct SwTileStage {
+  static constexpr int kChunks = kTK * 16;  // 16-byte chunks per tensor
+  static_assert(kChunks % NT == 0, "threads must divide the tile's chunks");
+  static constexpr int NC = kChunks / NT;
+  u32x4_t kr[NC];
+  u32x4_t vr[NC];
+  int jk;
+
+  template <class KeyFn>
+  __device__ __forceinline__ void load(const uint16_t* kbase, const uint16_t* vbase, int64_t ks_t, KeyFn key) {
+    load(kbase, vbase, ks_t, key, [](int j) { return j; });
+  }
+  template <class KeyFn, class RowFn>
+  __device__ __forceinline__ void load(const uint16_t* kbase, const uint16_t* vbase, int64_t ks_t, KeyFn key,
+                                       RowFn row) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int s = 0; s < NC; ++s) {
+      const int x = tid + s * NT, t = x >> 4, c = x & 15;
+      const int j = key(t);
+      const int64_t off = (int64_t)(j >= 0 ? row(j) : 0) * ks_t + 8 * c;
+      kr[s] = *reinterpret_cast<const u32x4_t*>(kbase + off);
+      vr[s] = *reinterpret_cast<const u32x4_t*>(vbase + off);
+    }
+    jk = (tid < kTK) ? key(tid) : -1;
+  }
+  __device__ __forceinline__ void store(unsigned char* stage, int* kj) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int s = 0; s < NC; ++s) {
+      const int x = tid + s * NT, t = x >> 4, c = x & 15;
+      *reinterpret_cast<u32x4_t*>(stage + t * DmaTile::kRow + ((c ^ (t & 15)) << 4)) = kr[s];
+      *reinterpret_cast<u32x4_t*>(stage + DmaTile::kHalf + t * DmaTile::kRow + ((c ^ (2 * (t & 7))) << 4)) = vr[s];
+    }
+    if (tid < kTK) kj[tid] = jk;
+  }
+};
+
 // K fragment (same lanes and k order as lds_k_frag) from a DMA stage.
 __device__ __forceinline__ bf16x8_t dma_k_frag(const unsigned char* stage, int kt, int c, int col, int quad) {
   const int row = 16 * kt + col;  // row & 15 == col

@@ -17,6 +17,8 @@
 // layers); the intelliparadigm article sections 2.2 and 3.1 (global branch on
 // the shared KV at the TopK indices, 128-token window branch, gated sum,
 // index sharing); the Baidu article's gather-then-attend pseudocode.
+#include <type_traits>
+
 #include "attn_tile.h"
 #include "hys_internal.h"
 
@@ -570,7 +572,12 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
   using ST = typename TR::storage;
   using L = TileLayout<TR, D>;
   constexpr int KC = D / 32, DT = D / 16;
-  __shared__ __align__(16) unsigned char sm[L::kBytes];
+  // bf16, head_dim 128: tiles in the swizzled DMA stage layout (conflict-free
+  // fragment reads, V read transposed by ds_read_b64_tr_b16), still staged
+  // through registers
+  constexpr bool kSw = TR::kBytes == 2 && D == 128;
+  constexpr size_t kTileBytes = kSw ? (size_t)DmaTile::kBytes : (size_t)L::kBytes;
+  __shared__ __align__(16) unsigned char sm[kTileBytes];
   __shared__ int kj[kTK];
   __shared__ int idx_stage[kIdxCh];
   // the window branch's gated share of each output row, kept in LDS until
@@ -578,7 +585,7 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
   // the output itself); rows of SP elements (pitch D + 8: conflict-free)
   constexpr int SP = D + 8;
   constexpr size_t kStash = (size_t)kNW * kRTW * 16 * SP * sizeof(ST);
-  constexpr bool kLdsStash = L::kBytes + kStash + (kTK + kIdxCh) * sizeof(int) <= 160 * 1024;
+  constexpr bool kLdsStash = kTileBytes + kStash + (kTK + kIdxCh) * sizeof(int) <= 160 * 1024;
   __shared__ __align__(16) ST wstash[kLdsStash ? kNW * kRTW * 16 * SP : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, quad = lane >> 4;
 
@@ -722,7 +729,7 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
         return e < ktop ? idx_s[e & (kIdxCh - 1)] : -1;
       };
     };
-    TileStage<TR, D, kNT, true> stg;
+    std::conditional_t<kSw, SwTileStage<kNT>, TileStage<TR, D, kNT, true>> stg;
     auto load_tile = [&](int tile) {
       if (tile < nwt)
         stg.load(wkbase, wvbase, wst, key_of(tile), [=](int j) { return ring > 0 ? j % ring : j; });
@@ -755,12 +762,18 @@ __global__ __launch_bounds__(kNW * 64) void sparse_block_kernel(PrefillArgs a) {
     };
     // The two branches run as two loops (one live output state; separate loops
     // keep the register pressure of one attention step each).
+    auto attend = [&](bool mask, auto valid) {
+      if constexpr (kSw)
+        attend_tile_dma<kRTW>(st, qf, sm, [&](int e) { return kj[e]; }, a.sl2, mask, valid);
+      else
+        attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, mask, valid);
+    };
     for (int it = 0; it < nwt; ++it) {
-      if (stage(it)) attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, true, window_valid);
+      if (stage(it)) attend(true, window_valid);
     }
     window_share();
     for (int it = nwt; it < ntiles; ++it) {
-      if (stage(it)) attend_tile<TR, D, kRTW>(st, qf, sm, kj, a.sl2, tile_needs_mask(kj, pmin), causal_valid);
+      if (stage(it)) attend(tile_needs_mask(kj, pmin), causal_valid);
     }
   }
   float gsig[kRTW][4];
