@@ -3,6 +3,10 @@
 ``python -m long_context_hybrid_amd.profiling stats DIR`` prints a markdown
 table of per-kernel durations from ``--kernel-trace --stats -f csv`` output.
 
+``python -m long_context_hybrid_amd.profiling counters DIR...`` prints SQ
+counter ratios (MFMA busy, co-issue, wave-time split, LDS bank conflicts) per
+kernel from ``--pmc`` runs of the counters named in the table's header.
+
 ``python -m long_context_hybrid_amd.profiling traffic --workload W --fetch DIR
 --write DIR --copy-fetch DIR --copy-write DIR`` turns two ``--pmc FETCH_SIZE``
 / ``--pmc WRITE_SIZE`` runs of ``bench.py`` into HBM bytes per launch for each
@@ -74,6 +78,45 @@ def counter_per_kernel(d: str, counter: str) -> dict:
     return {k: statistics.median(v) for k, v in vals.items()}
 
 
+def counters_table(dirs, xcds: int = 8, simds: int = 1024) -> str:
+    """Markdown table of SQ counter ratios per library kernel (medians over
+    dispatches) from one or more ``--pmc`` runs.  GRBM_GUI_ACTIVE is the sum
+    over the XCDs (``xcds``); ``simds`` is the chip's SIMD count.  Wave-cycle
+    counters are in units of four cycles, as the hardware reports them."""
+    vals = {}
+    for d in dirs:
+        path = _one(os.path.join(d, "**", "*counter_collection.csv"))
+        for r in csv.DictReader(open(path)):
+            name = short_name(r["Kernel_Name"])
+            if name not in KERNELS.values():
+                continue
+            per = vals.setdefault(name, {})
+            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            per.setdefault("_ns", []).append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    med = {k: {c: statistics.median(v) for c, v in per.items()} for k, per in vals.items()}
+    out = ["| kernel | clock GHz | MFMA busy % | VALU issued beside MFMA % | wave time issuing / waiting to "
+           "issue / waiting on counters % | LDS bank-conflict % | VALU per MFMA | LDS per MFMA |",
+           "|---|---|---|---|---|---|---|---|"]
+    for k in sorted(med):
+        m = med[k]
+        need = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_WAVE_CYCLES",
+                "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_LDS_BANK_CONFLICT",
+                "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS")
+        if any(c not in m for c in need):
+            continue
+        cyc = m["GRBM_GUI_ACTIVE"] / xcds
+        wave = m["SQ_WAVE_CYCLES"]
+        out.append(
+            f"| {k} | {cyc / m['_ns']:.2f} | {100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * simds):.1f} | "
+            f"{100 * m['SQ_VALU_MFMA_COEXEC_CYCLES'] / (cyc * simds):.1f} | "
+            f"{100 * m['SQ_ACTIVE_INST_ANY'] / wave:.0f} / {100 * m['SQ_WAIT_INST_ANY'] / wave:.0f} / "
+            f"{100 * m['SQ_WAIT_ANY'] / wave:.0f} | "
+            f"{100 * m['SQ_LDS_BANK_CONFLICT'] / max(m['SQ_LDS_IDX_ACTIVE'], 1.0):.1f} | "
+            + (f"{m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f} | {m['SQ_INSTS_LDS'] / m['SQ_INSTS_MFMA']:.2f} |"
+               if m["SQ_INSTS_MFMA"] > 0 else "— | — |"))
+    return "\n".join(out)
+
+
 def copy_factor(d: str, counter: str, nbytes: int) -> float:
     v = counter_per_kernel(d, counter)
     copy = [x for k, x in v.items() if "copyBuffer" in k or "copy" in k.lower()]
@@ -107,6 +150,8 @@ def main():
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("dir")
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
     t = sub.add_parser("traffic")
     t.add_argument("--workload", required=True)
     t.add_argument("--fetch", required=True)
@@ -119,6 +164,9 @@ def main():
     args = ap.parse_args()
     if args.cmd == "stats":
         print(stats_table(args.dir))
+        return
+    if args.cmd == "counters":
+        print(counters_table(args.dirs))
         return
     res = traffic(args)
     try:
