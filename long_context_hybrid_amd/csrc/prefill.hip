@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kNW * 64, kWPE) void prefill_fwd_kernel(PrefillArgs
 
 // ---------------------------------------------------------- sweep 2: scores
 // One staged tile for the streaming score sweep: per key, the sum of P over
-// the wave's RTW row tiles, written to wred[key] (lanes of quad 0).
+// the wave's RTW row tiles, written to wred[key].
 // kfrag(ct, c): K fragment of key sub-tile ct, k-step c; keys(e): key index
 // of tile entry e (-1: invalid).  Row tile x holds queries 16 (x % 4) .. of
 // the block, so the position of the lane's row r is pos0 + 16 (x % 4) + r
@@ -239,30 +239,43 @@ __device__ __forceinline__ void block_score_tile(const typename TR::frag (&qf)[R
                                                  const float (&nl)[RTW][4], int pos0, KFrag kfrag, Keys keys,
                                                  float sl2, float* wred) {
   constexpr int KC = D / 32;
-  const int lane = threadIdx.x & 63, col = lane & 15, quad = lane >> 4;
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
+  const int lane = threadIdx.x & 63, col = lane & 15;
+  // logits of key sub-tile ct for the wave's row tiles
+  auto qk = [&](int ct, f32x4_t (&s)[RTW]) {
     typename TR::frag kf[KC];
 #pragma unroll
     for (int c = 0; c < KC; ++c) kf[c] = kfrag(ct, c);
+#pragma unroll
+    for (int x = 0; x < RTW; ++x) {
+      s[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) TR::mma(s[x], qf[x][c], kf[c]);
+    }
+  };
+  // Software pipeline over the four sub-tiles: the MFMAs of sub-tile ct + 1
+  // are issued beside the exponentials and sums of sub-tile ct (independent
+  // work of one wave that the MFMA unit and the VALU can run at once).
+  f32x4_t sc[2][RTW];
+  qk(0, sc[0]);
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    if (ct + 1 < 4) qk(ct + 1, sc[(ct + 1) & 1]);
+    const f32x4_t(&s)[RTW] = sc[ct & 1];
     const int j = MASK ? keys(16 * ct + col) : 0;
     float pr[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int x = 0; x < RTW; ++x) {
-      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < KC; ++c) TR::mma(s, qf[x][c], kf[c]);
+    for (int x = 0; x < RTW; ++x)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(fmaf(s[r], sl2, nl[x][r]));
+        const float p = fast_exp2(fmaf(s[x][r], sl2, nl[x][r]));
         if constexpr (MASK)
           pr[r] += (j >= 0 && j <= pos0 + 16 * (x & 3) + r) ? p : 0.f;
         else
           pr[r] += p;
       }
-    }
-    const float v = wave_sum16x4(pr[0] + pr[1] + pr[2] + pr[3]);
-    if (quad == 0) wred[16 * ct + col] = v;
+    // the four lanes of a key hold the same sum (fixed order), so all of them
+    // store it: no branch splits the scheduling region
+    wred[16 * ct + col] = wave_sum16x4(pr[0] + pr[1] + pr[2] + pr[3]);
   }
 }
 
