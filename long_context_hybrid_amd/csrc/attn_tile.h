@@ -203,14 +203,15 @@ __device__ __forceinline__ void qk_tile(f32x4_t (&sacc)[RTW][4], const typename 
 // marks an invalid tile entry), then raises the running maxima that the tile
 // exceeds by more than the slack, rescaling O and l (one wave vote).  After
 // it, exp_pack_tile turns the logits into probabilities.
-template <typename TR, int D, int RTW, class Keys, class Valid>
-__device__ __forceinline__ void mask_vote_tile_k(RowState<RTW, D>& st, f32x4_t (&sacc)[RTW][4], Keys keys,
+// NKT is the number of 16-key sub-tiles the logits cover (4: a whole tile).
+template <typename TR, int D, int RTW, int NKT, class Keys, class Valid>
+__device__ __forceinline__ void mask_vote_tile_k(RowState<RTW, D>& st, f32x4_t (&sacc)[RTW][NKT], Keys keys,
                                                  float sl2, bool mask, Valid valid) {
   constexpr int DT = D / 16;
   const int lane = threadIdx.x & 63, quad = lane >> 4;
   if (mask) {  // masked logits in place
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = keys(16 * kt + 4 * quad + r);
@@ -227,7 +228,7 @@ __device__ __forceinline__ void mask_vote_tile_k(RowState<RTW, D>& st, f32x4_t (
   for (int rt = 0; rt < RTW; ++rt) {
     lm[rt] = kNegInf;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) lm[rt] = fmaxf(lm[rt], sacc[rt][kt][r]);
     // scale > 0, so max(raw) * sl2 is the max of the scaled logits
@@ -260,24 +261,24 @@ __device__ __forceinline__ void mask_vote_tile(RowState<RTW, D>& st, f32x4_t (&s
 // exp_pack_tile: probabilities 2^(logit * sl2 - m) of a tile whose maxima
 // mask_vote_tile has settled, added to the row sums and packed as PV's A
 // operand.
-template <typename TR, int D, int RTW>
-__device__ __forceinline__ void exp_pack_tile(RowState<RTW, D>& st, const f32x4_t (&sacc)[RTW][4], float sl2,
-                                              typename TR::frag (&pa)[RTW][2]) {
+template <typename TR, int D, int RTW, int NKT>
+__device__ __forceinline__ void exp_pack_tile(RowState<RTW, D>& st, const f32x4_t (&sacc)[RTW][NKT], float sl2,
+                                              typename TR::frag (&pa)[RTW][NKT / 2]) {
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
     const float nmu = (st.m[rt] == kNegInf) ? 0.f : -st.m[rt];
-    float p[4][4];
+    float p[NKT][4];
     float ls = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         p[kt][r] = fast_exp2(fmaf(sacc[rt][kt][r], sl2, nmu));
         ls += p[kt][r];
       }
     st.l[rt] += ls;
-    pa[rt][0] = TR::pack(p[0], p[1]);
-    pa[rt][1] = TR::pack(p[2], p[3]);
+#pragma unroll
+    for (int kk = 0; kk < NKT / 2; ++kk) pa[rt][kk] = TR::pack(p[2 * kk], p[2 * kk + 1]);
   }
 }
 
@@ -477,19 +478,23 @@ __device__ __forceinline__ void attend_tile_dma(RowState<RTW, 128>& st, const bf
                                                 const unsigned char* stage, Keys keys, float sl2, bool mask,
                                                 Valid valid) {
   const int lane = threadIdx.x & 63, col = lane & 15, quad = lane >> 4;
-  f32x4_t sacc[RTW][4];
+  // logits of the tile's four 16-key sub-tiles
+  auto qk = [&](f32x4_t(&sacc)[RTW][4]) {
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    bf16x8_t kf[4];
+    for (int kt = 0; kt < 4; ++kt) {
+      bf16x8_t kf[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) kf[c] = dma_k_frag(stage, kt, c, col, quad);
+      for (int c = 0; c < 4; ++c) kf[c] = dma_k_frag(stage, kt, c, col, quad);
 #pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
-      sacc[rt][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int rt = 0; rt < RTW; ++rt) {
+        sacc[rt][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) BF16::mma(sacc[rt][kt], kf[c], qf[rt][c]);
+        for (int c = 0; c < 4; ++c) BF16::mma(sacc[rt][kt], kf[c], qf[rt][c]);
+      }
     }
-  }
+  };
+  f32x4_t sacc[RTW][4];
+  qk(sacc);
   bf16x8_t pa[RTW][2];
   mask_vote_tile_k<BF16, 128, RTW>(st, sacc, keys, sl2, mask, valid);
   exp_pack_tile<BF16, 128, RTW>(st, sacc, sl2, pa);
