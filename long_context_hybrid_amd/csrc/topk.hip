@@ -264,8 +264,9 @@ __device__ __forceinline__ uint32_t sample_threshold(const float* srow, int n, u
 // Steps 2 and 3 over the C candidates in sm.ckey / sm.cidx (index order).
 __device__ __forceinline__ void select_candidates(uint32_t C, uint32_t kk, int32_t* out, TopkSmem& sm) {
   const int t = threadIdx.x;
-  // thread t owns a contiguous run of candidates
-  const uint32_t per = (C + kNT - 1) / kNT;
+  // thread t owns a contiguous run of candidates; an odd run length keeps the
+  // lanes' strided LDS reads on distinct banks
+  const uint32_t per = ((C + kNT - 1) / kNT) | 1u;
   const uint32_t c0 = min(C, t * per), c1 = min(C, c0 + per);
   uint32_t T, krem;
   radix_select(kk, [&](auto f) {
@@ -290,6 +291,27 @@ __device__ __forceinline__ void select_candidates(uint32_t C, uint32_t kk, int32
 }
 
 // this thread's kEPT consecutive keys of segment sg (0 past the row end)
+// A row of at most kCap keys is its own candidate list: coalesced loads
+// (thread t takes keys t, t + kNT, ...; clamped indices, so all are in
+// flight together) stored at their index in LDS (consecutive lanes,
+// consecutive words: no bank conflicts), then select_candidates.
+__device__ __forceinline__ void select_short_row(const float* srow, int n, uint32_t kk, int32_t* out,
+                                                 TopkSmem& sm) {
+  const int t = threadIdx.x;
+  constexpr int kB = kCap / kNT;  // 12 loads per thread
+  float v[kB];
+#pragma unroll
+  for (int e = 0; e < kB; ++e) v[e] = srow[min(t + e * kNT, n - 1)];
+#pragma unroll
+  for (int e = 0; e < kB; ++e)
+    if (t + e * kNT < n) {
+      sm.ckey[t + e * kNT] = order_key(v[e]);
+      sm.cidx[t + e * kNT] = t + e * kNT;
+    }
+  __syncthreads();
+  select_candidates((uint32_t)n, kk, out, sm);
+}
+
 __device__ __forceinline__ void load_seg(const float* srow, int n, bool vec, int sg, uint32_t (&keys)[kEPT]) {
   const int j0 = sg * kSeg + threadIdx.x * kEPT;
   if (vec && j0 + kEPT <= n) {
@@ -365,6 +387,10 @@ __global__ __launch_bounds__(kNT) void topk_row_kernel(TopkArgs a) {
     return;
   }
   const float* srow = a.scores + row * a.row_stride;
+  if (n <= kCap) {  // the whole row is the candidate list: no filter
+    select_short_row(srow, n, kk, out, sm);
+    return;
+  }
   const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
   const int nseg = (n + kSeg - 1) / kSeg;
 
@@ -474,18 +500,7 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkArgs a) {
   const float* srow = a.scores + row * a.row_stride;
   const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
   if (n <= kCap) {  // the whole row is the candidate list
-    constexpr int kB = kCap / kNT;  // 12 loads per thread, all in flight
-    float v[kB];
-#pragma unroll
-    for (int e = 0; e < kB; ++e) v[e] = t + e * kNT < n ? srow[t + e * kNT] : 0.f;
-#pragma unroll
-    for (int e = 0; e < kB; ++e)
-      if (t + e * kNT < n) {
-        sm.ckey[t + e * kNT] = order_key(v[e]);
-        sm.cidx[t + e * kNT] = t + e * kNT;
-      }
-    __syncthreads();
-    select_candidates((uint32_t)n, kk, out, sm);
+    select_short_row(srow, n, kk, out, sm);
     return;
   }
   if (t < 64) {  // one lane per part (nparts <= 64): counts, then an exclusive scan
