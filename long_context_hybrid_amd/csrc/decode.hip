@@ -388,20 +388,10 @@ __global__ __launch_bounds__(D) void sparse_merge_kernel(DecodeArgs a) {
     const float m = in ? pml[(sp * a.G + h) * 2] : kNegInf;
     const float l = in ? pml[(sp * a.G + h) * 2 + 1] : 0.f;
     // branch max and sum over the lanes of the same branch
-    float mg = (in && !win) ? m : kNegInf, mw = (in && win) ? m : kNegInf;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      mg = fmaxf(mg, __shfl_xor(mg, off));
-      mw = fmaxf(mw, __shfl_xor(mw, off));
-    }
+    const float mg = wave_max_f32((in && !win) ? m : kNegInf), mw = wave_max_f32((in && win) ? m : kNegInf);
     const float mu = win ? (mw == kNegInf ? 0.f : mw) : (mg == kNegInf ? 0.f : mg);
     const float w = in ? exp2f(m - mu) : 0.f;
-    float lg = (in && !win) ? l * w : 0.f, lw = (in && win) ? l * w : 0.f;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      lg += __shfl_xor(lg, off);
-      lw += __shfl_xor(lw, off);
-    }
+    const float lg = wave_sum_f32((in && !win) ? l * w : 0.f), lw = wave_sum_f32((in && win) ? l * w : 0.f);
     const float gt = 1.f / (1.f + expf(-gw));
     const float L = win ? lw : lg;
     const float scale = (L > 0.f) ? (win ? (1.f - gt) : gt) / L : 0.f;

@@ -180,6 +180,70 @@ __device__ __forceinline__ float dpp_quad(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (row
+// shifts by 1, 2, 4, 8 inside each row of 16 lanes, then the row broadcasts of
+// lanes 15 and 31 into the rows above); lanes without a source add 0.  Lane
+// layout checked against a CPU prefix sum on the GPU.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWMASK, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += dpp_or_zero<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_or_zero<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_or_zero<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_or_zero<0x118, 0xF>(x);  // row_shr:8
+  x += dpp_or_zero<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_or_zero<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+// Minimum and maximum over the 64 lanes of a wave (every lane gets both):
+// DPP moves inside each row of 16 lanes, then the four row results.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_or_self(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ void wave_min_max(uint32_t& mn, uint32_t& mx) {
+  mn = min(mn, dpp_or_self<0xB1>(mn));  // quad_perm [1,0,3,2]
+  mx = max(mx, dpp_or_self<0xB1>(mx));
+  mn = min(mn, dpp_or_self<0x4E>(mn));  // quad_perm [2,3,0,1]
+  mx = max(mx, dpp_or_self<0x4E>(mx));
+  mn = min(mn, dpp_or_self<0x124>(mn));  // row_ror:4
+  mx = max(mx, dpp_or_self<0x124>(mx));
+  mn = min(mn, dpp_or_self<0x128>(mn));  // row_ror:8
+  mx = max(mx, dpp_or_self<0x128>(mx));
+  // readlane returns int: compare the row results as unsigned
+  auto lane_u = [](uint32_t x, int l) { return (uint32_t)__builtin_amdgcn_readlane((int)x, l); };
+  mn = min(min(lane_u(mn, 0), lane_u(mn, 16)), min(lane_u(mn, 32), lane_u(mn, 48)));
+  mx = max(max(lane_u(mx, 0), lane_u(mx, 16)), max(lane_u(mx, 32), lane_u(mx, 48)));
+}
+
+// Float maximum / sum over the 64 lanes of a wave: DPP moves inside each row
+// of 16 lanes, then the rows' lane-0 values combined in a fixed order, so the
+// result is the same value in every lane and in every call.
+template <int CTRL>
+__device__ __forceinline__ float dpp_self_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f32(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ float wave_max_f32(float x) {
+  x = fmaxf(x, dpp_self_f32<0xB1>(x));
+  x = fmaxf(x, dpp_self_f32<0x4E>(x));
+  x = fmaxf(x, dpp_self_f32<0x124>(x));
+  x = fmaxf(x, dpp_self_f32<0x128>(x));
+  return fmaxf(fmaxf(lane_f32(x, 0), lane_f32(x, 16)), fmaxf(lane_f32(x, 32), lane_f32(x, 48)));
+}
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  x += dpp_self_f32<0xB1>(x);
+  x += dpp_self_f32<0x4E>(x);
+  x += dpp_self_f32<0x124>(x);
+  x += dpp_self_f32<0x128>(x);
+  return (lane_f32(x, 0) + lane_f32(x, 16)) + (lane_f32(x, 32) + lane_f32(x, 48));
+}
+
 // 4 x 4 transpose inside each group of four lanes: lane i (= l & 3) holds
 // v[0..3] on entry and, on exit, v[k] = the entry v[i] of the group's lane k.
 // Two exchange stages (lane bit 0 with value bit 0, then lane bit 1 with

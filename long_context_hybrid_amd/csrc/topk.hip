@@ -90,12 +90,7 @@ struct SampleSmem {
 // prefix and the total.  Two barriers.
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
   uint32_t pre = 0, tot = 0;
@@ -115,11 +110,7 @@ template <class SM>
 __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SM& sm, uint32_t* mn_out,
                                              uint32_t* mx_out) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
-  }
+  wave_min_max(mn, mx);
   if (lane == 0) {
     sm.wmin[wave] = mn;
     sm.wmax[wave] = mx;
@@ -505,12 +496,7 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkArgs a) {
   }
   if (t < 64) {  // one lane per part (nparts <= 64): counts, then an exclusive scan
     const uint32_t c = t < a.nparts ? a.pcnt[row * a.nparts + t] : 0u;
-    uint32_t x = c;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t y = __shfl_up(x, off);
-      if (t >= off) x += y;
-    }
+    const uint32_t x = wave_inclusive_scan(c);
     const bool ok = __builtin_amdgcn_ballot_w64(c > (uint32_t)kCap) == 0;
     if (t < a.nparts) pstart[t] = x - c;
     if (t == 63) pstart[a.nparts] = ok ? x : 0xFFFFFFFFu;
