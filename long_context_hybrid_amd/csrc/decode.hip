@@ -66,7 +66,10 @@ template <typename TR, int D>
 struct DecodeSmem {
   static constexpr int kVP = kStep + kVPad;
   static constexpr size_t kVt = (size_t)kWaves * D * kVP * TR::kBytes;
-  static constexpr size_t kObuf = (size_t)kWaves * 16 * D * sizeof(float);
+  // wave-merge rows, pitch D + 4 floats: the four lane groups of a store
+  // (rows 4 apart) fall on different banks
+  static constexpr int kOP = D + 4;
+  static constexpr size_t kObuf = (size_t)kWaves * 16 * kOP * sizeof(float);
   static constexpr size_t kMerge = 64 * 16 * 3 * sizeof(float);  // sparse merge: (m, l) + weights
   static constexpr size_t kA = kVt > kObuf ? kVt : kObuf;
   static constexpr size_t kBytes = kA > kMerge ? kA : kMerge;
@@ -258,12 +261,16 @@ __global__ __launch_bounds__(256, FULL ? 1 : 2) void decode_split_kernel(DecodeA
       }
     l_run = l_run * alpha + ls;
     m_run = m_new;
-    // rescale output rows (head 4*quad + r) by that head's alpha
+    // rescale output rows (head 4*quad + r) by that head's alpha; nothing to
+    // rescale on the wave's first step (o is zero; the sparse layer's waves
+    // take one step each)
+    if (t0 != t_begin + wave * kStep) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float ar = __shfl(alpha, 4 * quad + r);
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, 4 * quad + r);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt][r] *= ar;
+        for (int dt = 0; dt < DT; ++dt) o[dt][r] *= ar;
+      }
     }
 
     // stage V transposed: vt[d][key]
@@ -321,13 +328,14 @@ __global__ __launch_bounds__(256, FULL ? 1 : 2) void decode_split_kernel(DecodeA
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, ml_s[w][h][0]);
     const float mu = (M == kNegInf) ? 0.f : M;
-    f[r] = exp2f(ml_s[wave][h][0] - mu);
+    f[r] = fast_exp2(ml_s[wave][h][0] - mu);
   }
-  float* obuf = reinterpret_cast<float*>(smem);  // [kWaves][16][D]
+  constexpr int OP = DecodeSmem<TR, D>::kOP;
+  float* obuf = reinterpret_cast<float*>(smem);  // [kWaves][16][OP]
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) obuf[(wave * 16 + 4 * quad + r) * D + 16 * dt + col] = o[dt][r] * f[r];
+    for (int r = 0; r < 4; ++r) obuf[(wave * 16 + 4 * quad + r) * OP + 16 * dt + col] = o[dt][r] * f[r];
   __syncthreads();
 
   const int64_t pbase = (int64_t)unit * a.nsplit + split;
@@ -337,7 +345,7 @@ __global__ __launch_bounds__(256, FULL ? 1 : 2) void decode_split_kernel(DecodeA
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float4 y = *reinterpret_cast<const float4*>(obuf + (w * 16 + h) * D + d);
+      const float4 y = *reinterpret_cast<const float4*>(obuf + (w * 16 + h) * OP + d);
       acc.x += y.x;
       acc.y += y.y;
       acc.z += y.z;
@@ -353,7 +361,7 @@ __global__ __launch_bounds__(256, FULL ? 1 : 2) void decode_split_kernel(DecodeA
     const float mu = (M == kNegInf) ? 0.f : M;
     float L = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) L += ml_s[w][h][1] * exp2f(ml_s[w][h][0] - mu);
+    for (int w = 0; w < kWaves; ++w) L += ml_s[w][h][1] * fast_exp2(ml_s[w][h][0] - mu);
     a.part_ml[(pbase * a.G + h) * 2 + 0] = M;
     a.part_ml[(pbase * a.G + h) * 2 + 1] = L;
   }
