@@ -504,31 +504,35 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkArgs a) {
   __syncthreads();
   const uint32_t C = pstart[a.nparts];
   if (C <= (uint32_t)kCap && C >= kk) {
-    // candidate slot x comes from the part whose range holds it: every load
-    // is independent, so they are all in flight together
-    constexpr int kB = kCap / kNT;
-    uint32_t kv[kB];
-    int32_t iv[kB];
+    // part-major copy: tpp threads per part move its survivors to their
+    // place in the concatenated list (part order); the first kU rounds are
+    // unrolled with clamped indices, so those loads are all in flight
+    // together, and a part with more survivors finishes in a loop
+    const int tpp = kNT / a.nparts;
+    const int pp = t / tpp, r = t - pp * tpp;
+    if (pp < a.nparts) {
+      const uint32_t c0 = pstart[pp], cnt = pstart[pp + 1] - c0;
+      const int64_t base = (row * a.nparts + pp) * kCap;
+      constexpr int kU = 8;
+      uint32_t kv[kU];
+      int32_t iv[kU];
 #pragma unroll
-    for (int e = 0; e < kB; ++e) {
-      const uint32_t x = t + e * kNT;
-      if (x < C) {
-        int lo = 0, hi = a.nparts - 1;  // last part with pstart <= x
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (pstart[mid] <= x) lo = mid; else hi = mid - 1;
-        }
-        const int64_t src = (row * a.nparts + lo) * kCap + (x - pstart[lo]);
-        kv[e] = a.pkey[src];
-        iv[e] = a.pidx[src];
+      for (int u = 0; u < kU; ++u) {
+        const uint32_t i = min((uint32_t)(r + u * tpp), cnt > 0u ? cnt - 1u : 0u);
+        kv[u] = a.pkey[base + i];
+        iv[u] = a.pidx[base + i];
       }
-    }
 #pragma unroll
-    for (int e = 0; e < kB; ++e) {
-      const uint32_t x = t + e * kNT;
-      if (x < C) {
-        sm.ckey[x] = kv[e];
-        sm.cidx[x] = iv[e];
+      for (int u = 0; u < kU; ++u) {
+        const uint32_t i = r + u * tpp;
+        if (i < cnt) {
+          sm.ckey[c0 + i] = kv[u];
+          sm.cidx[c0 + i] = iv[u];
+        }
+      }
+      for (uint32_t i = r + kU * tpp; i < cnt; i += tpp) {
+        sm.ckey[c0 + i] = a.pkey[base + i];
+        sm.cidx[c0 + i] = a.pidx[base + i];
       }
     }
     __syncthreads();
