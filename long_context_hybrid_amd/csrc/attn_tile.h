@@ -333,8 +333,6 @@ __device__ __forceinline__ void attend_tile(RowState<RTW, D>& st, const typename
 //                        the two halves of the banks.
 // The DMA needs no staging registers and no LDS store instructions; the
 // caller keeps several stages in flight and waits with vmcnt.
-#define HYS_LDS __attribute__((address_space(3)))
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 // One 16-byte-per-lane LDS DMA: lane l's 16 bytes at `gaddr` go to LDS
 // address lds + 16 l (lds must be the same in every lane: it is M0).  Written
@@ -452,23 +450,9 @@ __device__ __forceinline__ bf16x8_t dma_k_frag(const unsigned char* stage, int k
 }
 
 // V fragment for P.V (same lanes and key order as lds_v_frag) from a DMA
-// stage, with the gfx950 transposed LDS read: in each group of 16 lanes,
-// lane L receives element L & 3 of the 8-byte read of lane 4e + (L >> 2) as
-// its element e.  Lane s of the group reads key r0 + (s >> 2), columns
-// d0 + 4 (s & 3) .. +3, so lane L receives keys r0 .. r0 + 3 of column
-// d0 + L.
+// stage's V half (transposed LDS read, see tr_v_frag).
 __device__ __forceinline__ bf16x8_t dma_v_frag(const unsigned char* stage, int dt, int kk, int col, int quad) {
-  const unsigned char* vs = stage + DmaTile::kHalf;
-  const int d = 16 * dt + 4 * (col & 3);
-  const int r0 = 32 * kk + 4 * quad + (col >> 2);
-  auto rd = [&](int row) {
-    const int off = row * DmaTile::kRow + (((d >> 3) ^ (2 * (row & 7))) << 4) + 8 * (col & 1);
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((HYS_LDS i16x4_t*)(vs + off));
-  };
-  const i16x4_t lo = rd(r0), hi = rd(r0 + 16);
-  typedef short i16x8_t __attribute__((ext_vector_type(8)));
-  const i16x8_t both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8_t, both);
+  return tr_v_frag(stage + DmaTile::kHalf, dt, kk, col, quad);
 }
 
 // The attention step on a DMA stage; keys(e) is the key index of tile entry

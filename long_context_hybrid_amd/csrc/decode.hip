@@ -76,7 +76,7 @@ struct DecodeSmem {
 };
 
 template <typename TR, int D, bool FULL>
-__global__ __launch_bounds__(256, FULL ? 1 : 2) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, TR::kBytes == 4 ? 1 : 2) void decode_split_kernel(DecodeArgs a) {
   using ST = typename TR::storage;
   using frag = typename TR::frag;
   using quad_t = typename TR::quad_t;
@@ -86,6 +86,11 @@ __global__ __launch_bounds__(256, FULL ? 1 : 2) void decode_split_kernel(DecodeA
   constexpr int NP = CPR / 8;           // (chunk, key-quad) pairs per lane and step
   constexpr int VP = kStep + kVPad;
   constexpr int DT = D / 16;            // 16-column output tiles
+  // bf16, head_dim 128: each V load instruction reads four whole 256-byte
+  // rows (16 lanes per row), the rows are staged unchanged (swizzled 16-byte
+  // slots, conflict-free) and read back transposed by ds_read_b64_tr_b16
+  constexpr bool kTrV = TR::kBytes == 2 && D == 128;
+  static_assert(!kTrV || NP * 4 * 4 == kStep, "eight row loads of four keys cover a step");
 
   __shared__ __align__(16) unsigned char smem[DecodeSmem<TR, D>::kBytes];
   __shared__ int kj_s[kWaves][2 * kStep];
@@ -177,14 +182,22 @@ __global__ __launch_bounds__(256, FULL ? 1 : 2) void decode_split_kernel(DecodeA
 #pragma unroll
       for (int c = 0; c < KC; ++c) kf[kt][c] = TR::template load8_stream<FULL>(kr + 32 * c + 8 * quad);
     }
+    if constexpr (kTrV) {
 #pragma unroll
-    for (int pp = 0; pp < NP; ++pp) {
-      const int pidx = lane + 64 * pp;
-      const int kq = pidx % (kStep / 4), tc = pidx / (kStep / 4);
+      for (int q = 0; q < NP * 4; ++q) {  // keys 4q .. 4q + 3, lane: chunk lane % 16 of key 4q + lane / 16
+        const int j = kjb[4 * q + (lane >> 4)];
+        vr[q >> 2][q & 3] = load16_stream<FULL>(vbase + row_of(j) * kst + 8 * (lane & 15));
+      }
+    } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = kjb[4 * kq + r];
-        vr[pp][r] = load16_stream<FULL>(vbase + row_of(j) * kst + tc * EPC);
+      for (int pp = 0; pp < NP; ++pp) {
+        const int pidx = lane + 64 * pp;
+        const int kq = pidx % (kStep / 4), tc = pidx / (kStep / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = kjb[4 * kq + r];
+          vr[pp][r] = load16_stream<FULL>(vbase + row_of(j) * kst + tc * EPC);
+        }
       }
     }
   };
@@ -273,6 +286,14 @@ __global__ __launch_bounds__(256, FULL ? 1 : 2) void decode_split_kernel(DecodeA
       }
     }
 
+    unsigned char* vtb = reinterpret_cast<unsigned char*>(vt);
+    if constexpr (kTrV) {  // V rows as loaded: key k's chunk c in slot c ^ 2 (k & 7)
+#pragma unroll
+      for (int q = 0; q < NP * 4; ++q) {
+        const int key = 4 * q + (lane >> 4), c = lane & 15;
+        *reinterpret_cast<uint4*>(vtb + key * 256 + ((c ^ (2 * (key & 7))) << 4)) = vrc[q >> 2][q & 3];
+      }
+    } else {
     // stage V transposed: vt[d][key]
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) {
@@ -300,16 +321,22 @@ __global__ __launch_bounds__(256, FULL ? 1 : 2) void decode_split_kernel(DecodeA
         }
       }
     }
+    }
     wave_lds_sync();
 
     // O += P . V ; A = P (head = col, keys {4q..4q+3, 16+4q..16+4q+3})
     const frag pa = TR::pack(p[0], p[1]);
+    if constexpr (kTrV) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const ST* row = vt + (16 * dt + col) * VP;
-      const quad_t lo = *reinterpret_cast<const quad_t*>(row + 4 * quad);
-      const quad_t hi = *reinterpret_cast<const quad_t*>(row + 16 + 4 * quad);
-      TR::mma(o[dt], pa, TR::join(lo, hi));
+      for (int dt = 0; dt < DT; ++dt) TR::mma(o[dt], pa, tr_v_frag(vtb, dt, 0, col, quad));
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const ST* row = vt + (16 * dt + col) * VP;
+        const quad_t lo = *reinterpret_cast<const quad_t*>(row + 4 * quad);
+        const quad_t hi = *reinterpret_cast<const quad_t*>(row + 16 + 4 * quad);
+        TR::mma(o[dt], pa, TR::join(lo, hi));
+      }
     }
   }
 

@@ -244,6 +244,29 @@ __device__ __forceinline__ float wave_sum_f32(float x) {
   return (lane_f32(x, 0) + lane_f32(x, 16)) + (lane_f32(x, 32) + lane_f32(x, 48));
 }
 
+#define HYS_LDS __attribute__((address_space(3)))
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// V fragment for P.V from a row-major bf16 V tile in LDS (head_dim 128, 256-byte
+// key rows, 16-byte chunk c of key k in slot c ^ 2 (k & 7)), with the gfx950
+// transposed LDS read: in each group of 16 lanes, lane L receives element
+// L & 3 of the 8-byte read of lane 4e + (L >> 2) as its element e.  Lane s of
+// the group reads key r0 + (s >> 2), columns d0 + 4 (s & 3) .. +3, so lane L
+// receives keys r0 .. r0 + 3 of column d0 + L: keys 32 kk + 4 quad + e
+// (e < 4) and 32 kk + 16 + 4 quad + e - 4 (e >= 4) of column 16 dt + col.
+__device__ __forceinline__ bf16x8_t tr_v_frag(const unsigned char* vs, int dt, int kk, int col, int quad) {
+  const int d = 16 * dt + 4 * (col & 3);
+  const int r0 = 32 * kk + 4 * quad + (col >> 2);
+  auto rd = [&](int row) {
+    const int off = row * 256 + (((d >> 3) ^ (2 * (row & 7))) << 4) + 8 * (col & 1);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((HYS_LDS i16x4_t*)(vs + off));
+  };
+  const i16x4_t lo = rd(r0), hi = rd(r0 + 16);
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, both);
+}
+
 // 4 x 4 transpose inside each group of four lanes: lane i (= l & 3) holds
 // v[0..3] on entry and, on exit, v[k] = the entry v[i] of the group's lane k.
 // Two exchange stages (lane bit 0 with value bit 0, then lane bit 1 with
