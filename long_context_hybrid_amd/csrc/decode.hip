@@ -71,7 +71,11 @@ struct DecodeSmem {
   static constexpr int kOP = D + 4;
   static constexpr size_t kObuf = (size_t)kWaves * 16 * kOP * sizeof(float);
   static constexpr size_t kMerge = 64 * 16 * 3 * sizeof(float);  // sparse merge: (m, l) + weights
-  static constexpr size_t kA = kVt > kObuf ? kVt : kObuf;
+  // bf16, head_dim 128: K is staged too (32 keys x 256 B per wave, after the
+  // V tiles), so its loads are whole rows like V's
+  static constexpr bool kLdsK = TR::kBytes == 2 && D == 128;
+  static constexpr size_t kKt = kLdsK ? (size_t)kWaves * kStep * 256 : 0;
+  static constexpr size_t kA = kVt + kKt > kObuf ? kVt + kKt : kObuf;
   static constexpr size_t kBytes = kA > kMerge ? kA : kMerge;
 };
 
@@ -174,13 +178,22 @@ __global__ __launch_bounds__(256, TR::kBytes == 4 ? 1 : 2) void decode_split_ker
   // issue the K and V row loads of one step whose key indices are in kjb
   frag kf[2][KC];
   uint4 vr[NP][4];
+  constexpr bool kLdsK = DecodeSmem<TR, D>::kLdsK;
   auto issue_loads = [&](const int* kjb) {
+    if constexpr (kLdsK) {  // whole K rows, like V: chunk lane % 16 of key 4q + lane / 16
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int j = kjb[16 * kt + col];
-      const ST* kr = kbase + row_of(j) * kst;
+      for (int q = 0; q < 8; ++q) {
+        const int j = kjb[4 * q + (lane >> 4)];
+        kf[q >> 2][q & 3] = __builtin_bit_cast(frag, load16_stream<FULL>(kbase + row_of(j) * kst + 8 * (lane & 15)));
+      }
+    } else {
 #pragma unroll
-      for (int c = 0; c < KC; ++c) kf[kt][c] = TR::template load8_stream<FULL>(kr + 32 * c + 8 * quad);
+      for (int kt = 0; kt < 2; ++kt) {
+        const int j = kjb[16 * kt + col];
+        const ST* kr = kbase + row_of(j) * kst;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) kf[kt][c] = TR::template load8_stream<FULL>(kr + 32 * c + 8 * quad);
+      }
     }
     if constexpr (kTrV) {
 #pragma unroll
@@ -230,6 +243,20 @@ __global__ __launch_bounds__(256, TR::kBytes == 4 ? 1 : 2) void decode_split_ker
       issue_loads(kjn);
     }
     buf ^= 1;
+    if constexpr (kLdsK) {  // K rows into the wave's LDS tile (chunk c of key k in slot c ^ (k & 15)), then fragments
+      unsigned char* ktb = smem + DecodeSmem<TR, D>::kVt + (size_t)wave * kStep * 256;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int key = 4 * q + (lane >> 4), c = lane & 15;
+        *reinterpret_cast<frag*>(ktb + key * 256 + ((c ^ (key & 15)) << 4)) = kfc[q >> 2][q & 3];
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          kfc[kt][c] = *reinterpret_cast<const frag*>(ktb + (16 * kt + col) * 256 + (((4 * c + quad) ^ col) << 4));
+    }
     // S^T = K . Q^T ; sacc[kt][r] = logit of key 16*kt + 4*quad + r for head col
     f32x4_t sacc[2];
 #pragma unroll
