@@ -464,16 +464,20 @@ __device__ __forceinline__ void attend_tile_dma(RowState<RTW, 128>& st, const bf
   const int lane = threadIdx.x & 63, col = lane & 15, quad = lane >> 4;
   // logits of the tile's four 16-key sub-tiles
   auto qk = [&](f32x4_t(&sacc)[RTW][4]) {
+    // the next sub-tile's K fragments are read while this one's MFMAs run
+    bf16x8_t kf[2][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kf[0][c] = dma_k_frag(stage, 0, c, col, quad);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      bf16x8_t kf[4];
+      if (kt + 1 < 4)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kf[c] = dma_k_frag(stage, kt, c, col, quad);
+        for (int c = 0; c < 4; ++c) kf[(kt + 1) & 1][c] = dma_k_frag(stage, kt + 1, c, col, quad);
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt) {
         sacc[rt][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) BF16::mma(sacc[rt][kt], kf[c], qf[rt][c]);
+        for (int c = 0; c < 4; ++c) BF16::mma(sacc[rt][kt], kf[kt & 1][c], qf[rt][c]);
       }
     }
   };
