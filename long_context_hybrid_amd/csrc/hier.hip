@@ -78,8 +78,9 @@ __global__ __launch_bounds__(256) void block_logits_kernel(const void* q, int64_
                                                            float* logit2) {
   constexpr int QN = 16 * D / 256;  // G <= 16 query rows
   constexpr int KN = 64 * D / 256;  // 64 pooled rows
-  __shared__ float qs[16 * D];
-  __shared__ float ks[64 * (D + 1)];
+  constexpr int KP = D + 4;  // pooled-key row pitch: 16-byte reads, lanes 16 apart on the same banks only
+  __shared__ __align__(16) float qs[16 * D];
+  __shared__ __align__(16) float ks[64 * KP];
   const int nchunk = (M + 63) / 64;
   const int bg = blockIdx.x / nchunk, ch = blockIdx.x - (blockIdx.x / nchunk) * nchunk;
   const int b = bg / Hkv, g = bg - (bg / Hkv) * Hkv;
@@ -102,14 +103,27 @@ __global__ __launch_bounds__(256) void block_logits_kernel(const void* q, int64_
 #pragma unroll
   for (int r = 0; r < KN; ++r) {
     const int x = t + 256 * r, mm = x / D, d = x - (x / D) * D;
-    ks[mm * (D + 1) + d] = kv[r];
+    ks[mm * KP + d] = kv[r];
   }
   __syncthreads();
-  for (int x = t; x < 64 * G; x += 256) {
-    const int mm = x & 63, h = x >> 6;
-    float acc = 0.f;
-    for (int d = 0; d < D; ++d) acc += qs[h * D + d] * ks[mm * (D + 1) + d];
-    if (m0 + mm < M) logit2[((int64_t)bg * G + h) * M + m0 + mm] = acc * sl2;
+  // thread (block mm = t & 63, head group hq = t >> 6) computes heads hq,
+  // hq + 4, hq + 8, hq + 12: one 16-byte pooled-key read feeds four heads
+  // (the query reads are wave-uniform broadcasts)
+  const int mm = t & 63, hq = t >> 6;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int d = 0; d < D; d += 4) {
+    const float4 kk = *reinterpret_cast<const float4*>(ks + mm * KP + d);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 qq = *reinterpret_cast<const float4*>(qs + (hq + 4 * u) * D + d);
+      acc[u] += qq.x * kk.x + qq.y * kk.y + qq.z * kk.z + qq.w * kk.w;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int h = hq + 4 * u;
+    if (h < G && m0 + mm < M) logit2[((int64_t)bg * G + h) * M + m0 + mm] = acc[u] * sl2;
   }
 }
 
@@ -136,20 +150,24 @@ __global__ __launch_bounds__(256) void block_softmax_kernel(const float* logit2,
     if (nm != kNegInf) {
       float add = 0.f;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) add += exp2f(v[u] - nm);
-      sum = sum * exp2f(mx - nm) + add;
+      for (int u = 0; u < 16; ++u) add += fast_exp2(v[u] - nm);
+      sum = sum * fast_exp2(mx - nm) + add;
       mx = nm;
     }
   }
-#pragma unroll
-  for (int off = 8; off > 0; off >>= 1) {
-    const float om = __shfl_xor(mx, off, 16), os = __shfl_xor(sum, off, 16);
+  // fold the 16 lanes of the head (one DPP row): quad butterflies, then the
+  // row rotations by 4 and 8; lane s == 0 holds a fixed fold order
+  auto fold = [&](float om, float os) {
     const float nm = fmaxf(mx, om);
     if (nm != kNegInf) {
-      sum = sum * exp2f(mx - nm) + os * exp2f(om - nm);
+      sum = sum * fast_exp2(mx - nm) + os * fast_exp2(om - nm);
       mx = nm;
     }
-  }
+  };
+  fold(dpp_self_f32<0xB1>(mx), dpp_self_f32<0xB1>(sum));
+  fold(dpp_self_f32<0x4E>(mx), dpp_self_f32<0x4E>(sum));
+  fold(dpp_self_f32<0x124>(mx), dpp_self_f32<0x124>(sum));
+  fold(dpp_self_f32<0x128>(mx), dpp_self_f32<0x128>(sum));
   if (s == 0 && h < G) lse[h] = mx + log2f(sum);
   __syncthreads();
   for (int m = t; m < M; m += 256) {
@@ -159,7 +177,7 @@ __global__ __launch_bounds__(256) void block_softmax_kernel(const float* logit2,
     float v = 0.f;
 #pragma unroll
     for (int hh = 0; hh < 16; ++hh)
-      if (hh < G) v += exp2f(e[hh] - lse[hh]);
+      if (hh < G) v += fast_exp2(e[hh] - lse[hh]);
     bscore[(int64_t)bg * M + m] = v;
   }
 }
