@@ -3,10 +3,12 @@
 // One workgroup (4 waves) handles one split of one unit's key list.  A unit is
 // one query row of one KV group with all of that group's query heads
 // (G <= 16 heads padded to the 16 rows of a 16x16 MFMA tile):
-//   * full layer (decode):  key list = the whole cache 0..Tkv-1; the scaled
-//     logits are also written (base 2, key-major: the group's heads of one
-//     key side by side) so that the importance scores can be formed once the
-//     log-sum-exp of every head is known;
+//   * full layer (decode):  key list = the whole cache 0..Tkv-1; each key's
+//     probability against the wave's running maximum (the P of the P.V
+//     product, key-major: the group's heads of one key side by side) is also
+//     written, with that maximum per 32-key step and head, so that the
+//     importance scores can be formed once the log-sum-exp of every head is
+//     known;
 //   * sparse layer (one query row per score row): key list = the row's top-K
 //     indices (global branch) followed by the W window keys (local branch);
 //     a split covers either global or window entries, never both.
@@ -27,6 +29,8 @@
 // the split kernel by its last-arriving workgroup would need a device-scope
 // fence per workgroup, which on this multi-die part writes back and
 // invalidates the die's L2 and costs far more than a second launch.)
+#include <type_traits>
+
 #include "hys_common.h"
 #include "hys_internal.h"
 
@@ -50,9 +54,11 @@ struct DecodeArgs {
   const int32_t* idx;
   int k_top, score_block, NB, window;
   int chunk, wchunk, nsplit, nsg;
-  float* logits;        // full decode: base-2 logits, key-major (see logit_slots)
-  int lgp;              // logit slots per key: G rounded up to 4, 8 or 16
-  int64_t lus;          // floats per unit of the logit scratch
+  void* probs;          // full decode: step probabilities, key-major (see prob_slots)
+  float* pmax;          // full decode: base-2 running maximum per (32-key step, head)
+  int lgp;              // slots per key: G rounded up to 4, 8 or 16
+  int64_t lus;          // elements per unit of probs
+  int64_t mus;          // floats per unit of pmax
   float* part_o;
   float* part_ml;
   GateRef gate;         // sparse: gate logits
@@ -61,6 +67,17 @@ struct DecodeArgs {
 };
 
 constexpr int kMaxSparseSplits = 64;
+
+// Element of the full layer's probability scratch.  The stored value is
+// 2^(s - m) for a base-2 logit s and the running maximum m of its step, so it
+// lies in [0, 1]: bf16 inputs keep it in fp16 scaled by 2^15 (11 significant
+// bits, more than the inputs' 8; only values below 2^-29 leave fp16's normal
+// range), fp32 inputs keep it in fp32.
+template <typename TR>
+using prob_t = std::conditional_t<TR::kBytes == 2, _Float16, float>;
+template <typename TR>
+constexpr float kProbShift = TR::kBytes == 2 ? 15.f : 0.f;
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 template <typename TR, int D>
 struct DecodeSmem {
@@ -165,9 +182,11 @@ __global__ __launch_bounds__(256, TR::kBytes == 4 ? 1 : 2) void decode_split_ker
 
   ST* vt = reinterpret_cast<ST*>(smem) + (size_t)wave * D * VP;
   int* kj = kj_s[wave];
-  // full layer: this unit's logits, key-major [key][lgp] (heads of a key
-  // contiguous, so a wave writes each step's logits as whole 1 KB runs)
-  float* lg_unit = FULL ? a.logits + (int64_t)unit * a.lus : nullptr;
+  // full layer: this unit's step probabilities, key-major [key][lgp] (heads
+  // of a key contiguous, so a wave writes each step's values as whole runs),
+  // and the running maximum of each (step, head)
+  prob_t<TR>* pr_unit = FULL ? static_cast<prob_t<TR>*>(a.probs) + (int64_t)unit * a.lus : nullptr;
+  float* pm_unit = FULL ? a.pmax + (int64_t)unit * a.mus : nullptr;
 
   // key index of list entry t (-1: past the list, negative index or after pos)
   auto key_at = [&](int t) -> int {
@@ -275,16 +294,6 @@ __global__ __launch_bounds__(256, TR::kBytes == 4 ? 1 : 2) void decode_split_ker
         s[kt][r] = (j >= 0) ? sacc[kt][r] * a.sl2 : kNegInf;
         mt = fmaxf(mt, s[kt][r]);
       }
-      if constexpr (FULL) {
-        // lane (head col, quad) holds keys 4*quad + r; after the transpose
-        // inside each lane quad it holds heads (col & ~3) + e of key
-        // 4*quad + (col & 3).  List entry t is key t in the full layer.
-        float w[4] = {s[kt][0], s[kt][1], s[kt][2], s[kt][3]};
-        quad_transpose4(w);
-        const int j = t0 + 16 * kt + 4 * quad + (col & 3);
-        if (col < a.lgp && j < t_end)
-          *reinterpret_cast<float4*>(lg_unit + (int64_t)j * a.lgp + (col & ~3)) = make_float4(w[0], w[1], w[2], w[3]);
-      }
     }
     mt = wave_max16x4(mt);
     const float m_new = fmaxf(m_run, mt);
@@ -301,6 +310,28 @@ __global__ __launch_bounds__(256, TR::kBytes == 4 ? 1 : 2) void decode_split_ker
       }
     l_run = l_run * alpha + ls;
     m_run = m_new;
+    if constexpr (FULL) {
+      // lane (head col, quad) holds keys 4*quad + r; after the transpose
+      // inside each lane quad it holds heads (col & ~3) + e of key
+      // 4*quad + (col & 3).  List entry t is key t in the full layer.
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        float w[4] = {p[kt][0], p[kt][1], p[kt][2], p[kt][3]};
+        quad_transpose4(w);
+        const int j = t0 + 16 * kt + 4 * quad + (col & 3);
+        if (col < a.lgp && j < t_end) {
+          prob_t<TR>* dst = pr_unit + (int64_t)j * a.lgp + (col & ~3);
+          if constexpr (TR::kBytes == 2) {
+            constexpr float sc = 1.f * (1 << (int)kProbShift<TR>);
+            *reinterpret_cast<f16x4_t*>(dst) =
+                __builtin_convertvector(f32x4_t{w[0] * sc, w[1] * sc, w[2] * sc, w[3] * sc}, f16x4_t);
+          } else {
+            *reinterpret_cast<float4*>(dst) = make_float4(w[0], w[1], w[2], w[3]);
+          }
+        }
+      }
+      if (quad == 0 && col < a.lgp) pm_unit[(int64_t)(t0 / kStep) * a.lgp + col] = mu;
+    }
     // rescale output rows (head 4*quad + r) by that head's alpha; nothing to
     // rescale on the wave's first step (o is zero; the sparse layer's waves
     // take one step each)
@@ -471,9 +502,11 @@ __global__ __launch_bounds__(D) void sparse_merge_kernel(DecodeArgs a) {
 struct FinishArgs {
   const float* part_o;
   const float* part_ml;
-  const float* logits;  // key-major [unit][key][lgp]
-  int lgp;              // logit slots per key (4, 8 or 16)
-  int64_t lus;          // floats per unit of the logit scratch
+  const void* probs;   // key-major [unit][key][lgp], see prob_t
+  const float* pmax;   // [unit][key / 32][lgp]
+  int lgp;             // slots per key (4, 8 or 16)
+  int64_t lus;         // elements per unit of probs
+  int64_t mus;         // floats per unit of pmax
   int nsplit, G, Hkv, Tkv, nchunk, units;
   void* out;
   float* lse;
@@ -516,41 +549,51 @@ __device__ __forceinline__ void unit_lse2(const float* pml, int nsplit, int G, f
 }
 
 // Importance scores of a wave's 256 keys (4 groups of 64) from the
-// key-major logits, Q = lgp / 4 lanes per key.  The wave reads the logits
-// as whole 1 KB runs: in run xi of a group, lane l holds heads 4*(l % Q) ..
-// +3 of key (64/Q)*xi + l/Q; a DPP sum over the key's Q lanes gives its S.
-// (The scratch holds nchunk * kScoreChunk keys per unit, so every run is in
-// it; keys past kv_len are read but not stored.)  The logit loads are issued
-// before the unit's LSE is formed (they do not depend on it).
-template <int Q>
-__device__ __forceinline__ void score_runs(const FinishArgs& f, int unit, int key0, float* lse_s) {
-  constexpr int NR = 4 * Q;   // 1 KB runs
+// key-major step probabilities, Q = lgp / 4 lanes per key.  The wave's keys
+// span 8 steps, so the factor 2^(m - lse2 - shift) that turns a stored value
+// into P takes 8 * lgp values: the wave forms them once into its LDS table
+// ct (0 for padding heads).  The wave reads the probabilities as whole runs
+// of 256 slots: in run xi of a group, lane l holds heads 4*(l % Q) .. +3 of
+// key (64/Q)*xi + l/Q; a DPP sum over the key's Q lanes gives its S.  (The
+// scratch holds nchunk * kScoreChunk keys per unit, so every run is in it;
+// keys past kv_len are read but not stored.)  All loads are issued before
+// the unit's LSE is formed (they do not depend on it).
+template <typename TR, int Q>
+__device__ __forceinline__ void score_runs(const FinishArgs& f, int unit, int key0, float* lse_s, float* ct) {
+  using PT = prob_t<TR>;
+  using PV = std::conditional_t<TR::kBytes == 2, f16x4_t, f32x4_t>;
+  constexpr int LG = 4 * Q;   // slots per key
+  constexpr int NR = 4 * Q;   // runs of 256 slots
   constexpr int KPR = 64 / Q; // keys per run
+  constexpr int NCT = 8 * LG; // (step, head) factors of the wave, <= 128
   const int lane = threadIdx.x & 63, hg = lane % Q;
-  const float* lg = f.logits + (int64_t)unit * f.lus + (int64_t)key0 * (4 * Q);
-  float4 x[NR];
+  const PT* pr = static_cast<const PT*>(f.probs) + (int64_t)unit * f.lus + (int64_t)key0 * LG;
+  const float* pm = f.pmax + (int64_t)unit * f.mus + (int64_t)(key0 / kStep) * LG;
+  PV x[NR];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) x[r] = *reinterpret_cast<const float4*>(lg + r * 256 + 4 * lane);
+  for (int r = 0; r < NR; ++r) x[r] = *reinterpret_cast<const PV*>(pr + r * 256 + 4 * lane);
+  float mv[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) mv[e] = (lane + 64 * e < NCT) ? pm[lane + 64 * e] : 0.f;
   unit_lse2(f.part_ml + (int64_t)unit * f.nsplit * f.G * 2, f.nsplit, f.G, lse_s);
-  float L[4];
-  bool hv[4];
+  // m <= lse2 for every stored key (the clamp only guards the steps whose
+  // keys are all masked, where m was taken as 0)
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    hv[e] = 4 * hg + e < f.G;
-    L[e] = hv[e] ? lse_s[4 * hg + e] : 0.f;
+  for (int e = 0; e < 2; ++e) {
+    const int t = lane + 64 * e, h = t % LG;
+    if (t < NCT) ct[t] = (h < f.G) ? fast_exp2(fminf(mv[e] - lse_s[h], 0.f) - kProbShift<TR>) : 0.f;
   }
+  wave_lds_sync();
   float* srow = f.scores + (int64_t)unit * f.Tkv;
 #pragma unroll
   for (int grp = 0; grp < 4; ++grp) {
     float mine = 0.f;
 #pragma unroll
     for (int xi = 0; xi < Q; ++xi) {
-      const float4 v = x[grp * Q + xi];
-      float p = 0.f;
-      p += hv[0] ? fast_exp2(v.x - L[0]) : 0.f;
-      p += hv[1] ? fast_exp2(v.y - L[1]) : 0.f;
-      p += hv[2] ? fast_exp2(v.z - L[2]) : 0.f;
-      p += hv[3] ? fast_exp2(v.w - L[3]) : 0.f;
+      const int r = grp * Q + xi;
+      const f32x4_t v = __builtin_convertvector(x[r], f32x4_t);
+      const float4 c = *reinterpret_cast<const float4*>(ct + ((r * KPR + lane / Q) / kStep) * LG + 4 * hg);
+      float p = v[0] * c.x + v[1] * c.y + v[2] * c.z + v[3] * c.w;
       if constexpr (Q >= 2) p += dpp_quad<0xB1>(p);
       if constexpr (Q == 4) p += dpp_quad<0x4E>(p);
       mine = (xi == hg) ? p : mine;
@@ -563,13 +606,15 @@ __device__ __forceinline__ void score_runs(const FinishArgs& f, int unit, int ke
 // Blocks [0, units*G): output row of one (unit, head): O = sum_s 2^(m_s - lse2) O_s,
 //   256 threads = D/4 float4 columns x NPH split phases, eight splits in flight.
 // Blocks [units*G, ...): importance scores of one chunk of kScoreChunk keys of a unit:
-//   S[b, g, 0, j] = sum over the group's heads of 2^(logit2[h, j] - lse2[h]).
+//   S[b, g, 0, j] = sum over the group's heads of 2^(logit2[h, j] - lse2[h]),
+//   formed as the stored 2^(logit2 - m) times 2^(m - lse2).
 template <typename TR, int D>
 __global__ __launch_bounds__(256) void decode_full_finish_kernel(FinishArgs f) {
   constexpr int DV = D / 4;      // float4 columns of a row
   constexpr int NPH = 256 / DV;  // split phases of the row merge
   __shared__ float lse_s[16];
   __shared__ __align__(16) float red[NPH][D];
+  __shared__ __align__(16) float ct_s[4][128];
   const int tid = threadIdx.x;
   const int nrow = f.units * f.G;
   const int Hq = f.Hkv * f.G;
@@ -578,13 +623,12 @@ __global__ __launch_bounds__(256) void decode_full_finish_kernel(FinishArgs f) {
     const int b = unit / f.Hkv, g = unit - b * f.Hkv;
     const float* pml = f.part_ml + (int64_t)unit * f.nsplit * f.G * 2;
     const float* po = f.part_o + (int64_t)unit * f.nsplit * f.G * D;
-    unit_lse2(pml, f.nsplit, f.G, lse_s);
-    const float l2 = lse_s[h];
     const int d4 = tid % DV, ph = tid / DV;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int base = ph; base < f.nsplit; base += NPH * 8) {
-      float m[8];
-      float4 o[8];
+    // batches of eight splits per thread (loading the first before the LSE
+    // is formed needs 40 more VGPRs and costs the score blocks occupancy)
+    float m[8];
+    float4 o[8];
+    auto load_batch = [&](int base) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int sp = base + NPH * u;
@@ -593,6 +637,12 @@ __global__ __launch_bounds__(256) void decode_full_finish_kernel(FinishArgs f) {
         o[u] = in ? *reinterpret_cast<const float4*>(po + ((int64_t)sp * f.G + h) * D + 4 * d4)
                   : make_float4(0.f, 0.f, 0.f, 0.f);
       }
+    };
+    unit_lse2(pml, f.nsplit, f.G, lse_s);
+    const float l2 = lse_s[h];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int base = ph; base < f.nsplit; base += NPH * 8) {
+      load_batch(base);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const float w = exp2f(m[u] - l2);
@@ -616,12 +666,13 @@ __global__ __launch_bounds__(256) void decode_full_finish_kernel(FinishArgs f) {
   const int bid = blockIdx.x - nrow;
   const int unit = bid / f.nchunk, c = bid - (bid / f.nchunk) * f.nchunk;
   const int key0 = c * kScoreChunk + (tid >> 6) * (kScoreChunk / 4);  // the wave's 256 keys
+  float* ct = ct_s[tid >> 6];
   if (f.lgp == 4)
-    score_runs<1>(f, unit, key0, lse_s);
+    score_runs<TR, 1>(f, unit, key0, lse_s, ct);
   else if (f.lgp == 8)
-    score_runs<2>(f, unit, key0, lse_s);
+    score_runs<TR, 2>(f, unit, key0, lse_s, ct);
   else
-    score_runs<4>(f, unit, key0, lse_s);
+    score_runs<TR, 4>(f, unit, key0, lse_s, ct);
 }
 
 DecodeArgs make_args(const Geom& g, const DecodePlan& p, const void* q, const void* k, const void* v) {
@@ -711,19 +762,23 @@ DecodePlan plan_sparse_rows(const Geom& g, int k_top, int window) {
   return p;
 }
 
-// Full-decode logit scratch: per unit (b, g), key-major rows of lgp slots
-// (the group's G heads, padded to 4, 8 or 16), for kv_len rounded up to
-// whole score chunks.
-static int logit_slots(const Geom& g) { return g.G <= 4 ? 4 : (g.G <= 8 ? 8 : 16); }
-static int64_t logit_unit_floats(const Geom& g) {
-  const int64_t keys = (int64_t)(g.Tkv + kScoreChunk - 1) / kScoreChunk * kScoreChunk;
-  return keys * logit_slots(g);
-}
+// Full-decode probability scratch: per unit (b, g), key-major rows of lgp
+// slots (the group's G heads, padded to 4, 8 or 16) of 2 bytes (bf16 inputs)
+// or 4, for kv_len rounded up to whole score chunks; and the running maxima,
+// lgp floats per 32-key step.
+static int prob_slots(const Geom& g) { return g.G <= 4 ? 4 : (g.G <= 8 ? 8 : 16); }
+static int64_t score_keys(const Geom& g) { return (int64_t)(g.Tkv + kScoreChunk - 1) / kScoreChunk * kScoreChunk; }
+static int64_t prob_unit_elems(const Geom& g) { return score_keys(g) * prob_slots(g); }
+static int64_t pmax_unit_floats(const Geom& g) { return score_keys(g) / kStep * prob_slots(g); }
+static size_t prob_elem_bytes(const Geom& g) { return g.dtype == 1 ? 2 : 4; }
 
 static size_t decode_ws(const Geom& g, const DecodePlan& p, bool full) {
   size_t n = align_up((size_t)p.units * p.nsplit * g.G * g.D * sizeof(float));
   n += align_up((size_t)p.units * p.nsplit * g.G * 2 * sizeof(float));
-  if (full) n += align_up((size_t)p.units * logit_unit_floats(g) * sizeof(float));
+  if (full) {
+    n += align_up((size_t)p.units * prob_unit_elems(g) * prob_elem_bytes(g));
+    n += align_up((size_t)p.units * pmax_unit_floats(g) * sizeof(float));
+  }
   return n;
 }
 
@@ -739,7 +794,11 @@ DecodeWs carve_decode_ws(const Geom& g, const DecodePlan& p, void* ws, bool full
   c += align_up((size_t)p.units * p.nsplit * g.G * g.D * sizeof(float));
   w.part_ml = reinterpret_cast<float*>(c);
   c += align_up((size_t)p.units * p.nsplit * g.G * 2 * sizeof(float));
-  if (full) w.logits = reinterpret_cast<float*>(c);
+  if (full) {
+    w.probs = c;
+    c += align_up((size_t)p.units * prob_unit_elems(g) * prob_elem_bytes(g));
+    w.pmax = reinterpret_cast<float*>(c);
+  }
   return w;
 }
 
@@ -748,17 +807,21 @@ hipError_t launch_full_decode(const Geom& g, const void* q, const void* k, const
   const DecodePlan p = plan_full_decode(g);
   const DecodeWs w = carve_decode_ws(g, p, ws, true);
   DecodeArgs a = make_args(g, p, q, k, v);
-  a.logits = w.logits;
-  a.lgp = logit_slots(g);
-  a.lus = logit_unit_floats(g);
+  a.probs = w.probs;
+  a.pmax = w.pmax;
+  a.lgp = prob_slots(g);
+  a.lus = prob_unit_elems(g);
+  a.mus = pmax_unit_floats(g);
   a.part_o = w.part_o;
   a.part_ml = w.part_ml;
   FinishArgs f{};
   f.part_o = w.part_o;
   f.part_ml = w.part_ml;
-  f.logits = w.logits;
-  f.lgp = logit_slots(g);
-  f.lus = logit_unit_floats(g);
+  f.probs = w.probs;
+  f.pmax = w.pmax;
+  f.lgp = prob_slots(g);
+  f.lus = prob_unit_elems(g);
+  f.mus = pmax_unit_floats(g);
   f.nsplit = p.nsplit;
   f.G = g.G;
   f.Hkv = g.Hkv;

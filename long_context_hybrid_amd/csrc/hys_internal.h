@@ -73,7 +73,9 @@ DecodePlan plan_sparse_rows(const Geom& g, int k_top, int window);
 struct DecodeWs {
   float* part_o;   // [units, nsplit, G, D]
   float* part_ml;  // [units, nsplit, G, 2]
-  float* logits;   // full only: base-2 scaled logits, [B, Hkv, keys, slots] (key-major)
+  void* probs;     // full only: probabilities against each step's running maximum,
+                   // [B, Hkv, keys, slots] (key-major), fp16 x 2^15 for bf16 inputs, fp32 otherwise
+  float* pmax;     // full only: that maximum (base 2), [B, Hkv, keys / 32, slots]
 };
 size_t decode_full_ws_bytes(const Geom& g);
 size_t decode_sparse_ws_bytes(const Geom& g, int k_top, int window);

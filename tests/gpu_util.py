@@ -11,8 +11,18 @@ from oracle import hysparse_oracle as orc
 # Tolerances on attention outputs: the stated max-abs bounds plus a relative
 # l2 bound (outputs here are often ~1e-2, where max-abs alone would accept 0).
 TOL = {"bf16": dict(max_abs=2e-2, rel_l2=1e-2), "f32": dict(max_abs=1e-4, rel_l2=1e-5)}
-# Score elements: |dS| <= 1e-4 |S| + 1e-7 (fp32 logits from the stored inputs).
+# Score elements: |dS| <= rtol |S| + 1e-7.  rtol = 1e-4 where the scores are
+# formed from fp32 logits of the stored inputs (prefill, and every fp32 path);
+# with bf16 inputs at one query row per call (the decode kernels) each head's
+# probability passes between the two kernels in fp16, unit roundoff 2^-11 =
+# 4.9e-4 relative per term, and a sum of positive terms keeps that relative
+# bound: rtol = 6e-4 there.
 S_RTOL, S_ATOL = 1e-4, 1e-7
+S_RTOL_F16 = 6e-4
+
+
+def score_rtol(dtype: str, q_len: int) -> float:
+    return S_RTOL_F16 if (dtype == "bf16" and q_len == 1) else S_RTOL
 
 
 def say(*a):
@@ -44,10 +54,10 @@ def assert_attn_close(gpu: torch.Tensor, ref: np.ndarray, dtype: str, what: str 
     return mx, rel
 
 
-def assert_scores_close(gpu: torch.Tensor, ref: np.ndarray, what: str = "scores"):
+def assert_scores_close(gpu: torch.Tensor, ref: np.ndarray, what: str = "scores", rtol: float = S_RTOL):
     g = host(gpu)
     r = np.asarray(ref, dtype=np.float64)
-    bad = np.abs(g - r) > S_RTOL * np.abs(r) + S_ATOL
+    bad = np.abs(g - r) > rtol * np.abs(r) + S_ATOL
     assert not bad.any(), f"{what}: {int(bad.sum())} elements out of tolerance, worst " \
                           f"{float(np.max(np.abs(g - r) / (np.abs(r) + 1e-30))):.3e}"
 
@@ -87,7 +97,8 @@ def check_hybrid(wl, inp, res, n_check_layers=None, blocks=None):
     assert_attn_close(res["out_full"], O_ref, wl.dtype, "O_full", mask=rows)
     S_gpu = host(res["scores"]).astype(np.float32)
     sel = tuple(np.array(units).T)
-    assert_scores_close(torch.from_numpy(S_gpu[sel]), S_ref[sel])
+    rtol = score_rtol(wl.dtype, Tq)
+    assert_scores_close(torch.from_numpy(S_gpu[sel]), S_ref[sel], rtol=rtol)
     idx_gpu = host(res["idx"])
     idx_from_gpu_S = orc.select_indices(S_gpu, Tq, Tkv, Sb, K, blocks=units)
     np.testing.assert_array_equal(idx_gpu[sel], idx_from_gpu_S[sel])
@@ -95,7 +106,7 @@ def check_hybrid(wl, inp, res, n_check_layers=None, blocks=None):
     differ = 0
     for (b, g, n) in units:
         c = orc.candidate_count(n, Tq, Tkv, Sb)
-        assert eps_valid(idx_gpu[b, g, n], S_ref[b, g, n], c)
+        assert eps_valid(idx_gpu[b, g, n], S_ref[b, g, n], c, eps_rel=rtol)
         differ += int(not np.array_equal(idx_gpu[b, g, n], idx_ref[b, g, n]))
     say(f"  index rows differing from the oracle's own selection: {differ}/{len(units)}")
     layers = range(len(inp.q_sparse)) if n_check_layers is None else range(n_check_layers)
