@@ -64,13 +64,18 @@ class Workload:
     n_kv_heads: int
     head_dim: int
     dtype: str            # "f32" or "bf16"
-    std: float            # standard deviation of Q, K, V
+    std: float            # standard deviation of Q, K (and V unless v_std is set)
     gate_dist: str        # "uniform2" (U(-2,2)) or "normal" (N(0,1))
     score_block: int
     k_top: int
     window: int
     n_sparse: int
     n_planted: int = 0
+    v_std: Optional[float] = None  # standard deviation of V (None: std)
+
+    @property
+    def value_std(self) -> float:
+        return self.std if self.v_std is None else self.v_std
 
     @property
     def group(self) -> int:
@@ -177,7 +182,7 @@ def make_inputs(wl: Workload, n_sparse: Optional[int] = None) -> Inputs:
             k64[b, planted[b]] = 32.0 * u[b][None, :, :]
     k = _store(k64, wl.dtype)
     del k64
-    v = _store(_normal(_rng(cid, T_V), (B, Tkv, Hkv, D), wl.std), wl.dtype)
+    v = _store(_normal(_rng(cid, T_V), (B, Tkv, Hkv, D), wl.value_std), wl.dtype)
     q_sparse = [_store(_normal(_rng(cid, T_QSPARSE, l), (B, Tq, Hq, D), wl.std), wl.dtype)
                 for l in range(N)]
     grng = _rng(cid, T_GATE)
@@ -224,17 +229,17 @@ def make_device_inputs(wl: Workload, device, n_sparse: Optional[int] = None):
     N = wl.n_sparse if n_sparse is None else n_sparse
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
 
-    def draw(shape, tensor_id, layer=0):
+    def draw(shape, tensor_id, layer=0, std=wl.std):
         seed = int(np.random.SeedSequence([wl.config_id, tensor_id, layer]).generate_state(1, np.uint64)[0] >> 1)
         g = torch.Generator(device=device)
         g.manual_seed(seed)
         x = torch.empty(shape, dtype=torch.float32, device=device)
-        x.normal_(0.0, wl.std, generator=g)
+        x.normal_(0.0, std, generator=g)
         return x.to(dt)
 
     q_full = draw((B, Tq, Hq, D), T_QFULL)
     k = draw((B, Tkv, Hkv, D), T_K)
-    v = draw((B, Tkv, Hkv, D), T_V)
+    v = draw((B, Tkv, Hkv, D), T_V, std=wl.value_std)
     q_sparse = [draw((B, Tq, Hq, D), T_QSPARSE, l) for l in range(N)]
     grng = _rng(wl.config_id, T_GATE)
     gates = grng.uniform(-2.0, 2.0, size=(N, Hq)) if wl.gate_dist == "uniform2" else grng.standard_normal(size=(N, Hq))
@@ -246,5 +251,5 @@ def own_window_kv(wl: Workload, layer: int = 0):
     position: [B, Tkv, Hkv, D] each, same distribution and rounding as k, v."""
     shape = (wl.batch, wl.kv_len, wl.n_kv_heads, wl.head_dim)
     kw = _store(_normal(_rng(wl.config_id, T_KWIN, layer), shape, wl.std), wl.dtype)
-    vw = _store(_normal(_rng(wl.config_id, T_VWIN, layer), shape, wl.std), wl.dtype)
+    vw = _store(_normal(_rng(wl.config_id, T_VWIN, layer), shape, wl.value_std), wl.dtype)
     return kw, vw

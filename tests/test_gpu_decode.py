@@ -26,6 +26,12 @@ DECODE_CASES = {
     "g16_window300": W["decode128k"].replace(batch=1, kv_len=2000, k_top=300, window=300, n_sparse=1,
                                              n_planted=8),
     "short_ctx": W["decode8k"].replace(batch=1, kv_len=20, k_top=64, window=128, n_sparse=1),
+    # logits with std 8 (Q, K std 2.83, V std 1): base-2 logits spread over
+    # about +-45, so most per-head probabilities fall below 2^-29 of their
+    # step's maximum, the range where the fp16 scratch of the decode full
+    # layer leaves the normal numbers (their absolute error stays below 2^-40)
+    "wide_logits": W["decode128k"].replace(batch=1, kv_len=5000, k_top=256, n_sparse=1, n_planted=8,
+                                           std=float(np.sqrt(8.0)), v_std=1.0),
     # fp32 with head_dim 128 (no other case covers this instantiation)
     "f32_d128_g4": W["tiny"].replace(batch=2, q_len=1, kv_len=1300, n_q_heads=8, n_kv_heads=2, head_dim=128,
                                      std=1.0 / np.sqrt(128.0), k_top=200, window=64, n_sparse=2),
