@@ -96,6 +96,9 @@ enum { HYS_OP_FULL = 0, HYS_OP_TOPK = 1, HYS_OP_SPARSE = 2, HYS_OP_HYBRID = 3 };
  *   out          [B, Tq, Hq, D] desc.dtype, written.
  *   lse          [B, Hq, Tq] float32 log-sum-exp of the scaled logits, or NULL.
  *   scores       [B, Hkv, NB, Tkv] float32, written in full (0 past last(n)).
+ *                Formed from fp32 logits; with bf16 inputs and Tq == 1 each
+ *                head's probability passes through an fp16 intermediate, so
+ *                a score's relative error there is at most about 2^-11.
  *   ws/ws_bytes  workspace of at least hysparse_workspace_bytes(HYS_OP_FULL, ...).
  */
 hys_status hysparse_full_attn_scores(const hys_attn_desc* desc, const void* q, const void* k,
