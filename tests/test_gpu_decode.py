@@ -32,6 +32,11 @@ DECODE_CASES = {
     # layer leaves the normal numbers (their absolute error stays below 2^-40)
     "wide_logits": W["decode128k"].replace(batch=1, kv_len=5000, k_top=256, n_sparse=1, n_planted=8,
                                            std=float(np.sqrt(8.0)), v_std=1.0),
+    # kv_len on and one past the 1024-key score chunks and 32-key steps of
+    # the decode full layer's probability scratch
+    "chunk_exact": W["decode128k"].replace(batch=1, kv_len=2048, k_top=256, n_sparse=1, n_planted=4),
+    "chunk_plus1": W["decode128k"].replace(batch=1, kv_len=1025, k_top=128, n_sparse=1, n_planted=4),
+    "step_plus1_g8": W["decode8k"].replace(batch=2, kv_len=33, k_top=16, window=8, n_sparse=1),
     # fp32 with head_dim 128 (no other case covers this instantiation)
     "f32_d128_g4": W["tiny"].replace(batch=2, q_len=1, kv_len=1300, n_q_heads=8, n_kv_heads=2, head_dim=128,
                                      std=1.0 / np.sqrt(128.0), k_top=200, window=64, n_sparse=2),
