@@ -744,6 +744,14 @@ DecodePlan plan_full_decode(const Geom& g) {
 #define HYS_SPARSE_GSPLITS 48
 #endif
 
+// Split-kernel workgroups resident at once (two per CU at its register
+// budget, 256 CUs).  When many units fill the chip, fewer and longer global
+// splits keep every workgroup in the first round, its waves pipelining their
+// steps, instead of a second round of single-step waves (decode, batch 16,
+// 8K context: 23.7 -> 21.8 us per sparse layer; batch 4 at 128K keeps its 16
+// global splits).
+constexpr int kSparseResidentWGs = 512;
+
 DecodePlan plan_sparse_rows(const Geom& g, int k_top, int window) {
   // at most HYS_SPARSE_GSPLITS (<= 48) global and 16 window splits
   // (kMaxSparseSplits merge weights)
@@ -751,14 +759,18 @@ DecodePlan plan_sparse_rows(const Geom& g, int k_top, int window) {
   DecodePlan p{};
   const int quantum = kWaves * kStep;
   p.units = g.B * g.Hkv * g.Tq;
-  int cg = (k_top + HYS_SPARSE_GSPLITS - 1) / HYS_SPARSE_GSPLITS;
-  cg = (cg + quantum - 1) / quantum * quantum;
-  p.chunk = cg;
   int cw = (window + 15) / 16;
   cw = (cw + quantum - 1) / quantum * quantum;
   p.wchunk = cw;
+  const int nw = (window + cw - 1) / cw;
+  int gs = HYS_SPARSE_GSPLITS;
+  const int fit = kSparseResidentWGs / p.units - nw;
+  if (fit < gs) gs = fit < 1 ? 1 : fit;
+  int cg = (k_top + gs - 1) / gs;
+  cg = (cg + quantum - 1) / quantum * quantum;
+  p.chunk = cg;
   p.nsg = (k_top + cg - 1) / cg;
-  p.nsplit = p.nsg + (window + cw - 1) / cw;
+  p.nsplit = p.nsg + nw;
   return p;
 }
 
