@@ -96,9 +96,11 @@ enum { HYS_OP_FULL = 0, HYS_OP_TOPK = 1, HYS_OP_SPARSE = 2, HYS_OP_HYBRID = 3 };
  *   out          [B, Tq, Hq, D] desc.dtype, written.
  *   lse          [B, Hq, Tq] float32 log-sum-exp of the scaled logits, or NULL.
  *   scores       [B, Hkv, NB, Tkv] float32, written in full (0 past last(n)).
- *                Formed from fp32 logits; with bf16 inputs and Tq == 1 each
- *                head's probability passes through an fp16 intermediate, so
- *                a score's relative error there is at most about 2^-11.
+ *                Formed from fp32 logits of the stored inputs.  With
+ *                q_len 1 each head's probability passes between two kernels
+ *                as an fp32 value (fp32 inputs) or an fp32 value rounded to
+ *                16 significant bits (bf16 inputs), a relative error of at
+ *                most 2^-16 per term.
  *   ws/ws_bytes  workspace of at least hysparse_workspace_bytes(HYS_OP_FULL, ...).
  */
 hys_status hysparse_full_attn_scores(const hys_attn_desc* desc, const void* q, const void* k,
@@ -118,7 +120,12 @@ hys_status hysparse_full_attn_scores(const hys_attn_desc* desc, const void* q, c
  *   k            K >= 1.
  *   idx          int32 [n_rows, k], written: ascending indices, -1 padded.
  *   ws/ws_bytes  at least hysparse_topk_workspace_bytes(n_rows, row_len, k)
- *                bytes (currently 0: ws may be NULL).
+ *                bytes.  That size is 0 (ws may be NULL) unless there are
+ *                fewer than 256 rows longer than 12288 keys: such rows are
+ *                filtered in parts by several workgroups each, whose
+ *                candidates go to the workspace (16 rows of 131072 keys:
+ *                about 12.6 MB).  A NULL or smaller ws then returns
+ *                HYS_ERR_WORKSPACE.
  * Results are bit-exact functions of the input bits (no atomics-order effects).
  */
 hys_status hysparse_topk(const float* scores, int64_t n_rows, int32_t row_len, int64_t row_stride,

@@ -68,16 +68,52 @@ struct DecodeArgs {
 
 constexpr int kMaxSparseSplits = 64;
 
-// Element of the full layer's probability scratch.  The stored value is
-// 2^(s - m) for a base-2 logit s and the running maximum m of its step, so it
-// lies in [0, 1]: bf16 inputs keep it in fp16 scaled by 2^15 (11 significant
-// bits, more than the inputs' 8; only values below 2^-29 leave fp16's normal
-// range), fp32 inputs keep it in fp32.
+// Element format of the full layer's probability scratch.  The stored value
+// is 2^(s - m) for a base-2 logit s and the running maximum m of its step, so
+// it lies in [0, 1].  fp32 inputs keep it in fp32.  bf16 inputs keep it in
+// three bytes: the fp32 value rounded (to nearest, ties to even) to its upper
+// 24 bits, i.e. sign, exponent and 15 stored mantissa bits, a relative error
+// of at most 2^-16 per value.  Four consecutive slots (four heads of one key)
+// always travel together, in three dwords: the upper three bytes of each of
+// the first three values, with the fourth value's three bytes in their low
+// bytes.
 template <typename TR>
-using prob_t = std::conditional_t<TR::kBytes == 2, _Float16, float>;
-template <typename TR>
-constexpr float kProbShift = TR::kBytes == 2 ? 15.f : 0.f;
-typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+struct ProbFmt;
+template <>
+struct ProbFmt<F32> {
+  static constexpr int kSlotBytes = 4;
+  __device__ static __forceinline__ void store4(unsigned char* p, const float (&w)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(w[0], w[1], w[2], w[3]);
+  }
+  __device__ static __forceinline__ f32x4_t load4(const unsigned char* p) {
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    return f32x4_t{x.x, x.y, x.z, x.w};
+  }
+};
+template <>
+struct ProbFmt<BF16> {
+  static constexpr int kSlotBytes = 3;
+  struct __attribute__((aligned(4))) pack_t {
+    uint32_t x, y, z;
+  };
+  __device__ static __forceinline__ uint32_t round24(float v) {
+    const uint32_t u = __float_as_uint(v);
+    return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+  }
+  __device__ static __forceinline__ void store4(unsigned char* p, const float (&w)[4]) {
+    const uint32_t r3 = round24(w[3]);
+    pack_t t;
+    t.x = (round24(w[0]) << 8) | (r3 & 0xFFu);
+    t.y = (round24(w[1]) << 8) | ((r3 >> 8) & 0xFFu);
+    t.z = (round24(w[2]) << 8) | (r3 >> 16);
+    *reinterpret_cast<pack_t*>(p) = t;
+  }
+  __device__ static __forceinline__ f32x4_t unpack(const pack_t& t) {
+    const uint32_t v3 = ((t.x & 0xFFu) << 8) | ((t.y & 0xFFu) << 16) | (t.z << 24);
+    return f32x4_t{__uint_as_float(t.x & ~0xFFu), __uint_as_float(t.y & ~0xFFu), __uint_as_float(t.z & ~0xFFu),
+                   __uint_as_float(v3)};
+  }
+};
 
 template <typename TR, int D>
 struct DecodeSmem {
@@ -185,7 +221,8 @@ __global__ __launch_bounds__(256, TR::kBytes == 4 ? 1 : 2) void decode_split_ker
   // full layer: this unit's step probabilities, key-major [key][lgp] (heads
   // of a key contiguous, so a wave writes each step's values as whole runs),
   // and the running maximum of each (step, head)
-  prob_t<TR>* pr_unit = FULL ? static_cast<prob_t<TR>*>(a.probs) + (int64_t)unit * a.lus : nullptr;
+  unsigned char* pr_unit =
+      FULL ? static_cast<unsigned char*>(a.probs) + (int64_t)unit * a.lus * ProbFmt<TR>::kSlotBytes : nullptr;
   float* pm_unit = FULL ? a.pmax + (int64_t)unit * a.mus : nullptr;
 
   // key index of list entry t (-1: past the list, negative index or after pos)
@@ -319,16 +356,8 @@ __global__ __launch_bounds__(256, TR::kBytes == 4 ? 1 : 2) void decode_split_ker
         float w[4] = {p[kt][0], p[kt][1], p[kt][2], p[kt][3]};
         quad_transpose4(w);
         const int j = t0 + 16 * kt + 4 * quad + (col & 3);
-        if (col < a.lgp && j < t_end) {
-          prob_t<TR>* dst = pr_unit + (int64_t)j * a.lgp + (col & ~3);
-          if constexpr (TR::kBytes == 2) {
-            constexpr float sc = 1.f * (1 << (int)kProbShift<TR>);
-            *reinterpret_cast<f16x4_t*>(dst) =
-                __builtin_convertvector(f32x4_t{w[0] * sc, w[1] * sc, w[2] * sc, w[3] * sc}, f16x4_t);
-          } else {
-            *reinterpret_cast<float4*>(dst) = make_float4(w[0], w[1], w[2], w[3]);
-          }
-        }
+        if (col < a.lgp && j < t_end)
+          ProbFmt<TR>::store4(pr_unit + ((int64_t)j * a.lgp + (col & ~3)) * ProbFmt<TR>::kSlotBytes, w);
       }
       if (quad == 0 && col < a.lgp) pm_unit[(int64_t)(t0 / kStep) * a.lgp + col] = mu;
     }
@@ -502,7 +531,7 @@ __global__ __launch_bounds__(D) void sparse_merge_kernel(DecodeArgs a) {
 struct FinishArgs {
   const float* part_o;
   const float* part_ml;
-  const void* probs;   // key-major [unit][key][lgp], see prob_t
+  const void* probs;   // key-major [unit][key][lgp], see ProbFmt
   const float* pmax;   // [unit][key / 32][lgp]
   int lgp;             // slots per key (4, 8 or 16)
   int64_t lus;         // elements per unit of probs
@@ -560,18 +589,19 @@ __device__ __forceinline__ void unit_lse2(const float* pml, int nsplit, int G, f
 // the unit's LSE is formed (they do not depend on it).
 template <typename TR, int Q>
 __device__ __forceinline__ void score_runs(const FinishArgs& f, int unit, int key0, float* lse_s, float* ct) {
-  using PT = prob_t<TR>;
-  using PV = std::conditional_t<TR::kBytes == 2, f16x4_t, f32x4_t>;
+  using PF = ProbFmt<TR>;
+  constexpr int SB = PF::kSlotBytes;
+  using PV = std::conditional_t<SB == 3, typename ProbFmt<BF16>::pack_t, float4>;
   constexpr int LG = 4 * Q;   // slots per key
   constexpr int NR = 4 * Q;   // runs of 256 slots
   constexpr int KPR = 64 / Q; // keys per run
   constexpr int NCT = 8 * LG; // (step, head) factors of the wave, <= 128
   const int lane = threadIdx.x & 63, hg = lane % Q;
-  const PT* pr = static_cast<const PT*>(f.probs) + (int64_t)unit * f.lus + (int64_t)key0 * LG;
+  const unsigned char* pr = static_cast<const unsigned char*>(f.probs) + ((int64_t)unit * f.lus + (int64_t)key0 * LG) * SB;
   const float* pm = f.pmax + (int64_t)unit * f.mus + (int64_t)(key0 / kStep) * LG;
   PV x[NR];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) x[r] = *reinterpret_cast<const PV*>(pr + r * 256 + 4 * lane);
+  for (int r = 0; r < NR; ++r) x[r] = *reinterpret_cast<const PV*>(pr + (r * 256 + 4 * lane) * SB);
   float mv[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) mv[e] = (lane + 64 * e < NCT) ? pm[lane + 64 * e] : 0.f;
@@ -581,7 +611,7 @@ __device__ __forceinline__ void score_runs(const FinishArgs& f, int unit, int ke
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int t = lane + 64 * e, h = t % LG;
-    if (t < NCT) ct[t] = (h < f.G) ? fast_exp2(fminf(mv[e] - lse_s[h], 0.f) - kProbShift<TR>) : 0.f;
+    if (t < NCT) ct[t] = (h < f.G) ? fast_exp2(fminf(mv[e] - lse_s[h], 0.f)) : 0.f;
   }
   wave_lds_sync();
   float* srow = f.scores + (int64_t)unit * f.Tkv;
@@ -591,7 +621,11 @@ __device__ __forceinline__ void score_runs(const FinishArgs& f, int unit, int ke
 #pragma unroll
     for (int xi = 0; xi < Q; ++xi) {
       const int r = grp * Q + xi;
-      const f32x4_t v = __builtin_convertvector(x[r], f32x4_t);
+      f32x4_t v;
+      if constexpr (SB == 3)
+        v = PF::unpack(x[r]);
+      else
+        v = f32x4_t{x[r].x, x[r].y, x[r].z, x[r].w};
       const float4 c = *reinterpret_cast<const float4*>(ct + ((r * KPR + lane / Q) / kStep) * LG + 4 * hg);
       float p = v[0] * c.x + v[1] * c.y + v[2] * c.z + v[3] * c.w;
       if constexpr (Q >= 2) p += dpp_quad<0xB1>(p);
@@ -785,7 +819,7 @@ static int prob_slots(const Geom& g) { return g.G <= 4 ? 4 : (g.G <= 8 ? 8 : 16)
 static int64_t score_keys(const Geom& g) { return (int64_t)(g.Tkv + kScoreChunk - 1) / kScoreChunk * kScoreChunk; }
 static int64_t prob_unit_elems(const Geom& g) { return score_keys(g) * prob_slots(g); }
 static int64_t pmax_unit_floats(const Geom& g) { return score_keys(g) / kStep * prob_slots(g); }
-static size_t prob_elem_bytes(const Geom& g) { return g.dtype == 1 ? 2 : 4; }
+static size_t prob_elem_bytes(const Geom& g) { return g.dtype == 1 ? 3 : 4; }
 
 static size_t decode_ws(const Geom& g, const DecodePlan& p, bool full) {
   size_t n = align_up((size_t)p.units * p.nsplit * g.G * g.D * sizeof(float));

@@ -74,7 +74,7 @@ struct DecodeWs {
   float* part_o;   // [units, nsplit, G, D]
   float* part_ml;  // [units, nsplit, G, 2]
   void* probs;     // full only: probabilities against each step's running maximum,
-                   // [B, Hkv, keys, slots] (key-major), fp16 x 2^15 for bf16 inputs, fp32 otherwise
+                   // [B, Hkv, keys, slots] (key-major), 3-byte rounded fp32 for bf16 inputs, fp32 otherwise
   float* pmax;     // full only: that maximum (base 2), [B, Hkv, keys / 32, slots]
 };
 size_t decode_full_ws_bytes(const Geom& g);

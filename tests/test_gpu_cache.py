@@ -7,7 +7,7 @@ import torch
 from long_context_hybrid_amd import hysparse as hy
 from long_context_hybrid_amd import inputs as gen
 from oracle import hysparse_oracle as orc
-from tests.gpu_util import assert_attn_close, assert_scores_close, dev_tensor, eps_valid, host, say, score_rtol
+from tests.gpu_util import assert_attn_close, assert_scores_close, dev_tensor, eps_valid, host, say
 
 pytestmark = pytest.mark.gpu
 W = gen.WORKLOADS
@@ -80,11 +80,11 @@ def test_multi_step_decode_recomputes_indices_each_step():
     for t in range(T):
         L = L0 + t + 1
         assert_attn_close(torch.from_numpy(outs_full[t]), O_ref[:, t:t + 1], dt, f"O_full step {t}")
-        assert_scores_close(torch.from_numpy(scores[t][:, :, 0]), S_ref[:, :, t, :L], rtol=score_rtol(dt, 1))
+        assert_scores_close(torch.from_numpy(scores[t][:, :, 0]), S_ref[:, :, t, :L])
         for b in range(B):
             for g in range(Hkv):
                 np.testing.assert_array_equal(idxs[t][b, g, 0], orc.topk_row(scores[t][b, g, 0], L, K))
-                assert eps_valid(idxs[t][b, g, 0], S_ref[b, g, t], L, eps_rel=score_rtol(dt, 1))
+                assert eps_valid(idxs[t][b, g, 0], S_ref[b, g, t], L)
         idx_all[:, :, t] = idxs[t][:, :, 0]
     for l in range(len(qs)):
         ref = orc.sparse_layer(inp.q_sparse[l], inp.k, inp.v, idx_all, 1, wl.window, inp.gate_logits[l])

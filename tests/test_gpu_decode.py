@@ -10,8 +10,7 @@ import torch
 from long_context_hybrid_amd import hysparse as hy
 from long_context_hybrid_amd import inputs as gen
 from oracle import hysparse_oracle as orc
-from tests.gpu_util import (assert_attn_close, assert_scores_close, check_hybrid, dev_tensor, host, say,
-                             score_rtol)
+from tests.gpu_util import assert_attn_close, assert_scores_close, check_hybrid, dev_tensor, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -141,7 +140,7 @@ def test_full_decode_matches_oracle(name):
     O_ref, LSE_ref, S_ref = orc.full_layer(inp.q_full, inp.k, inp.v, wl.score_block)
     assert_attn_close(out, O_ref, wl.dtype, "O_full")
     np.testing.assert_allclose(host(lse), LSE_ref, rtol=0, atol=2e-5 if wl.dtype == "bf16" else 1e-5)
-    assert_scores_close(S, S_ref, rtol=score_rtol(wl.dtype, wl.q_len))
+    assert_scores_close(S, S_ref)
 
 
 # -------------------------------------------------------------- sparse decode
@@ -181,13 +180,16 @@ def test_hybrid_block_decode(name):
                 assert set(inp.planted[b].tolist()) <= set(idx_gpu[b, g, 0].tolist())
 
 
-def test_hybrid_block_deterministic():
-    wl = DECODE_CASES["decode8k_small"]
-    say("determinism decode8k_small x5")
+@pytest.mark.parametrize("name", ["decode8k_small", "g16_window300"])
+def test_hybrid_block_deterministic(name):
+    """Twenty runs of the same block give bit-identical outputs, scores and
+    indices (no atomics-order or scheduling effects)."""
+    wl = DECODE_CASES[name]
+    say(f"determinism {name} x20")
     inp = _inputs(wl)
     qf, k, v, qs, gates = _dev(inp)
     first = None
-    for _ in range(5):
+    for _ in range(20):
         res = hy.hysparse_hybrid_block(qf, k, v, qs, gates, wl.k_top, wl.score_block, wl.window)
         torch.cuda.synchronize()
         cur = [res["out_full"].clone(), res["scores"].clone(), res["idx"].clone()] + [o.clone() for o in res["out"]]
@@ -200,6 +202,13 @@ def test_hybrid_block_deterministic():
 
 # ------------------------------------------------------------- full sizes
 
+# agreement of the GPU's index rows (the top-K of its own scores) with the
+# oracle's selection on the oracle's scores, at full size: every row is
+# eps-valid; rows can differ only where candidates' scores lie within the
+# score tolerance of each other at the K-th place
+MIN_MEAN_IOU = {"decode8k": 0.99, "decode128k": 0.99}
+
+
 @pytest.mark.parametrize("name", ["decode8k", "decode128k"])
 def test_hybrid_block_full_size(name):
     """The real decode workloads (two of their sparse layers checked)."""
@@ -210,7 +219,34 @@ def test_hybrid_block_full_size(name):
     res = hy.hysparse_hybrid_block(qf, k, v, qs, gates, wl.k_top, wl.score_block, wl.window)
     torch.cuda.synchronize()
     _, idx_gpu = check_hybrid(wl, inp, res)
+    agree = check_hybrid.last_agreement
+    say(f"  RECORD index agreement {name}: {agree}")
+    assert agree["mean_iou"] >= MIN_MEAN_IOU[name]
     if inp.planted is not None:
         for b in range(wl.batch):
             for g in range(wl.n_kv_heads):
                 assert set(inp.planted[b].tolist()) <= set(idx_gpu[b, g, 0].tolist())
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode8k"])
+def test_topk_on_oracle_scores_bit_exact(name):
+    """The GPU top-K fed the oracle's own fp32 scores of a workload selects
+    exactly the oracle's index rows (the tiny workload: 256 per-query rows;
+    the 8K decode workload at full size, whose near-uniform scores put many
+    exactly equal fp32 values at the K-th place)."""
+    wl = W[name]
+    say(f"topk on oracle scores {name}")
+    inp = _inputs(wl)
+    _, _, S_ref = orc.full_layer(inp.q_full, inp.k, inp.v, wl.score_block)
+    S32 = S_ref.astype(np.float32)
+    B, Hkv, NB, Tkv = S32.shape
+    ref = orc.select_indices(S32, wl.q_len, wl.kv_len, wl.score_block, wl.k_top)
+    rows = np.array([orc.candidate_count(n, wl.q_len, wl.kv_len, wl.score_block)
+                     for b in range(B) for g in range(Hkv) for n in range(NB)], np.int32)
+    kth = [np.sort(S32.reshape(-1, Tkv)[r, :rows[r]])[::-1][min(wl.k_top, rows[r]) - 1] for r in range(len(rows))]
+    ties = [int((S32.reshape(-1, Tkv)[r, :rows[r]] == kth[r]).sum()) for r in range(len(rows))]
+    say(f"  candidates equal to the K-th score per row: mean {np.mean(ties):.1f}, max {max(ties)}")
+    got = hy.hysparse_topk(torch.from_numpy(S32.reshape(-1, Tkv)).cuda(), wl.k_top,
+                           valid_len=torch.from_numpy(rows).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(got).reshape(ref.shape), ref)

@@ -122,12 +122,13 @@ def test_hybrid_block_prefill(name):
 
 
 def test_hybrid_prefill_deterministic():
+    """Twenty runs of the same prefill block give bit-identical results."""
     wl = PREFILL_CASES["prefill32k_small"]
-    say("determinism prefill32k_small x3")
+    say("determinism prefill32k_small x20")
     inp = gen.make_inputs(wl)
     qf, k, v, qs, gates = _dev(inp)
     first = None
-    for _ in range(3):
+    for _ in range(20):
         res = hy.hysparse_hybrid_block(qf, k, v, qs, gates, wl.k_top, wl.score_block, wl.window)
         torch.cuda.synchronize()
         cur = [res["out_full"].clone(), res["scores"].clone(), res["idx"].clone()] + [o.clone() for o in res["out"]]
