@@ -1,18 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of the HySparse hybrid-block hot path on one MI355X.
 
-One step = one hybrid block over one batch of synthetic input: the full
-attention layer with score emission, the top-K select, then every sparse
-layer (all of them reading the full layer's K/V and indices).  Default
-workload: decode at 128K context (B 4, Hq 64 / Hkv 4, D 128, bf16, K 2048,
-window 128, 9 sparse layers); ``value`` is decoded tokens per second of the
-whole block, inputs resident in HBM.
+Default workload: decode at 128K context (B 4, Hq 64 / Hkv 4, D 128, bf16,
+K 2048, window 128, 9 sparse layers).  ``value`` is the sparse layer's decode
+tokens per second (batch / time of one sparse layer), measured cold: a 1 GiB
+write evicts the caches before each timed layer, and HIP events on the
+library's stream bracket the layer (its split and merge kernels).  The line
+also carries the same layer warm (layers back to back, rows partly served
+from the last-level cache), its per-kernel cold durations, the bandwidth a
+launch of the same size reaches with nothing else to do (a streaming read of
+the layer's bytes, a gather of its rows), the whole hybrid block (full layer
++ top-K + all sparse layers: the K timed steps), and the 128K prefill full
+layer (both sweeps) against the bf16 MFMA peak.
 
-Prints one JSON line.  Per-kernel durations come from HIP events that the
-library records around each kernel on its launch stream (a second pass over
-the same steps, so the timed pass carries no extra events).  The
-``cpu_baseline`` leg times the CPU oracle on a bounded sample of the same
-workload.
+Inputs are resident in HBM before any timed region.  Per-kernel durations
+come from HIP events that the library records around each kernel on its
+launch stream (separate passes, so the timed steps carry no extra events).
+The ``cpu_baseline`` leg times the CPU oracle on a bounded sample of the same
+workload.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -46,36 +51,17 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times): the reference for HBM counters")
+    ap.add_argument("--layer-reps", type=int, default=50, help="cold / warm sparse-layer repetitions")
+    ap.add_argument("--prefill128k", type=int, default=1,
+                    help="decode128k: also time the 128K prefill full layer (0 skips it)")
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic.json")
-
-
-def kernel_source_hash(kernel: str) -> str:
-    """Hash of the HIP source that defines a kernel (traffic figures are only
-    reported while the kernel is unchanged since its counters were taken)."""
-    import hashlib
-    src = {"full_decode_split": "decode.hip", "sparse_decode": "decode.hip", "full_prefill_fwd": "prefill.hip",
-           "full_prefill_scores": "prefill.hip", "sparse_prefill": "prefill.hip", "topk": "topk.hip"}.get(kernel)
-    if src is None:
-        return ""
-    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_hybrid_amd", "csrc")
-    h = hashlib.sha256()
-    for f in (src, "hys_common.h", "attn_tile.h"):
-        h.update(open(os.path.join(root, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from the committed counter runs, or None."""
-    try:
-        rec = json.load(open(TRAFFIC_FILE))[workload][kernel]
-    except (OSError, KeyError, ValueError):
-        return None
-    if rec.get("source_hash") != kernel_source_hash(kernel):
-        return None
-    return rec.get("bytes_per_launch")
+    """HBM bytes per launch from the committed counter runs (profiles/
+    hbm_traffic.json), or None once the kernel's source has changed."""
+    from long_context_hybrid_amd.profiling import recorded_traffic
+    return recorded_traffic(workload, kernel)
 
 
 def copy_calibration(mib: int):
@@ -142,31 +128,219 @@ def full_split_bytes(wl):
 
 
 def cpu_baseline(wl, inp, budget_s: float):
-    """Time the oracle on (b, g) units of the block until the budget is spent,
-    then scale to the whole block."""
+    """Time the oracle on the same inputs, within a bounded budget.
+
+    Decode workloads: the oracle's sparse layer (the metric's subject) over
+    every (batch, KV-group) unit of the workload, repeated over the layers'
+    queries until half the budget is spent, with indices from the oracle's
+    own full layer and top-K (computed before the timed part); then the whole
+    block (full layer, top-K, every sparse layer) on (batch, KV-group) units
+    for the other half, scaled to the block.  Prefill workloads: the block on
+    (batch, KV-group) units, scaled."""
     from threadpoolctl import threadpool_info
     from oracle import hysparse_oracle as orc
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     units = [(b, g) for b in range(wl.batch) for g in range(wl.n_kv_heads)]
     NB = wl.n_blocks
+    res = {"unit": "tokens/s", "cores": int(threads), "kind": "oracle"}
+    block_budget = budget_s
+    if wl.q_len == 1:
+        idx = {}
+        for (b, g) in units:
+            _, _, s = orc.full_layer_block(inp.q_full, inp.k, inp.v, b, g, 0, 1)
+            idx[b, g] = orc.topk_row(s.astype(np.float32), wl.kv_len, wl.k_top)
+        layers = 0
+        t0 = time.perf_counter()
+        while True:
+            l = layers % wl.n_sparse
+            for (b, g) in units:
+                orc.sparse_layer_block(inp.q_sparse[l], inp.k, inp.v, idx[b, g], b, g, 0, 1, wl.window,
+                                       inp.gate_logits[l])
+            layers += 1
+            if time.perf_counter() - t0 > budget_s / 2:
+                break
+        el = time.perf_counter() - t0
+        res["value"] = wl.batch * layers / el
+        res["sample"] = (f"{layers} whole sparse layers (all {len(units)} (batch, KV-group) units, K {wl.k_top}, "
+                         f"window {wl.window}) in {el:.1f} s, on the oracle's own indices")
+        block_budget = budget_s / 2
     done = 0
     t0 = time.perf_counter()
     for (b, g) in units:
         for n in range(NB):
             _, _, s = orc.full_layer_block(inp.q_full, inp.k, inp.v, b, g, n, wl.score_block)
             c = orc.candidate_count(n, wl.q_len, wl.kv_len, wl.score_block)
-            idx = orc.topk_row(s.astype(np.float32), c, wl.k_top)
+            ix = orc.topk_row(s.astype(np.float32), c, wl.k_top)
             for l in range(wl.n_sparse):
-                orc.sparse_layer_block(inp.q_sparse[l], inp.k, inp.v, idx, b, g, n, wl.score_block, wl.window,
+                orc.sparse_layer_block(inp.q_sparse[l], inp.k, inp.v, ix, b, g, n, wl.score_block, wl.window,
                                        inp.gate_logits[l])
         done += 1
-        if time.perf_counter() - t0 > budget_s:
+        if time.perf_counter() - t0 > block_budget:
             break
     el = time.perf_counter() - t0
-    step_s = el * len(units) / done
-    return {"value": wl.batch * wl.q_len / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {len(units)} (batch, KV-group) units of one block (full layer, top-K, "
-                      f"{wl.n_sparse} sparse layers) in {el:.1f} s, scaled to the whole block"}
+    block_tps = wl.batch * wl.q_len / (el * len(units) / done)
+    res["block_tokens_per_s"] = block_tps
+    res["block_sample"] = (f"{done} of {len(units)} (batch, KV-group) units of one block (full layer, top-K, "
+                           f"{wl.n_sparse} sparse layers) in {el:.1f} s, scaled to the whole block")
+    if wl.q_len != 1:
+        res["value"] = block_tps
+        res["sample"] = res["block_sample"]
+    return res
+
+
+def events_ms(pairs):
+    return np.array([a.elapsed_time(b) for a, b in pairs])
+
+
+def timed_reps(torch, fn, reps, before=None):
+    """Run fn reps times, each bracketed by HIP events on the current stream
+    (the stream the library launches on); before() runs ahead of each
+    bracket.  Returns the per-rep durations in ms."""
+    pairs = []
+    for r in range(reps):
+        if before is not None:
+            before(r)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn(r)
+        e1.record()
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    return events_ms(pairs)
+
+
+def traced(hy, torch, fn, reps, before=None):
+    """Per-kernel durations (us) of fn over reps runs from the library's event
+    trace: {name: [durations]}."""
+    trace = hy.KernelTrace(capacity_kernels=64 * (reps + 1))
+    per = {}
+    for r in range(reps):
+        if before is not None:
+            before(r)
+        trace.begin()
+        fn(r)
+        for name, t in trace.end():
+            per.setdefault(name, []).append(1e3 * t)
+    torch.cuda.synchronize()
+    return per
+
+
+def decode_layer_measurements(args, wl, hy, torch, k, v, qs, gates, idx, sb_bytes, dev):
+    """The sparse decode layer cold and warm, per-kernel cold durations, and
+    the size-matched bandwidth ceilings (module docstring)."""
+    B, Tkv, Hkv, D = k.shape
+    N = len(qs)
+    outs = [torch.empty_like(q) for q in qs]
+    desc = hy.make_desc(qs[0], k)
+    ws = torch.empty(hy.hysparse_workspace_bytes(hy.HYS_OP_SPARSE, desc, 1, wl.k_top, wl.window), dtype=torch.uint8,
+                     device=dev)
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def flush(r):
+        flush_buf.fill_(r & 0xFF)  # 1 GiB written: evicts the L2s and the last-level cache
+
+    def layer(r):
+        l = r % N
+        hy.hysparse_sparse_attn(qs[l], k, v, idx, wl.k_top, 1, wl.window, gates[l], out=outs[l], workspace=ws)
+
+    reps = args.layer_reps
+    for r in range(5):
+        layer(r)
+    cold = timed_reps(torch, layer, reps, before=flush)
+    # warm: the N layers of a block back to back, per layer; a spin kernel
+    # ahead of each bracket keeps the GPU busy while the host enqueues the
+    # bracket, so that host-side call overhead is not timed
+    warm = timed_reps(torch, lambda r: [layer(l) for l in range(N)], max(reps // N, 5),
+                      before=lambda r: torch.cuda._sleep(2_000_000)) / N
+    per = traced(hy, torch, layer, reps, before=flush)
+    kern_cold = {n: float(np.median(t)) for n, t in per.items()}
+
+    # ceilings of one launch of the same size
+    row_bytes = D * k.element_size()
+    idx_np = idx.cpu().numpy()
+    rows = []
+    for b in range(B):
+        for g in range(Hkv):
+            sel = idx_np[b, g, 0]
+            sel = sel[sel >= 0].astype(np.int64)
+            win = np.arange(max(0, Tkv - wl.window), Tkv, dtype=np.int64)
+            rows.append((b * Tkv + np.concatenate([sel, win])) * Hkv + g)
+    rows_t = torch.from_numpy(np.concatenate(rows).astype(np.int32)).to(dev)
+    gather_bytes = 2 * rows_t.numel() * row_bytes + 4 * rows_t.numel()
+    stream_bytes = (sb_bytes + 15) // 16 * 16
+    kflat, vflat = k.view(-1), v.view(-1)
+    cws = torch.empty(hy.hysparse_ceiling_workspace_bytes(stream_bytes, rows_t.numel()), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        hy.hysparse_ceiling_stream_read(kflat, stream_bytes, workspace=cws)
+        hy.hysparse_ceiling_gather(k, v, rows_t, workspace=cws)
+    c_stream = timed_reps(torch, lambda r: hy.hysparse_ceiling_stream_read(kflat, stream_bytes, workspace=cws), reps,
+                          before=flush)
+    c_gather = timed_reps(torch, lambda r: hy.hysparse_ceiling_gather(k, v, rows_t, workspace=cws), reps,
+                          before=flush)
+    torch.cuda.synchronize()
+    del flush_buf
+
+    def rate(nbytes, ms):
+        us = float(np.median(ms)) * 1e3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return {"us_median": us, "us_mean": float(np.mean(ms)) * 1e3, "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+
+    cold_r, warm_r = rate(sb_bytes, cold), rate(sb_bytes, warm)
+    st_r, ga_r = rate(stream_bytes, c_stream), rate(gather_bytes, c_gather)
+    cold_r.update({"tokens_per_s": B / (cold_r["us_median"] * 1e-6),
+                   "method": f"median of {reps} layers, each after a 1 GiB write (caches evicted); HIP events "
+                             "around the layer's split and merge kernels"})
+    warm_r.update({"tokens_per_s": B / (warm_r["us_median"] * 1e-6),
+                   "method": f"the {N} layers of a block back to back (gathered rows partly in the last-level "
+                             f"cache), HIP events around the {N} layers (enqueued behind a spin kernel), per "
+                             "layer"})
+    st_r.update({"bytes": stream_bytes, "what": "one launch reading the layer's byte count as one contiguous "
+                                                "stream (non-temporal 16-byte loads), cold"})
+    ga_r.update({"bytes": gather_bytes, "rows": int(rows_t.numel()),
+                 "what": "one launch reading the layer's own K and V rows (selected + window, 256 B each) at "
+                         "their row indices, indices loaded first, cold"})
+    return {"alg_bytes": sb_bytes, "cold": cold_r, "warm": warm_r, "kernels_cold_us": kern_cold,
+            "ceiling": {"stream_read": st_r, "gather_rows": ga_r,
+                        "cold_frac_of_stream_ceiling": st_r["us_median"] / cold_r["us_median"],
+                        "cold_frac_of_gather_ceiling": ga_r["us_median"] / cold_r["us_median"]}}
+
+
+def prefill128k_full_layer(hy, torch, gen, dev, reps=2):
+    """The 128K prefill full layer (both sweeps), inputs drawn on the GPU,
+    against the bf16 MFMA peak."""
+    wl = gen.WORKLOADS["prefill128k"]
+    qf, k, v, _, _ = gen.make_device_inputs(wl, dev, n_sparse=0)
+    B, Tq, Hq, D = qf.shape
+    Hkv, Tkv = k.shape[2], k.shape[1]
+    out = torch.empty_like(qf)
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=dev)
+    scores = torch.empty((B, Hkv, wl.n_blocks, Tkv), dtype=torch.float32, device=dev)
+    desc = hy.make_desc(qf, k)
+    ws = torch.empty(hy.hysparse_workspace_bytes(hy.HYS_OP_FULL, desc, wl.score_block), dtype=torch.uint8, device=dev)
+
+    def run(r):
+        hy.hysparse_full_attn_scores(qf, k, v, wl.score_block, out=out, lse=lse, scores=scores, workspace=ws)
+
+    run(0)
+    torch.cuda.synchronize()
+    ms = timed_reps(torch, run, reps)
+    per = traced(hy, torch, run, reps)
+    ff = full_layer_flops(wl)
+    t_us = float(np.median(ms)) * 1e3
+    fwd = float(np.median(per["full_prefill_fwd"]))
+    sco = float(np.median(per["full_prefill_scores"]))
+    res = {"workload": "prefill128k full layer (B 1, 131072 queries and keys, Hq 64 / Hkv 4, D 128, bf16, "
+                       "scores per 64-query block)",
+           "alg_flops": ff, "us": t_us, "tflops_algorithmic": ff / (t_us * 1e-6) / 1e12,
+           "frac_bf16_peak": ff / (t_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+           "fwd_sweep_us": fwd, "fwd_sweep_frac_bf16_peak": ff / (fwd * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+           "score_sweep_us": sco,
+           "score_sweep_qk_frac_bf16_peak": (ff // 2) / (sco * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+           "note": "algorithmic FLOPs = QK^T + PV over every causal (query, head, key) triple; the score sweep "
+                   "recomputes QK^T once the final LSE is known", "inputs": "drawn on the GPU"}
+    del qf, k, v, out, lse, scores, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -278,45 +452,19 @@ def main():
     wall = time.perf_counter() - w0
     ms = e0.elapsed_time(e1) / args.steps
     tokens_per_step = B * Tq
-    value = tokens_per_step / (ms * 1e-3)
+    block_tps = tokens_per_step / (ms * 1e-3)
     print(f"[bench] {args.steps} steps: {ms:.4f} ms/step (wall {1e3 * wall / args.steps:.4f})", file=sys.stderr,
           flush=True)
 
-    # decode: the sparse layers' share of the untraced step, from the same block
-    # without sparse layers (full layer + top-K), timed the same way
-    sparse_b2b_us = None
-    if Tq == 1 and not loop and not hier and qs:
-        def step0():
-            hy.hysparse_hybrid_block(qf, k, v, [], gates, wl.k_top, wl.score_block, wl.window, out_full=out_full,
-                                     lse=lse, scores=scores, idx=idx, workspace=ws)
-
-        for _ in range(args.warmup):
-            step0()
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.steps):
-            step0()
-        e1.record()
-        torch.cuda.synchronize()
-        ms0 = e0.elapsed_time(e1) / args.steps
-        sparse_b2b_us = 1e3 * (ms - ms0) / len(qs)
-
     # per-kernel durations: second pass with the library's event trace
-    trace = hy.KernelTrace(capacity_kernels=64 * (args.steps + 1))
-    trace.begin()
-    for _ in range(args.steps):
-        step()
-    rows = trace.end()
-    torch.cuda.synchronize()
-    per = {}
-    for name, t in rows:
-        per.setdefault(name, []).append(t)
-    kernels = {n: {"launches_per_step": len(t) / args.steps, "avg_us": 1e3 * float(np.mean(t)),
-                   "us_per_step": 1e3 * float(np.sum(t)) / args.steps} for n, t in per.items()}
-    traced_ms = float(sum(np.sum(t) for t in per.values())) / args.steps
+    per = traced(hy, torch, lambda r: step(), args.steps)
+    kernels = {n: {"launches_per_step": len(t) / args.steps, "avg_us": float(np.mean(t)),
+                   "us_per_step": float(np.sum(t)) / args.steps} for n, t in per.items()}
+    traced_ms = sum(v["us_per_step"] for v in kernels.values()) / 1e3
 
     idx_np = idx.cpu().numpy()
-    result = {"metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+    decode = Tq == 1 and not loop and not hier and len(qs) > 0
+    result = {"metric": METRIC, "value": block_tps, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
               "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
               "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
               "config": {"workload": wl.name, "batch": B, "q_len": Tq, "context": Tkv, "q_heads": Hq,
@@ -324,10 +472,10 @@ def main():
                          "n_sparse": len(qs), "score_block": wl.score_block,
                          "step": "hybrid block: full layer + top-K + all sparse layers"}}
 
-    def roof(name, alg_bytes):
-        if name not in kernels:
+    def roof(name, alg_bytes, us=None):
+        if name not in kernels and us is None:
             return None
-        us = kernels[name]["avg_us"]
+        us = kernels[name]["avg_us"] if us is None else us
         gbs = alg_bytes / (us * 1e-6) / 1e9
         return {"kernel": name, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name, name),
@@ -349,22 +497,21 @@ def main():
     if Tq == 1:
         sb = sparse_layer_bytes(wl, idx_np)
         rf = roof("full_decode_split", full_split_bytes(wl))
-        rs = roof("sparse_decode", sb)
-        result["roofline"] = rf if dom == "full_decode_split" else (rs if dom == "sparse_decode" else rf)
-        result["roofline_full"] = rf
-        result["roofline_sparse"] = rs
-        if rs:
-            traced_us = rs["avg_us"] + kernels.get("sparse_merge", {"avg_us": 0.0})["avg_us"]
-            # per layer: the untraced share of the step when it was measured
-            # (back to back, launch gaps included), else the two traced kernels
-            layer_us = sparse_b2b_us if sparse_b2b_us else traced_us
-            result["sparse_layer"] = {"tokens_per_s": tokens_per_step / (layer_us * 1e-6), "us_per_layer": layer_us,
-                                      "method": "step minus the block without sparse layers, per layer"
-                                      if sparse_b2b_us else "traced split + merge kernels",
-                                      "us_per_layer_traced": traced_us,
-                                      "GB_per_s": sb / (layer_us * 1e-6) / 1e9,
-                                      "frac_hbm": sb / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "alg_bytes": sb,
-                                      "split_kernel_us": rs["avg_us"]}
+        result["roofline"] = rf
+        result["hybrid_block"] = {"tokens_per_s": block_tps, "ms_per_step": ms,
+                                  "what": "full layer + top-K + all sparse layers, the timed steps"}
+        if decode:
+            print("[bench] sparse layer cold / warm, ceilings", file=sys.stderr, flush=True)
+            sl = decode_layer_measurements(args, wl, hy, torch, k, v, qs, gates, idx, sb, dev)
+            result["value"] = sl["cold"]["tokens_per_s"]
+            result["value_is"] = ("sparse-layer decode tokens/s, cold (batch / median time of one sparse layer "
+                                  "after a 1 GiB cache-evicting write); sparse_layer.cold.frac_hbm is its "
+                                  "fraction of the 8 TB/s HBM peak")
+            result["sparse_layer"] = sl
+            result["roofline_sparse"] = roof("sparse_decode", sb, us=sl["kernels_cold_us"].get("sparse_decode"))
+            if result["roofline_sparse"]:
+                result["roofline_sparse"]["note"] = ("cold split kernel alone (gather, both branches' softmax); "
+                                                     "the merge kernel is the rest of the layer")
     else:
         ff = full_layer_flops(wl)
         rf = roof_flops("full_prefill_fwd", ff)
@@ -409,7 +556,13 @@ def main():
         result["input_sha256"] = inp.sha256()
     else:
         result["inputs"] = "drawn on the GPU: torch generator seeded per (config, tensor, layer)"
+    if decode and wl.name == "decode128k" and args.prefill128k:
+        print("[bench] 128K prefill full layer", file=sys.stderr, flush=True)
+        del ws
+        torch.cuda.empty_cache()
+        result["full_layer_prefill128k"] = prefill128k_full_layer(hy, torch, gen, dev)
     if args.cpu_baseline and not hier and inp is not None:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

@@ -324,6 +324,31 @@ const char* hysparse_last_error(void);
 int32_t hysparse_version(void);
 
 /*
+ * Measurement helpers (not part of the computation): size-matched bandwidth
+ * ceilings.  A decode-time sparse layer moves a few tens of MB per launch,
+ * too little for one launch to reach the HBM peak; these kernels give what a
+ * launch of the same size reaches with nothing else to do (Baidu article,
+ * "Key Engineering Considerations": decoding is bound by memory bandwidth).
+ * Both only read their inputs and write one word per workgroup into ws.
+ *
+ * hysparse_ceiling_stream_read  reads n_bytes (a multiple of 16) from the
+ *                               16-byte aligned device buffer p.
+ * hysparse_ceiling_gather       reads row_bytes (a multiple of 16, <= 256)
+ *                               at k + rows[r] * row_stride_bytes and at
+ *                               v + rows[r] * row_stride_bytes for every
+ *                               r < n_rows whose rows[r] lies in
+ *                               [0, n_buffer_rows) (others are skipped),
+ *                               the row indices loaded first.
+ * ws/ws_bytes: at least hysparse_ceiling_workspace_bytes(n_bytes, n_rows).
+ */
+size_t hysparse_ceiling_workspace_bytes(int64_t n_bytes, int64_t n_rows);
+hys_status hysparse_ceiling_stream_read(const void* p, int64_t n_bytes, void* ws, size_t ws_bytes,
+                                        hipStream_t stream);
+hys_status hysparse_ceiling_gather(const void* k, const void* v, int64_t row_stride_bytes, int64_t n_buffer_rows,
+                                   const int32_t* rows, int64_t n_rows, int32_t row_bytes, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/*
  * Kernel-level timing hook for profilers (not part of the computation).
  * While a trace is active on the calling thread, the library records, on the
  * launch stream, events[2i] just before and events[2i+1] just after the i-th

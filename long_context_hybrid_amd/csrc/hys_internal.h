@@ -137,4 +137,12 @@ hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const
 hipError_t launch_hier_pool(const Geom& g, const void* k, int block, int m_begin, int m_end, float* kbar,
                             int64_t kbar_blocks, hipStream_t st);
 
+// Bandwidth ceilings of one launch (ceiling.hip): sink holds one word per
+// workgroup.
+int64_t ceiling_stream_blocks(int64_t n_bytes);
+int64_t ceiling_gather_blocks(int64_t n_rows);
+hipError_t launch_ceiling_stream(const void* p, int64_t n_bytes, uint32_t* sink, hipStream_t st);
+hipError_t launch_ceiling_gather(const void* k, const void* v, int64_t row_stride_bytes, int64_t n_buf_rows,
+                                 const int32_t* rows, int64_t n_rows, int row_bytes, uint32_t* sink, hipStream_t st);
+
 }  // namespace hys

@@ -6,10 +6,9 @@
 #include <cmath>
 #include <cstdint>
 #include <string>
+#include <vector>
 
 #include "hys_internal.h"
-
-#include <vector>
 
 namespace {
 
@@ -412,6 +411,38 @@ size_t hysparse_hier_workspace_bytes(const hys_attn_desc* desc, int32_t block, i
 size_t hysparse_topk_workspace_bytes(int64_t n_rows, int32_t row_len, int32_t k) {
   if (n_rows < 0 || row_len < 1 || k < 1) return 0;
   return hys::topk_ws_bytes(n_rows, row_len, k);
+}
+
+size_t hysparse_ceiling_workspace_bytes(int64_t n_bytes, int64_t n_rows) {
+  if (n_bytes < 0 || n_rows < 0) return 0;
+  const int64_t a = hys::ceiling_stream_blocks(n_bytes), b = hys::ceiling_gather_blocks(n_rows);
+  return hys::align_up((size_t)(a > b ? a : b) * sizeof(uint32_t));
+}
+
+hys_status hysparse_ceiling_stream_read(const void* p, int64_t n_bytes, void* ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+  if (n_bytes < 0 || n_bytes % 16 != 0) return fail(HYS_ERR_BAD_SHAPE, "n_bytes must be a non-negative multiple of 16");
+  if (n_bytes == 0) return ok();
+  hys_status s;
+  if ((s = check_tensor(p, "p", 16))) return s;
+  if ((s = check_ws(ws, ws_bytes, hysparse_ceiling_workspace_bytes(n_bytes, 0)))) return s;
+  return from_hip(hys::launch_ceiling_stream(p, n_bytes, static_cast<uint32_t*>(ws), stream));
+}
+
+hys_status hysparse_ceiling_gather(const void* k, const void* v, int64_t row_stride_bytes, int64_t n_buffer_rows,
+                                   const int32_t* rows, int64_t n_rows, int32_t row_bytes, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  if (n_rows < 0 || n_buffer_rows < 0) return fail(HYS_ERR_BAD_SHAPE, "n_rows and n_buffer_rows must be >= 0");
+  if (row_bytes < 16 || row_bytes > 256 || row_bytes % 16 != 0)
+    return fail(HYS_ERR_UNSUPPORTED, "row_bytes must be a multiple of 16 in [16, 256]");
+  if (row_stride_bytes < row_bytes || row_stride_bytes % 16 != 0)
+    return fail(HYS_ERR_ALIGN, "row_stride_bytes must be >= row_bytes and a multiple of 16");
+  if (n_rows == 0) return ok();
+  hys_status s;
+  if ((s = check_tensor(k, "k", 16)) || (s = check_tensor(v, "v", 16)) || (s = check_tensor(rows, "rows", 4))) return s;
+  if ((s = check_ws(ws, ws_bytes, hysparse_ceiling_workspace_bytes(0, n_rows)))) return s;
+  return from_hip(hys::launch_ceiling_gather(k, v, row_stride_bytes, n_buffer_rows, rows, n_rows, row_bytes,
+                                             static_cast<uint32_t*>(ws), stream));
 }
 
 const char* hysparse_status_string(hys_status status) {

@@ -30,7 +30,8 @@ EXPORTS = ("hysparse_full_attn_scores", "hysparse_topk", "hysparse_sparse_attn",
            "hysparse_last_error", "hysparse_version", "hysparse_trace_begin", "hysparse_trace_end",
            "hysparse_trace_name", "hysparse_hier_select", "hysparse_hier_workspace_bytes", "hysparse_append_kv",
            "hysparse_sparse_attn_token_gate", "hysparse_sparse_attn_ex", "hysparse_hier_pool",
-           "hysparse_hier_select_pooled")
+           "hysparse_hier_select_pooled", "hysparse_ceiling_workspace_bytes", "hysparse_ceiling_stream_read",
+           "hysparse_ceiling_gather")
 
 
 class HysWindowKV(ctypes.Structure):
@@ -96,6 +97,12 @@ def lib() -> ctypes.CDLL:
     L.hysparse_sparse_attn_ex.restype = i32
     L.hysparse_append_kv.restype = i32
     L.hysparse_hier_workspace_bytes.restype = sz
+    L.hysparse_ceiling_workspace_bytes.argtypes = [i64, i64]
+    L.hysparse_ceiling_workspace_bytes.restype = sz
+    L.hysparse_ceiling_stream_read.argtypes = [_P, i64, _P, sz, _P]
+    L.hysparse_ceiling_stream_read.restype = i32
+    L.hysparse_ceiling_gather.argtypes = [_P, _P, i64, i64, _P, i64, i32, _P, sz, _P]
+    L.hysparse_ceiling_gather.restype = i32
     L.hysparse_trace_begin.argtypes = [_P, i32]
     L.hysparse_trace_begin.restype = None
     L.hysparse_trace_end.argtypes = []
@@ -441,3 +448,32 @@ def hysparse_sparse_attn_ex(q, k, v, idx, k_top: int, score_block: int, window: 
                                          ctypes.byref(win) if win is not None else None, _ptr(out), _ptr(ws),
                                          0 if ws is None else ws.numel(), _stream(dev)))
     return out
+
+
+def hysparse_ceiling_workspace_bytes(n_bytes: int, n_rows: int) -> int:
+    return int(lib().hysparse_ceiling_workspace_bytes(n_bytes, n_rows))
+
+
+def hysparse_ceiling_stream_read(buf, n_bytes: int, workspace=None):
+    """Measurement helper: read the first n_bytes of the device tensor buf in
+    one launch (nothing computed)."""
+    dev = _same_device(buf)
+    if n_bytes > buf.numel() * buf.element_size() or not buf.is_contiguous():
+        raise ValueError("n_bytes exceeds the contiguous buffer")
+    ws = _workspace(hysparse_ceiling_workspace_bytes(n_bytes, 0), dev, workspace)
+    _check(lib().hysparse_ceiling_stream_read(_ptr(buf), n_bytes, _ptr(ws), 0 if ws is None else ws.numel(),
+                                              _stream(dev)))
+
+
+def hysparse_ceiling_gather(k, v, rows, workspace=None):
+    """Measurement helper: read the K and V rows (last axis) of the contiguous
+    caches k, v [..., D] at the flat row indices rows (int32) in one launch."""
+    dev = _same_device(k, v, rows)
+    if not (k.is_contiguous() and v.is_contiguous() and k.shape == v.shape and rows.dtype == torch.int32
+            and rows.is_contiguous()):
+        raise ValueError("k, v must be matching contiguous tensors, rows contiguous int32")
+    row_bytes = k.shape[-1] * k.element_size()
+    n_buf = k.numel() // k.shape[-1]
+    ws = _workspace(hysparse_ceiling_workspace_bytes(0, rows.numel()), dev, workspace)
+    _check(lib().hysparse_ceiling_gather(_ptr(k), _ptr(v), row_bytes, n_buf, _ptr(rows), rows.numel(), row_bytes,
+                                         _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)))

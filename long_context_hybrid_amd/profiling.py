@@ -40,7 +40,42 @@ KERNELS = {  # symbol fragment -> name used by the library's trace hook
     "block_softmax_kernel": "hier_block_softmax",
     "gather_candidates_kernel": "hier_gather",
     "map_positions_kernel": "hier_map",
+    "ceiling_stream_kernel": "ceiling_stream",
+    "ceiling_gather_kernel": "ceiling_gather",
 }
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = {"full_decode_split": "decode.hip", "full_decode_finish": "decode.hip", "sparse_decode": "decode.hip",
+                  "sparse_merge": "decode.hip", "full_prefill_fwd": "prefill.hip",
+                  "full_prefill_scores": "prefill.hip", "sparse_prefill": "prefill.hip", "topk": "topk.hip",
+                  "topk_part": "topk.hip", "topk_select": "topk.hip"}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the HIP sources that define a kernel: traffic figures are only
+    reported while the kernel is unchanged since its counters were taken."""
+    import hashlib
+    src = KERNEL_SOURCES.get(kernel)
+    if src is None:
+        return ""
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    h = hashlib.sha256()
+    for f in (src, "hys_common.h", "attn_tile.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of a kernel from the committed counter runs, or
+    None (no record, or the kernel's source changed since)."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[workload][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def short_name(symbol: str) -> str:
@@ -126,9 +161,6 @@ def copy_factor(d: str, counter: str, nbytes: int) -> float:
 
 
 def traffic(args) -> dict:
-    import sys
-    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
-    from bench import kernel_source_hash  # the hash bench.py checks before reporting traffic
     nbytes = args.copy_mib << 20
     ff = copy_factor(args.copy_fetch, "FETCH_SIZE", nbytes)
     wf = copy_factor(args.copy_write, "WRITE_SIZE", nbytes)
@@ -159,8 +191,7 @@ def main():
     t.add_argument("--copy-fetch", required=True)
     t.add_argument("--copy-write", required=True)
     t.add_argument("--copy-mib", type=int, default=1024)
-    t.add_argument("--out", default=os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                                                 "profiles", "hbm_traffic.json"))
+    t.add_argument("--out", default=TRAFFIC_FILE)
     args = ap.parse_args()
     if args.cmd == "stats":
         print(stats_table(args.dir))

@@ -209,3 +209,20 @@ def test_sparse_ex_validation():
     assert L.hysparse_sparse_attn_ex(*args(ctypes.byref(w))) == 4
     w.k = None
     assert L.hysparse_sparse_attn_ex(*args(ctypes.byref(w))) == 1
+
+
+def test_ceiling_helpers_validation():
+    L = hy.lib()
+    assert L.hysparse_ceiling_workspace_bytes(18 << 20, 0) >= 4 * ((18 << 20) // 16 // 1024)
+    assert L.hysparse_ceiling_workspace_bytes(0, 34816) >= 4 * (34816 // 64)
+    assert L.hysparse_ceiling_workspace_bytes(-1, 0) == 0
+    assert L.hysparse_ceiling_stream_read(FAKE, 100, FAKE, 1 << 20, None) == 2        # not a multiple of 16
+    assert L.hysparse_ceiling_stream_read(FAKE_ODD, 4096, FAKE, 1 << 20, None) == 4
+    assert L.hysparse_ceiling_stream_read(FAKE, 1 << 20, None, 0, None) == 5          # no sink
+    assert L.hysparse_ceiling_stream_read(FAKE, 0, None, 0, None) == 0                # empty: no-op
+    assert L.hysparse_ceiling_gather(FAKE, FAKE, 256, 100, FAKE, 10, 512, FAKE, 1 << 20, None) == 3   # row > 256 B
+    assert L.hysparse_ceiling_gather(FAKE, FAKE, 128, 100, FAKE, 10, 256, FAKE, 1 << 20, None) == 4   # stride < row
+    assert L.hysparse_ceiling_gather(FAKE, None, 256, 100, FAKE, 10, 256, FAKE, 1 << 20, None) == 1
+    assert L.hysparse_ceiling_gather(FAKE, FAKE, 256, 100, FAKE, 10, 256, None, 0, None) == 5
+    assert L.hysparse_ceiling_gather(FAKE, FAKE, 256, -1, FAKE, 10, 256, FAKE, 1 << 20, None) == 2
+
