@@ -202,6 +202,31 @@ hys_status hysparse_sparse_attn_ex(const hys_attn_desc* desc, const void* q, con
                                    hipStream_t stream);
 
 /*
+ * hysparse_sparse_attn without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Arguments, outputs and errors as
+ * hysparse_sparse_attn, minus ws/ws_bytes: the split partial states of the
+ * one-query-row path (score_block 1 or q_len 1) go to a fixed scratch array
+ * inside the library, hysparse_noalloc_scratch_bytes() bytes (16 MiB) per
+ * GPU, held from the first call on that GPU until the process ends.  The
+ * scratch used is that of the device current at the call, so `stream` must
+ * belong to the current device.  Calls needing more scratch than that (what
+ * hysparse_workspace_bytes(HYS_OP_SPARSE, ...) returns) fail with
+ * HYS_ERR_WORKSPACE before anything is launched.  The call allocates nothing.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one GPU (different streams, or graphs replayed concurrently) race and must
+ * not be issued; calls ordered on one stream are safe.  Nothing in the
+ * scratch needs to start at zero (each call writes every partial it reads).
+ */
+hys_status hysparse_sparse_attn_noalloc(const hys_attn_desc* desc, const void* q, const void* k,
+                                        const void* v, const int32_t* idx, int32_t k_top,
+                                        int32_t score_block, int32_t window, const float* gate_logits,
+                                        void* out, hipStream_t stream);
+
+/* Bytes of the fixed scratch behind hysparse_sparse_attn_noalloc. */
+size_t hysparse_noalloc_scratch_bytes(void);
+
+/*
  * One hybrid block (intelliparadigm article 2.1 and 3.1): the full layer on
  * q_full, top-K over its scores, then n_sparse sparse layers that reuse its
  * k, v and indices, each with its own queries and gate logits.

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -130,6 +131,35 @@ hipError_t run_sparse(const hys::Geom& g, const void* q, const void* k, const vo
   return hys::launch_sparse_block(g, q, k, v, idx, kt, sb, w, gate, win, out, ws, st);
 }
 
+// Scratch of hysparse_sparse_attn_noalloc: a fixed device array of this
+// library, one copy per GPU, held until the process ends.  Host code must
+// never pass the array's name to a kernel or a copy (on the host it is only a
+// stand-in): it uses the device address that hipGetSymbolAddress returns,
+// looked up once per device with that device current.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hys_status scratch_on_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HYS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(HYS_ERR_UNSUPPORTED, "device ordinal out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(HYS_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return HYS_OK;
+}
+
 }  // namespace
 
 namespace hys {
@@ -228,6 +258,31 @@ hys_status hysparse_sparse_attn_ex(const hys_attn_desc* desc, const void* q, con
   const hys::GateRef gate{gate_logits, gate_stride_b, gate_stride_t};
   return from_hip(run_sparse(g, q, k, v, idx, k_top, score_block, window, gate, out, ws, stream, win));
 }
+
+hys_status hysparse_sparse_attn_noalloc(const hys_attn_desc* desc, const void* q, const void* k, const void* v,
+                                        const int32_t* idx, int32_t k_top, int32_t score_block, int32_t window,
+                                        const float* gate_logits, void* out, hipStream_t stream) {
+  hys::Geom g;
+  hys_status s;
+  if ((s = check_desc(desc, &g))) return s;
+  if ((s = check_sb(score_block))) return s;
+  if (k_top < 1) return fail(HYS_ERR_BAD_SHAPE, "k_top must be >= 1");
+  if (window < 1) return fail(HYS_ERR_BAD_SHAPE, "window must be >= 1");
+  if ((s = check_tensor(q, "q", 16)) || (s = check_tensor(k, "k", 16)) || (s = check_tensor(v, "v", 16)) ||
+      (s = check_tensor(out, "out", 16)) || (s = check_tensor(idx, "idx", 4)) ||
+      (s = check_tensor(gate_logits, "gate_logits", 4)))
+    return s;
+  const size_t need = sparse_ws(g, score_block, k_top, window);
+  if (need > kScratchBytes)
+    return fail(HYS_ERR_WORKSPACE, "this call needs " + std::to_string(need) + " bytes of scratch; the library's "
+                "fixed scratch holds " + std::to_string(kScratchBytes) + " (use hysparse_sparse_attn with a workspace)");
+  void* ws = nullptr;
+  if (need > 0 && (s = scratch_on_current_device(&ws))) return s;
+  const hys::GateRef gate{gate_logits, 0, 0};
+  return from_hip(run_sparse(g, q, k, v, idx, k_top, score_block, window, gate, out, ws, stream));
+}
+
+size_t hysparse_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 hys_status hysparse_hybrid_block(const hys_attn_desc* desc, const void* q_full, const void* k, const void* v,
                                  int32_t n_sparse, const void* const* q_sparse, const float* gate_logits,

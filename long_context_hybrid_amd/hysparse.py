@@ -31,7 +31,7 @@ EXPORTS = ("hysparse_full_attn_scores", "hysparse_topk", "hysparse_sparse_attn",
            "hysparse_trace_name", "hysparse_hier_select", "hysparse_hier_workspace_bytes", "hysparse_append_kv",
            "hysparse_sparse_attn_token_gate", "hysparse_sparse_attn_ex", "hysparse_hier_pool",
            "hysparse_hier_select_pooled", "hysparse_ceiling_workspace_bytes", "hysparse_ceiling_stream_read",
-           "hysparse_ceiling_gather")
+           "hysparse_ceiling_gather", "hysparse_sparse_attn_noalloc", "hysparse_noalloc_scratch_bytes")
 
 
 class HysWindowKV(ctypes.Structure):
@@ -97,6 +97,10 @@ def lib() -> ctypes.CDLL:
     L.hysparse_sparse_attn_ex.restype = i32
     L.hysparse_append_kv.restype = i32
     L.hysparse_hier_workspace_bytes.restype = sz
+    L.hysparse_sparse_attn_noalloc.argtypes = [D, _P, _P, _P, _P, i32, i32, i32, _P, _P, _P]
+    L.hysparse_sparse_attn_noalloc.restype = i32
+    L.hysparse_noalloc_scratch_bytes.argtypes = []
+    L.hysparse_noalloc_scratch_bytes.restype = sz
     L.hysparse_ceiling_workspace_bytes.argtypes = [i64, i64]
     L.hysparse_ceiling_workspace_bytes.restype = sz
     L.hysparse_ceiling_stream_read.argtypes = [_P, i64, _P, sz, _P]
@@ -229,6 +233,25 @@ def hysparse_sparse_attn(q, k, v, idx, k_top: int, score_block: int, window: int
                                       window, _ptr(gate_logits), _ptr(out), _ptr(ws),
                                       0 if ws is None else ws.numel(), _stream(dev)))
     return out
+
+
+def hysparse_sparse_attn_noalloc(q, k, v, idx, k_top: int, score_block: int, window: int, gate_logits, out,
+                                 scale: float = 0.0):
+    """hysparse_sparse_attn with the library's fixed scratch instead of a
+    workspace; out must be given (nothing is allocated).  Returns out."""
+    dev = _same_device(q, k, v, idx, gate_logits, out)
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be contiguous int32 [B, Hkv, NB, k_top]")
+    if gate_logits.dtype != torch.float32 or not gate_logits.is_contiguous():
+        raise ValueError("gate_logits must be contiguous float32 [Hq]")
+    desc = make_desc(q, k, scale)
+    _check(lib().hysparse_sparse_attn_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), k_top,
+                                              score_block, window, _ptr(gate_logits), _ptr(out), _stream(dev)))
+    return out
+
+
+def hysparse_noalloc_scratch_bytes() -> int:
+    return int(lib().hysparse_noalloc_scratch_bytes())
 
 
 def hysparse_sparse_attn_token_gate(q, k, v, idx, k_top: int, score_block: int, window: int, gate_logits,

@@ -226,3 +226,23 @@ def test_ceiling_helpers_validation():
     assert L.hysparse_ceiling_gather(FAKE, FAKE, 256, 100, FAKE, 10, 256, None, 0, None) == 5
     assert L.hysparse_ceiling_gather(FAKE, FAKE, 256, -1, FAKE, 10, 256, FAKE, 1 << 20, None) == 2
 
+
+def test_noalloc_validation():
+    """The no-allocation sparse layer validates like hysparse_sparse_attn and
+    refuses, before any HIP call, shapes whose partial states exceed its
+    fixed scratch."""
+    L = hy.lib()
+    assert L.hysparse_noalloc_scratch_bytes() == 16 << 20
+    d = _desc()
+    call = lambda d, sb=1, kt=64, w=16, q=FAKE, idx=FAKE: L.hysparse_sparse_attn_noalloc(
+        ctypes.byref(d), q, FAKE, FAKE, idx, kt, sb, w, FAKE, FAKE, None)
+    assert call(d, q=None) == 1
+    assert call(d, q=FAKE_ODD) == 4
+    assert call(d, kt=0) == 2
+    assert call(d, w=0) == 2
+    assert call(d, sb=32) == 3
+    big = _desc(B=1, Tq=8192, Tkv=8192, Hq=32, Hkv=8)
+    need = L.hysparse_workspace_bytes(hy.HYS_OP_SPARSE, ctypes.byref(big), 1, 2048, 128)
+    assert need > L.hysparse_noalloc_scratch_bytes()
+    assert call(big, kt=2048, w=128) == 5
+    assert b"fixed scratch" in L.hysparse_last_error()
