@@ -210,19 +210,23 @@ def timed_reps(torch, fn, reps, before=None):
 
 
 def traced(hy, torch, fn, reps, before=None):
-    """Per-kernel durations (us) of fn over reps runs from the library's event
-    trace: {name: [durations]}."""
-    trace = hy.KernelTrace(capacity_kernels=64 * (reps + 1))
-    per = {}
+    """Per-kernel durations (us) of fn over reps runs from the library's
+    trace (each kernel's dispatch begin/end times): {name: [durations]}, and
+    the span of each run (begin of its first kernel to end of its last, us)."""
+    trace = hy.KernelTrace(capacity_kernels=64)
+    per, spans = {}, []
     for r in range(reps):
         if before is not None:
             before(r)
         trace.begin()
         fn(r)
-        for name, t in trace.end():
+        rows = trace.end()
+        for name, t in rows:
             per.setdefault(name, []).append(1e3 * t)
+        if rows:
+            spans.append(1e3 * trace.span_ms(0, len(rows) - 1))
     torch.cuda.synchronize()
-    return per
+    return per, np.array(spans)
 
 
 def decode_layer_measurements(args, wl, hy, torch, k, v, qs, gates, idx, sb_bytes, dev):
@@ -246,14 +250,19 @@ def decode_layer_measurements(args, wl, hy, torch, k, v, qs, gates, idx, sb_byte
     reps = args.layer_reps
     for r in range(5):
         layer(r)
-    cold = timed_reps(torch, layer, reps, before=flush)
-    # warm: the N layers of a block back to back, per layer; a spin kernel
-    # ahead of each bracket keeps the GPU busy while the host enqueues the
-    # bracket, so that host-side call overhead is not timed
-    warm = timed_reps(torch, lambda r: [layer(l) for l in range(N)], max(reps // N, 5),
-                      before=lambda r: torch.cuda._sleep(2_000_000)) / N
-    per = traced(hy, torch, layer, reps, before=flush)
+    spin = lambda r: torch.cuda._sleep(2_000_000)
+    # cold: each layer after the flush.  The layer's time is the sum of its
+    # kernels' durations (dispatch begin/end timestamps, as a kernel trace
+    # gives them); the same layers between two ordinary HIP events (launch
+    # gaps and the events' own overhead included) are reported beside it
+    per, _ = traced(hy, torch, layer, reps, before=flush)
+    cold = np.sum([np.array(t) for t in per.values()], axis=0) / 1e3
+    cold_ev = timed_reps(torch, layer, reps, before=flush)
     kern_cold = {n: float(np.median(t)) for n, t in per.items()}
+    # warm: the N layers of a block back to back between two HIP events, per
+    # layer; a spin kernel ahead of each run keeps the GPU busy while the host
+    # enqueues the run, so that host-side call overhead is not timed
+    warm = timed_reps(torch, lambda r: [layer(l) for l in range(N)], max(reps // N, 5), before=spin) / N
 
     # ceilings of one launch of the same size
     row_bytes = D * k.element_size()
@@ -273,10 +282,11 @@ def decode_layer_measurements(args, wl, hy, torch, k, v, qs, gates, idx, sb_byte
     for _ in range(3):
         hy.hysparse_ceiling_stream_read(kflat, stream_bytes, workspace=cws)
         hy.hysparse_ceiling_gather(k, v, rows_t, workspace=cws)
-    c_stream = timed_reps(torch, lambda r: hy.hysparse_ceiling_stream_read(kflat, stream_bytes, workspace=cws), reps,
-                          before=flush)
-    c_gather = timed_reps(torch, lambda r: hy.hysparse_ceiling_gather(k, v, rows_t, workspace=cws), reps,
-                          before=flush)
+    _, c_stream = traced(hy, torch, lambda r: hy.hysparse_ceiling_stream_read(kflat, stream_bytes, workspace=cws),
+                         reps, before=flush)
+    _, c_gather = traced(hy, torch, lambda r: hy.hysparse_ceiling_gather(k, v, rows_t, workspace=cws), reps,
+                         before=flush)
+    c_stream, c_gather = c_stream / 1e3, c_gather / 1e3
     torch.cuda.synchronize()
     del flush_buf
 
@@ -288,17 +298,20 @@ def decode_layer_measurements(args, wl, hy, torch, k, v, qs, gates, idx, sb_byte
     cold_r, warm_r = rate(sb_bytes, cold), rate(sb_bytes, warm)
     st_r, ga_r = rate(stream_bytes, c_stream), rate(gather_bytes, c_gather)
     cold_r.update({"tokens_per_s": B / (cold_r["us_median"] * 1e-6),
-                   "method": f"median of {reps} layers, each after a 1 GiB write (caches evicted); HIP events "
-                             "around the layer's split and merge kernels"})
+                   "us_median_event_bracket": float(np.median(cold_ev)) * 1e3,
+                   "method": f"median over {reps} layers, each after a 1 GiB write (caches evicted), of the sum of "
+                             "the layer's kernel durations (dispatch begin/end timestamps, as a kernel trace gives "
+                             "them); us_median_event_bracket: the same layers between two ordinary HIP events "
+                             "(launch gaps and event overhead included)"})
     warm_r.update({"tokens_per_s": B / (warm_r["us_median"] * 1e-6),
                    "method": f"the {N} layers of a block back to back (gathered rows partly in the last-level "
-                             f"cache), HIP events around the {N} layers (enqueued behind a spin kernel), per "
-                             "layer"})
+                             f"cache) between two HIP events, enqueued behind a spin kernel, per layer (launch "
+                             "gaps included)"})
     st_r.update({"bytes": stream_bytes, "what": "one launch reading the layer's byte count as one contiguous "
-                                                "stream (non-temporal 16-byte loads), cold"})
+                                                "stream (non-temporal 16-byte loads), cold, kernel duration"})
     ga_r.update({"bytes": gather_bytes, "rows": int(rows_t.numel()),
                  "what": "one launch reading the layer's own K and V rows (selected + window, 256 B each) at "
-                         "their row indices, indices loaded first, cold"})
+                         "their row indices, indices loaded first, cold, kernel duration"})
     return {"alg_bytes": sb_bytes, "cold": cold_r, "warm": warm_r, "kernels_cold_us": kern_cold,
             "ceiling": {"stream_read": st_r, "gather_rows": ga_r,
                         "cold_frac_of_stream_ceiling": st_r["us_median"] / cold_r["us_median"],
@@ -324,7 +337,7 @@ def prefill128k_full_layer(hy, torch, gen, dev, reps=2):
     run(0)
     torch.cuda.synchronize()
     ms = timed_reps(torch, run, reps)
-    per = traced(hy, torch, run, reps)
+    per, _ = traced(hy, torch, run, reps)
     ff = full_layer_flops(wl)
     t_us = float(np.median(ms)) * 1e3
     fwd = float(np.median(per["full_prefill_fwd"]))
@@ -457,7 +470,7 @@ def main():
           flush=True)
 
     # per-kernel durations: second pass with the library's event trace
-    per = traced(hy, torch, lambda r: step(), args.steps)
+    per, _ = traced(hy, torch, lambda r: step(), args.steps)
     kernels = {n: {"launches_per_step": len(t) / args.steps, "avg_us": float(np.mean(t)),
                    "us_per_step": float(np.sum(t)) / args.steps} for n, t in per.items()}
     traced_ms = sum(v["us_per_step"] for v in kernels.values()) / 1e3
@@ -505,8 +518,8 @@ def main():
             sl = decode_layer_measurements(args, wl, hy, torch, k, v, qs, gates, idx, sb, dev)
             result["value"] = sl["cold"]["tokens_per_s"]
             result["value_is"] = ("sparse-layer decode tokens/s, cold (batch / median time of one sparse layer "
-                                  "after a 1 GiB cache-evicting write); sparse_layer.cold.frac_hbm is its "
-                                  "fraction of the 8 TB/s HBM peak")
+                                  "after a 1 GiB cache-evicting write, kernel durations); sparse_layer.cold.frac_hbm "
+                                  "is its fraction of the 8 TB/s HBM peak")
             result["sparse_layer"] = sl
             result["roofline_sparse"] = roof("sparse_decode", sb, us=sl["kernels_cold_us"].get("sparse_decode"))
             if result["roofline_sparse"]:

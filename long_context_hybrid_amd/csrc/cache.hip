@@ -37,11 +37,10 @@ hipError_t launch_append_kv(const Geom& g, const void* k_new, const void* v_new,
   const int cpr = g.D * esz / 16;
   const int64_t n_chunks = (int64_t)g.B * n_new * g.Hkv * cpr;
   if (n_chunks == 0) return hipSuccess;
-  TraceScope ts(st, "append_kv");
-  append_kv_kernel<<<(unsigned)((n_chunks + 255) / 256), 256, 0, st>>>(
-      static_cast<const u32x4_t*>(k_new), static_cast<const u32x4_t*>(v_new), n_chunks, cpr, g.Hkv, n_new, esz,
-      g.ks_b, g.ks_t, g.ks_h, pos, static_cast<unsigned char*>(k_cache), static_cast<unsigned char*>(v_cache));
-  return hipGetLastError();
+  return launch("append_kv", append_kv_kernel, dim3((unsigned)((n_chunks + 255) / 256)), dim3(256), 0, st,
+                static_cast<const u32x4_t*>(k_new), static_cast<const u32x4_t*>(v_new), n_chunks, cpr, g.Hkv, n_new,
+                esz, g.ks_b, g.ks_t, g.ks_h, pos, static_cast<unsigned char*>(k_cache),
+                static_cast<unsigned char*>(v_cache));
 }
 
 }  // namespace hys

@@ -92,20 +92,17 @@ int64_t ceiling_gather_blocks(int64_t n_rows) { return (n_rows + 16 * kGatherU -
 hipError_t launch_ceiling_stream(const void* p, int64_t n_bytes, uint32_t* sink, hipStream_t st) {
   const int64_t nb = ceiling_stream_blocks(n_bytes);
   if (nb == 0) return hipSuccess;
-  TraceScope ts(st, "ceiling_stream");
-  ceiling_stream_kernel<<<(unsigned)nb, kNT, 0, st>>>(static_cast<const unsigned char*>(p), n_bytes / 16, sink);
-  return hipGetLastError();
+  return launch("ceiling_stream", ceiling_stream_kernel, dim3((unsigned)nb), dim3(kNT), 0, st,
+                static_cast<const unsigned char*>(p), n_bytes / 16, sink);
 }
 
 hipError_t launch_ceiling_gather(const void* k, const void* v, int64_t row_stride_bytes, int64_t n_buf_rows,
                                  const int32_t* rows, int64_t n_rows, int row_bytes, uint32_t* sink, hipStream_t st) {
   const int64_t nb = ceiling_gather_blocks(n_rows);
   if (nb == 0) return hipSuccess;
-  TraceScope ts(st, "ceiling_gather");
-  ceiling_gather_kernel<<<(unsigned)nb, kNT, 0, st>>>(static_cast<const unsigned char*>(k),
-                                                      static_cast<const unsigned char*>(v), row_stride_bytes, rows,
-                                                      n_rows, n_buf_rows, row_bytes / 16, sink);
-  return hipGetLastError();
+  return launch("ceiling_gather", ceiling_gather_kernel, dim3((unsigned)nb), dim3(kNT), 0, st,
+                static_cast<const unsigned char*>(k), static_cast<const unsigned char*>(v), row_stride_bytes, rows,
+                n_rows, n_buf_rows, row_bytes / 16, sink);
 }
 
 }  // namespace hys

@@ -880,17 +880,15 @@ hipError_t launch_full_decode(const Geom& g, const void* q, const void* k, const
   f.out = out;
   f.lse = lse;
   f.scores = scores;
+  hipError_t e = hipSuccess;
   HYS_DISPATCH(g, {
-    {
-      TraceScope ts(st, "full_decode_split");
-      decode_split_kernel<TR, DD, true><<<p.units * p.nsplit, 256, 0, st>>>(a);
-    }
-    {
-      TraceScope ts(st, "full_decode_finish");
-      decode_full_finish_kernel<TR, DD><<<p.units * (g.G + f.nchunk), 256, 0, st>>>(f);
-    }
+    e = launch("full_decode_split", decode_split_kernel<TR, DD, true>, dim3(p.units * p.nsplit), dim3(256), 0, st,
+               a);
+    if (e == hipSuccess)
+      e = launch("full_decode_finish", decode_full_finish_kernel<TR, DD>, dim3(p.units * (g.G + f.nchunk)),
+                 dim3(256), 0, st, f);
   });
-  return hipGetLastError();
+  return e;
 }
 
 hipError_t launch_sparse_rows(const Geom& g, const void* q, const void* k, const void* v,
@@ -909,17 +907,13 @@ hipError_t launch_sparse_rows(const Geom& g, const void* q, const void* k, const
   a.gate = gate;
   a.win = win;
   a.out = out;
+  hipError_t e = hipSuccess;
   HYS_DISPATCH(g, {
-    {
-      TraceScope ts(st, "sparse_decode");
-      decode_split_kernel<TR, DD, false><<<p.units * p.nsplit, 256, 0, st>>>(a);
-    }
-    {
-      TraceScope ts(st, "sparse_merge");
-      sparse_merge_kernel<TR, DD><<<p.units * g.G, DD, 0, st>>>(a);
-    }
+    e = launch("sparse_decode", decode_split_kernel<TR, DD, false>, dim3(p.units * p.nsplit), dim3(256), 0, st, a);
+    if (e == hipSuccess)
+      e = launch("sparse_merge", sparse_merge_kernel<TR, DD>, dim3(p.units * g.G), dim3(DD), 0, st, a);
   });
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace hys

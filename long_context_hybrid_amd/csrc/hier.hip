@@ -289,12 +289,12 @@ hipError_t launch_hier_pool(const Geom& g, const void* k, int block, int m_begin
   if (m_end <= m_begin) return hipSuccess;
   const int nm = m_end - m_begin;
   const int64_t kbs = kbar_blocks * g.Hkv * g.D;
+  hipError_t e = hipSuccess;
   HIER_DT({
-    TraceScope ts(st, "hier_pool_keys");
-    pool_keys_kernel<TR, DD><<<g.B * nm * g.Hkv, 256, 0, st>>>(k, g.ks_b, g.ks_t, g.ks_h, g.Tkv, g.Hkv, m_begin, nm,
-                                                               block, kbar, kbs);
+    e = launch("hier_pool_keys", pool_keys_kernel<TR, DD>, dim3(g.B * nm * g.Hkv), dim3(256), 0, st, k, g.ks_b,
+               g.ks_t, g.ks_h, g.Tkv, g.Hkv, m_begin, nm, block, kbar, kbs);
   });
-  return hipGetLastError();
+  return e;
 }
 
 hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const float* kbar_in, int64_t kbar_blocks,
@@ -315,36 +315,32 @@ hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const
     kbar = w.kbar;
     kbs = (int64_t)M * g.Hkv * g.D;
   }
+  e = hipSuccess;
   HIER_DT({
-    {
-      TraceScope ts(st, "hier_block_logits");
-      block_logits_kernel<TR, DD><<<rows * ((M + 63) / 64), 256, 0, st>>>(q, g.qs_b, g.qs_h, kbar, kbs, g.Hkv, g.G,
-                                                                            M, sl2, w.logit2);
-    }
-    {
-      TraceScope ts(st, "hier_block_softmax");
-      block_softmax_kernel<<<rows, 256, 0, st>>>(w.logit2, g.G, M, bscore);
-    }
+    e = launch("hier_block_logits", block_logits_kernel<TR, DD>, dim3(rows * ((M + 63) / 64)), dim3(256), 0, st, q,
+               g.qs_b, g.qs_h, kbar, kbs, g.Hkv, g.G, M, sl2, w.logit2);
   });
+  if (e != hipSuccess) return e;
+  if ((e = launch("hier_block_softmax", block_softmax_kernel, dim3(rows), dim3(256), 0, st, w.logit2, g.G, M,
+                  bscore)) != hipSuccess)
+    return e;
   ValidLen all{nullptr, M, 0, 1, 1, 1, 1};
   if ((e = launch_topk(bscore, rows, M, M, all, n_keep, blk, w.topk_ws, st)) != hipSuccess) return e;
   const int64_t ncand = (int64_t)n_keep * block;
   {
-    TraceScope ts(st, "hier_gather");
     int gx = (int)((ncand + 255) / 256);
     if (gx > 64) gx = 64;
-    gather_candidates_kernel<<<dim3(gx, rows), 256, 0, st>>>(scores, g.Tkv, blk, n_keep, block, w.cand, w.valid);
+    if ((e = launch("hier_gather", gather_candidates_kernel, dim3(gx, rows), dim3(256), 0, st, scores, g.Tkv, blk,
+                    n_keep, block, w.cand, w.valid)) != hipSuccess)
+      return e;
   }
   ValidLen vl{w.valid, (int32_t)ncand, 0, 1, 1, 1, 1};
   if ((e = launch_topk(w.cand, rows, (int32_t)ncand, ncand, vl, k_top, w.pos, w.topk_ws, st)) != hipSuccess) return e;
-  {
-    TraceScope ts(st, "hier_map");
-    const int64_t n = (int64_t)rows * k_top;
-    int gb = (int)((n + 255) / 256);
-    if (gb > 4096) gb = 4096;
-    map_positions_kernel<<<gb, 256, 0, st>>>(w.pos, blk, n_keep, block, k_top, n, idx);
-  }
-  return hipGetLastError();
+  const int64_t n = (int64_t)rows * k_top;
+  int gb = (int)((n + 255) / 256);
+  if (gb > 4096) gb = 4096;
+  return launch("hier_map", map_positions_kernel, dim3(gb), dim3(256), 0, st, w.pos, blk, n_keep, block, k_top, n,
+                idx);
 }
 
 #undef HIER_DT

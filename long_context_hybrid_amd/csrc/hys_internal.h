@@ -2,9 +2,12 @@
 // translation units.  Plain structs passed by value to the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <utility>
 
 namespace hys {
 
@@ -47,15 +50,24 @@ __host__ __device__ inline int32_t valid_len_of(const ValidLen& v, int64_t row) 
 
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
-// Kernel-level event tracing (see hysparse_trace_begin): every launch site
-// wraps its kernel launch in a TraceScope.
-void trace_pre(hipStream_t st, const char* name);
-void trace_post(hipStream_t st);
-struct TraceScope {
-  hipStream_t st;
-  TraceScope(hipStream_t s, const char* name) : st(s) { trace_pre(s, name); }
-  ~TraceScope() { trace_post(st); }
-};
+// Kernel-level event tracing (see hysparse_trace_begin).  Every kernel goes
+// through launch(): while a trace is active on the calling thread and has room,
+// trace_slot hands out the next (start, stop) event pair and records the
+// kernel's name, and the kernel is launched with hipExtLaunchKernelGGL, which
+// stamps the two events with the dispatch's own begin and end times (no
+// marker packets between kernels); otherwise it is an ordinary launch.
+bool trace_slot(const char* name, hipEvent_t* start, hipEvent_t* stop);
+
+template <typename... KArgs, typename... Args>
+hipError_t launch(const char* name, void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t smem, hipStream_t st,
+                  Args&&... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (trace_slot(name, &e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, smem, st, e0, e1, 0, std::forward<Args>(args)...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, smem, st, std::forward<Args>(args)...);
+  return hipGetLastError();
+}
 
 // ---------------------------------------------------------------- decode path
 // Split-K attention of one query row per (batch, KV group) unit against a key

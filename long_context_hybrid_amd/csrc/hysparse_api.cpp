@@ -19,7 +19,6 @@ thread_local std::string g_err;
 thread_local hipEvent_t* t_events = nullptr;
 thread_local int32_t t_capacity = 0;
 thread_local int32_t t_count = 0;
-thread_local const char* t_current = "";
 thread_local std::vector<const char*> t_names;
 
 hys_status fail(hys_status s, const std::string& msg) {
@@ -163,16 +162,13 @@ hys_status scratch_on_current_device(void** ptr) {
 }  // namespace
 
 namespace hys {
-void trace_pre(hipStream_t st, const char* name) {
-  t_current = name;
-  if (t_events && 2 * t_count + 1 < t_capacity) (void)hipEventRecord(t_events[2 * t_count], st);
-}
-void trace_post(hipStream_t st) {
-  if (t_events && 2 * t_count + 1 < t_capacity) {
-    (void)hipEventRecord(t_events[2 * t_count + 1], st);
-    t_names.push_back(t_current);
-    ++t_count;
-  }
+bool trace_slot(const char* name, hipEvent_t* start, hipEvent_t* stop) {
+  if (!t_events || 2 * t_count + 1 >= t_capacity) return false;
+  *start = t_events[2 * t_count];
+  *stop = t_events[2 * t_count + 1];
+  t_names.push_back(name);
+  ++t_count;
+  return true;
 }
 }  // namespace hys
 

@@ -874,24 +874,26 @@ hipError_t launch_full_prefill(const Geom& g, const void* q, const void* k, cons
   a.scores = scores;
   a.SB = score_block;
   a.NB = (g.Tq + score_block - 1) / score_block;
+  hipError_t e = hipSuccess;
   HYS_PF_DISPATCH(g, {
     {
-      TraceScope ts(st, "full_prefill_fwd");
       constexpr bool kDma = HYS_FWD_DMA && TR::kBytes == 2 && DD == 128;
-      prefill_fwd_kernel<TR, DD, kFwdNW, kFwdRTW, kFwdWPE, kDma><<<a.nqt * g.B * g.Hkv * a.NHC, kFwdNW * 64, 0, st>>>(a);
+      e = launch("full_prefill_fwd", prefill_fwd_kernel<TR, DD, kFwdNW, kFwdRTW, kFwdWPE, kDma>,
+                 dim3(a.nqt * g.B * g.Hkv * a.NHC), dim3(kFwdNW * 64), 0, st, a);
     }
-    if (score_block == 64) {
-      TraceScope ts(st, "full_prefill_scores");
+    if (e != hipSuccess) {
+    } else if (score_block == 64) {
       constexpr bool kDma = HYS_SC_DMA && TR::kBytes == 2 && DD == 128;
-      prefill_block_scores_kernel<TR, DD, kScNW, kScRTW, kDma><<<a.NB * g.B * g.Hkv, kScNW * 64, 0, st>>>(a);
+      e = launch("full_prefill_scores", prefill_block_scores_kernel<TR, DD, kScNW, kScRTW, kDma>,
+                 dim3(a.NB * g.B * g.Hkv), dim3(kScNW * 64), 0, st, a);
     } else {
       a.nqb = (g.Tq + 15) / 16;
       a.nkr = (g.Tkv + 127) / 128;
-      TraceScope ts(st, "full_prefill_scores");
-      prefill_scores_kernel<TR, DD, 1, kScNW, kScRTW><<<a.nqb * g.B * g.Hkv * a.nkr, kScNW * 64, 0, st>>>(a);
+      e = launch("full_prefill_scores", prefill_scores_kernel<TR, DD, 1, kScNW, kScRTW>,
+                 dim3(a.nqb * g.B * g.Hkv * a.nkr), dim3(kScNW * 64), 0, st, a);
     }
   });
-  return hipGetLastError();
+  return e;
 }
 
 size_t sparse_block_ws_bytes(const Geom&, int, int) { return 0; }
@@ -912,11 +914,11 @@ hipError_t launch_sparse_block(const Geom& g, const void* q, const void* k, cons
   a.nrc = (4 * g.G + kSpNW * kSpRTW - 1) / (kSpNW * kSpRTW);
   const int units = g.B * g.Hkv * a.NB;
   const int grid = ((units + 7) / 8) * 8 * a.nrc;
+  hipError_t e = hipSuccess;
   HYS_PF_DISPATCH(g, {
-    TraceScope ts(st, "sparse_prefill");
-    sparse_block_kernel<TR, DD, kSpNW, kSpRTW><<<grid, kSpNW * 64, 0, st>>>(a);
+    e = launch("sparse_prefill", sparse_block_kernel<TR, DD, kSpNW, kSpRTW>, dim3(grid), dim3(kSpNW * 64), 0, st, a);
   });
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace hys

@@ -577,11 +577,7 @@ hipError_t launch_topk(const float* scores, int64_t n_rows, int32_t row_len, int
   a.k = k;
   a.idx = idx;
   a.nparts = topk_parts(n_rows, row_len);
-  TraceScope ts(st, "topk");
-  if (a.nparts == 1) {
-    topk_row_kernel<<<(unsigned)n_rows, kNT, 0, st>>>(a);
-    return hipGetLastError();
-  }
+  if (a.nparts == 1) return launch("topk", topk_row_kernel, dim3((unsigned)n_rows), dim3(kNT), 0, st, a);
   const size_t slots = (size_t)n_rows * a.nparts;
   unsigned char* c = static_cast<unsigned char*>(ws);
   a.pkey = reinterpret_cast<uint32_t*>(c);
@@ -590,9 +586,9 @@ hipError_t launch_topk(const float* scores, int64_t n_rows, int32_t row_len, int
   c += align_up(slots * kCap * sizeof(uint32_t));
   a.pcnt = reinterpret_cast<uint32_t*>(c);
   a.part_len = topk_part_len(row_len, a.nparts);
-  topk_part_kernel<<<(unsigned)slots, kNT, 0, st>>>(a);
-  topk_select_kernel<<<(unsigned)n_rows, kNT, 0, st>>>(a);
-  return hipGetLastError();
+  hipError_t e = launch("topk_part", topk_part_kernel, dim3((unsigned)slots), dim3(kNT), 0, st, a);
+  if (e != hipSuccess) return e;
+  return launch("topk_select", topk_select_kernel, dim3((unsigned)n_rows), dim3(kNT), 0, st, a);
 }
 
 }  // namespace hys

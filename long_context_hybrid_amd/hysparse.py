@@ -370,13 +370,14 @@ def hysparse_hier_select_pooled(q, k, kbar, scores, block: int, n_keep: int, k_t
 
 
 class KernelTrace:
-    """Per-kernel HIP-event timing through the library's trace hook.
+    """Per-kernel timing through the library's trace hook.
 
-    Events are recorded by the library on the stream each kernel is launched
-    on, immediately before and after the kernel.  Usage::
+    While the trace is active the library launches each kernel with a pair of
+    these events, which take the dispatch's own begin and end times.  Usage::
 
         tr = KernelTrace(capacity_kernels=4096)
         tr.begin(); ...library calls...; rows = tr.end()   # [(name, ms), ...]
+        tr.span_ms(0, 1)   # begin of kernel 0 to end of kernel 1
     """
 
     def __init__(self, capacity_kernels: int):
@@ -407,7 +408,18 @@ class KernelTrace:
             if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.events[2 * i], self.events[2 * i + 1]) != 0:
                 raise RuntimeError("hipEventElapsedTime failed")
             out.append((names[i], float(ms.value)))
+        self.count = n
         return out
+
+    def span_ms(self, i: int, j: int) -> float:
+        """Milliseconds from the begin of traced kernel i to the end of kernel
+        j of the last trace (after end())."""
+        if not (0 <= i <= j < getattr(self, "count", 0)):
+            raise IndexError("kernel index outside the last trace")
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.events[2 * i], self.events[2 * j + 1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
 
     def __del__(self):
         try:
