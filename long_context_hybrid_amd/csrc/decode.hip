@@ -778,16 +778,20 @@ DecodePlan plan_full_decode(const Geom& g) {
 #define HYS_SPARSE_GSPLITS 48
 #endif
 
-// Split-kernel workgroups resident at once (two per CU at its register
-// budget, 256 CUs).  When the units would need a few rounds of them, fewer
-// and longer global splits keep every workgroup in the first round, its
-// waves pipelining their steps, instead of a second round of single-step
-// waves (decode, batch 16, 8K context: 23.7 -> 21.8 us per sparse layer;
-// batch 4 at 128K keeps its 16 global splits).  When not even one global
-// split per unit fits (per-query prefill: tens of thousands of units), the
-// default splits stay: one long split per unit measured 6.24 vs 5.12 ms at
-// 8K queries.
-constexpr int kSparseResidentWGs = 512;
+// Split-kernel workgroups resident at once: the instantiation's workgroups
+// per CU at its register budget (__launch_bounds__: two for bf16, one for
+// fp32) times the 256 CUs of gfx950.  A compile-time figure, not a device
+// query, because the same plan sizes the workspace on hosts without a GPU.
+// When the units would need a few rounds of split workgroups, fewer and
+// longer global splits keep every workgroup in the first round, its waves
+// pipelining their steps, instead of a second round of single-step waves
+// (decode, batch 16, 8K context: 23.7 -> 21.8 us per sparse layer; batch 4
+// at 128K keeps its 16 global splits).  The cap applies only while at least
+// two global splits per unit fit: one long split per unit was measured
+// slower (per-query prefill at 8K queries: 6.24 vs 5.12 ms with the default
+// splits).
+constexpr int kGfx950CUs = 256;
+inline int sparse_resident_wgs(const Geom& g) { return kGfx950CUs * (g.dtype == 1 ? 2 : 1); }
 
 DecodePlan plan_sparse_rows(const Geom& g, int k_top, int window) {
   // at most HYS_SPARSE_GSPLITS (<= 48) global and 16 window splits
@@ -801,8 +805,8 @@ DecodePlan plan_sparse_rows(const Geom& g, int k_top, int window) {
   p.wchunk = cw;
   const int nw = (window + cw - 1) / cw;
   int gs = HYS_SPARSE_GSPLITS;
-  const int fit = kSparseResidentWGs / p.units - nw;
-  if (fit >= 1 && fit < gs) gs = fit;
+  const int fit = sparse_resident_wgs(g) / p.units - nw;
+  if (fit >= 2 && fit < gs) gs = fit;
   int cg = (k_top + gs - 1) / gs;
   cg = (cg + quantum - 1) / quantum * quantum;
   p.chunk = cg;

@@ -36,6 +36,10 @@ DECODE_CASES = {
     "chunk_exact": W["decode128k"].replace(batch=1, kv_len=2048, k_top=256, n_sparse=1, n_planted=4),
     "chunk_plus1": W["decode128k"].replace(batch=1, kv_len=1025, k_top=128, n_sparse=1, n_planted=4),
     "step_plus1_g8": W["decode8k"].replace(batch=2, kv_len=33, k_top=16, window=8, n_sparse=1),
+    # 128 units (batch 32 x 4 KV heads): the split plan caps the global
+    # splits so that the split workgroups fit one resident round (3 splits of
+    # 384 entries here), with a K that is not a multiple of the split
+    "capped_splits_128_units": W["decode128k"].replace(batch=32, kv_len=3000, k_top=777, n_sparse=1, n_planted=4),
     # fp32 with head_dim 128 (no other case covers this instantiation)
     "f32_d128_g4": W["tiny"].replace(batch=2, q_len=1, kv_len=1300, n_q_heads=8, n_kv_heads=2, head_dim=128,
                                      std=1.0 / np.sqrt(128.0), k_top=200, window=64, n_sparse=2),
