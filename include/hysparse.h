@@ -349,6 +349,28 @@ const char* hysparse_last_error(void);
 int32_t hysparse_version(void);
 
 /*
+ * Index-set check, a debugging aid for callers that build index rows for the
+ * sparse layer themselves (the sparse layer requires distinct entries: a key
+ * listed twice would enter the global branch's softmax twice; see
+ * hysparse_sparse_attn).  Nothing traps; for each row r of idx (int32
+ * [n_rows, k], rows k apart) status[r] (int32, device) gets the OR of:
+ *   HYS_IDX_DUPLICATE     a non-negative entry below row_len appears twice;
+ *   HYS_IDX_OUT_OF_RANGE  an entry is below -1, or not below the row's
+ *                         candidate count (valid_len[r] clamped to
+ *                         [0, row_len], or row_len when valid_len is NULL);
+ *                         the sparse layer skips or masks such entries;
+ *   HYS_IDX_ORDER         the row is not in the form hysparse_topk writes
+ *                         (non-negative entries strictly ascending, -1
+ *                         padding only after them); the sparse layer accepts
+ *                         any order.
+ * A row written by hysparse_topk has status 0.  Requires 1 <= row_len <=
+ * 524288 (HYS_ERR_UNSUPPORTED otherwise), k >= 1, 0 <= n_rows < 2^31.
+ */
+enum { HYS_IDX_DUPLICATE = 1, HYS_IDX_OUT_OF_RANGE = 2, HYS_IDX_ORDER = 4 };
+hys_status hysparse_check_indices(const int32_t* idx, int64_t n_rows, int32_t k, int32_t row_len,
+                                  const int32_t* valid_len, int32_t* status, hipStream_t stream);
+
+/*
  * Measurement helpers (not part of the computation): size-matched bandwidth
  * ceilings.  A decode-time sparse layer moves a few tens of MB per launch,
  * too little for one launch to reach the HBM peak; these kernels give what a

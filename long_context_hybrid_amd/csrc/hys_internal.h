@@ -149,6 +149,12 @@ hipError_t launch_hier_select(const Geom& g, const void* q, const void* k, const
 hipError_t launch_hier_pool(const Geom& g, const void* k, int block, int m_begin, int m_end, float* kbar,
                             int64_t kbar_blocks, hipStream_t st);
 
+// Index-set check (check.hip): status bits of one row.
+constexpr uint32_t kIdxDuplicate = 1, kIdxOutOfRange = 2, kIdxOrder = 4;
+int check_indices_max_row_len();
+hipError_t launch_check_indices(const int32_t* idx, int64_t n_rows, int k, int row_len, const ValidLen& vl,
+                                int32_t* status, hipStream_t st);
+
 // Bandwidth ceilings of one launch (ceiling.hip): sink holds one word per
 // workgroup.
 int64_t ceiling_stream_blocks(int64_t n_bytes);

@@ -464,6 +464,22 @@ size_t hysparse_topk_workspace_bytes(int64_t n_rows, int32_t row_len, int32_t k)
   return hys::topk_ws_bytes(n_rows, row_len, k);
 }
 
+hys_status hysparse_check_indices(const int32_t* idx, int64_t n_rows, int32_t k, int32_t row_len,
+                                  const int32_t* valid_len, int32_t* status, hipStream_t stream) {
+  static_assert(hys::kIdxDuplicate == HYS_IDX_DUPLICATE && hys::kIdxOutOfRange == HYS_IDX_OUT_OF_RANGE &&
+                    hys::kIdxOrder == HYS_IDX_ORDER,
+                "status bits");
+  if (n_rows < 0 || n_rows > INT32_MAX || k < 1) return fail(HYS_ERR_BAD_SHAPE, "need 0 <= n_rows < 2^31 and k >= 1");
+  if (row_len < 1 || row_len > hys::check_indices_max_row_len())
+    return fail(HYS_ERR_UNSUPPORTED, "row_len must be in [1, " + std::to_string(hys::check_indices_max_row_len()) + "]");
+  if (n_rows == 0) return ok();
+  hys_status s;
+  if ((s = check_tensor(idx, "idx", 4)) || (s = check_tensor(status, "status", 4))) return s;
+  if (valid_len && !aligned(valid_len, 4)) return fail(HYS_ERR_ALIGN, "valid_len is not 4-byte aligned");
+  hys::ValidLen vl{valid_len, row_len, 0, 1, 1, 1, 1};
+  return from_hip(hys::launch_check_indices(idx, n_rows, k, row_len, vl, status, stream));
+}
+
 size_t hysparse_ceiling_workspace_bytes(int64_t n_bytes, int64_t n_rows) {
   if (n_bytes < 0 || n_rows < 0) return 0;
   const int64_t a = hys::ceiling_stream_blocks(n_bytes), b = hys::ceiling_gather_blocks(n_rows);

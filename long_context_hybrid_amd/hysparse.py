@@ -31,7 +31,8 @@ EXPORTS = ("hysparse_full_attn_scores", "hysparse_topk", "hysparse_sparse_attn",
            "hysparse_trace_name", "hysparse_hier_select", "hysparse_hier_workspace_bytes", "hysparse_append_kv",
            "hysparse_sparse_attn_token_gate", "hysparse_sparse_attn_ex", "hysparse_hier_pool",
            "hysparse_hier_select_pooled", "hysparse_ceiling_workspace_bytes", "hysparse_ceiling_stream_read",
-           "hysparse_ceiling_gather", "hysparse_sparse_attn_noalloc", "hysparse_noalloc_scratch_bytes")
+           "hysparse_ceiling_gather", "hysparse_sparse_attn_noalloc", "hysparse_noalloc_scratch_bytes",
+           "hysparse_check_indices")
 
 
 class HysWindowKV(ctypes.Structure):
@@ -101,6 +102,8 @@ def lib() -> ctypes.CDLL:
     L.hysparse_sparse_attn_noalloc.restype = i32
     L.hysparse_noalloc_scratch_bytes.argtypes = []
     L.hysparse_noalloc_scratch_bytes.restype = sz
+    L.hysparse_check_indices.argtypes = [_P, i64, i32, i32, _P, _P, _P]
+    L.hysparse_check_indices.restype = i32
     L.hysparse_ceiling_workspace_bytes.argtypes = [i64, i64]
     L.hysparse_ceiling_workspace_bytes.restype = sz
     L.hysparse_ceiling_stream_read.argtypes = [_P, i64, _P, sz, _P]
@@ -512,3 +515,21 @@ def hysparse_ceiling_gather(k, v, rows, workspace=None):
     ws = _workspace(hysparse_ceiling_workspace_bytes(0, rows.numel()), dev, workspace)
     _check(lib().hysparse_ceiling_gather(_ptr(k), _ptr(v), row_bytes, n_buf, _ptr(rows), rows.numel(), row_bytes,
                                          _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)))
+
+
+HYS_IDX_DUPLICATE, HYS_IDX_OUT_OF_RANGE, HYS_IDX_ORDER = 1, 2, 4
+
+
+def hysparse_check_indices(idx, row_len: int, valid_len=None, status=None):
+    """Status bits of each index row (HYS_IDX_*; 0 = a valid top-K row) of a
+    contiguous int32 tensor whose last axis holds the rows."""
+    dev = _same_device(idx)
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.dim() < 1:
+        raise ValueError("idx must be a contiguous int32 tensor")
+    k = idx.shape[-1]
+    R = idx.numel() // k
+    if valid_len is not None and (valid_len.dtype != torch.int32 or valid_len.numel() != R):
+        raise ValueError("valid_len must be int32 with one entry per row")
+    status = torch.empty(idx.shape[:-1], dtype=torch.int32, device=dev) if status is None else status
+    _check(lib().hysparse_check_indices(_ptr(idx), R, k, row_len, _ptr(valid_len), _ptr(status), _stream(dev)))
+    return status

@@ -112,6 +112,11 @@ int main() {
                                      1 << 30, nullptr), 2, "pooled select, too few pooled blocks");
   expect(hysparse_append_kv(&d, P, P, 1, 256, P, P, nullptr), 2, "append past capacity");
   expect(hysparse_append_kv(&d, P, P, 0, 0, P, P, nullptr), 2, "append nothing");
+  // index-set check
+  expect(hysparse_check_indices((int32_t*)P, 4, 0, 100, nullptr, (int32_t*)P, nullptr), 2, "check k 0");
+  expect(hysparse_check_indices((int32_t*)P, 4, 8, (1 << 19) + 1, nullptr, (int32_t*)P, nullptr), 3,
+         "check row_len");
+  expect(hysparse_check_indices(nullptr, 4, 8, 100, nullptr, (int32_t*)P, nullptr), 1, "check idx null");
   // measurement helpers
   expect(hysparse_ceiling_stream_read(P, 100, P, 1 << 20, nullptr), 2, "stream bytes % 16");
   expect(hysparse_ceiling_gather(P, P, 256, 100, (int32_t*)P, 10, 512, P, 1 << 20, nullptr), 3, "gather row bytes");

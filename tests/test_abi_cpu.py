@@ -246,3 +246,14 @@ def test_noalloc_validation():
     assert need > L.hysparse_noalloc_scratch_bytes()
     assert call(big, kt=2048, w=128) == 5
     assert b"fixed scratch" in L.hysparse_last_error()
+
+
+def test_check_indices_validation():
+    L = hy.lib()
+    assert L.hysparse_check_indices(FAKE, -1, 8, 100, None, FAKE, None) == 2
+    assert L.hysparse_check_indices(FAKE, 4, 0, 100, None, FAKE, None) == 2
+    assert L.hysparse_check_indices(FAKE, 4, 8, 0, None, FAKE, None) == 3
+    assert L.hysparse_check_indices(FAKE, 4, 8, (1 << 19) + 1, None, FAKE, None) == 3
+    assert L.hysparse_check_indices(None, 4, 8, 100, None, FAKE, None) == 1
+    assert L.hysparse_check_indices(FAKE, 4, 8, 100, ctypes.c_void_p(0x10002), FAKE, None) == 4
+    assert L.hysparse_check_indices(FAKE, 0, 8, 100, None, None, None) == 0   # empty: no-op
