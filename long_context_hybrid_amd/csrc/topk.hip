@@ -436,16 +436,22 @@ __global__ __launch_bounds__(kNT) void topk_part_kernel(TopkArgs a) {
   if (n <= a.k || n <= kCap) return;  // the select kernel takes the row whole
   const float* srow = a.scores + row * a.row_stride;
   const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
+  const int pend = min(n, (p + 1) * a.part_len);
+  // the part's first kPartLen keys are loaded before the threshold is formed,
+  // so their round trip overlaps the sample's
+  const int jf = p * a.part_len + 4 * t;
+  const bool first_vec = vec && jf + 4 <= pend;
+  float4 first = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (first_vec) first = *reinterpret_cast<const float4*>(srow + jf);
   const uint32_t t0 = sample_threshold(srow, n, kk, sm);
   const int64_t slot = row * a.nparts + p;
   uint32_t* okey = a.pkey + slot * kCap;
   int32_t* oidx = a.pidx + slot * kCap;
-  const int pend = min(n, (p + 1) * a.part_len);
   uint32_t C = 0;
   for (int j0 = p * a.part_len + 4 * t, jb = p * a.part_len; jb < pend; j0 += kPartLen, jb += kPartLen) {
     uint32_t keys[4];
     if (vec && j0 + 4 <= pend) {
-      const float4 x = *reinterpret_cast<const float4*>(srow + j0);
+      const float4 x = j0 == jf ? first : *reinterpret_cast<const float4*>(srow + j0);
       keys[0] = order_key(x.x);
       keys[1] = order_key(x.y);
       keys[2] = order_key(x.z);
@@ -494,6 +500,21 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkArgs a) {
     select_short_row(srow, n, kk, out, sm);
     return;
   }
+  // part-major copy below: tpp threads per part; its first kU rounds of
+  // survivor loads are issued before the counts are known (indices clamped
+  // to the part's workspace slot), so both round trips overlap
+  const int tpp = kNT / a.nparts;
+  const int pp = t / tpp, r = t - pp * tpp;
+  const int64_t base = (row * a.nparts + (pp < a.nparts ? pp : 0)) * kCap;
+  constexpr int kU = 8;
+  uint32_t kv[kU];
+  int32_t iv[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int i = min(r + u * tpp, kCap - 1);
+    kv[u] = a.pkey[base + i];
+    iv[u] = a.pidx[base + i];
+  }
   if (t < 64) {  // one lane per part (nparts <= 64): counts, then an exclusive scan
     const uint32_t c = t < a.nparts ? a.pcnt[row * a.nparts + t] : 0u;
     const uint32_t x = wave_inclusive_scan(c);
@@ -504,24 +525,11 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkArgs a) {
   __syncthreads();
   const uint32_t C = pstart[a.nparts];
   if (C <= (uint32_t)kCap && C >= kk) {
-    // part-major copy: tpp threads per part move its survivors to their
-    // place in the concatenated list (part order); the first kU rounds are
-    // unrolled with clamped indices, so those loads are all in flight
-    // together, and a part with more survivors finishes in a loop
-    const int tpp = kNT / a.nparts;
-    const int pp = t / tpp, r = t - pp * tpp;
+    // part-major copy: each part's survivors to their place in the
+    // concatenated list (part order); a part with more survivors than the
+    // first kU rounds finishes in a loop
     if (pp < a.nparts) {
       const uint32_t c0 = pstart[pp], cnt = pstart[pp + 1] - c0;
-      const int64_t base = (row * a.nparts + pp) * kCap;
-      constexpr int kU = 8;
-      uint32_t kv[kU];
-      int32_t iv[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const uint32_t i = min((uint32_t)(r + u * tpp), cnt > 0u ? cnt - 1u : 0u);
-        kv[u] = a.pkey[base + i];
-        iv[u] = a.pidx[base + i];
-      }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const uint32_t i = r + u * tpp;
