@@ -7,24 +7,28 @@
 // ascending index order, padded with -1 when a row has fewer than K
 // candidates.
 //
-// One workgroup (1024 threads) per row.  When there are few long rows (decode:
-// a handful of rows of the whole context) the candidate filter of step 1 is
-// spread over `nparts` workgroups per row, each writing the survivors of its
-// part of the row, in index order, to its own workspace region; a second
-// kernel concatenates the regions in part order and runs steps 2 and 3.
-// Both forms select exactly the same indices.
+// One workgroup per row, in one of two sizes (TopkCfg): many rows (prefill:
+// one row per (KV group, 64-query block)) run in 256-thread workgroups, four
+// per CU, so that the rows' barrier-separated phases overlap; few rows run in
+// 1024-thread workgroups.  When there are few long rows (decode: a handful of
+// rows of the whole context) the candidate filter of step 1 is spread over
+// `nparts` workgroups per row, each writing the survivors of its part of the
+// row, in index order, to its own workspace region; a second kernel
+// concatenates the regions in part order and runs steps 2 and 3.  Every form
+// selects exactly the same indices.
 //
 // 1. Candidate filter.  A row longer than the LDS candidate capacity is first
-//    sampled (64 evenly spread runs of 64 keys); a radix select on the
-//    sample gives a threshold t0, the sample key of rank about twice the
-//    expected rank of the K-th largest key.  One pass over the row keeps every key >= t0, in index
-//    order, in LDS.  If at least K keys survive, the exact top K are among
-//    them (every key outside is below t0, hence below the K-th largest), so
-//    the result is exact whatever the sample was; otherwise, or if too many
-//    survive, the row falls back to a radix select over the whole row.
+//    sampled (evenly spread runs of 64 keys); a radix select on the sample
+//    gives a threshold t0, the sample key whose rank is a fixed multiple of
+//    the expected rank of the K-th largest key.  One pass over the row keeps
+//    every key >= t0, in index order, in LDS.  If at least K keys survive,
+//    the exact top K are among them (every key outside is below t0, hence
+//    below the K-th largest), so the result is exact whatever the sample
+//    was; otherwise, or if too many survive, the row falls back to a radix
+//    select over the whole row.
 // 2. Exact select: radix select of the K-th largest key T over an LDS
-//    histogram, with 12-bit digits of (key - min) taken over the range the
-//    keys actually span (at most three passes).
+//    histogram, with digits of (key - min) taken over the range the keys
+//    actually span.
 // 3. Index-order compaction with one block-wide scan:
 //      position(j) = #{j' < j : key > T} + min(#{j' < j : key == T}, k_rem)
 //    where k_rem is the number of keys equal to T that belong to the top K,
@@ -36,18 +40,52 @@ namespace hys {
 
 namespace {
 
-constexpr int kNT = 1024;          // threads per row
-constexpr int kEPT = 16;           // row elements per thread per segment
-constexpr int kSeg = kNT * kEPT;   // 16384
-constexpr int kCap = 12288;        // candidate capacity (LDS)
-constexpr int kRuns = 64;          // sample: kRuns runs of kRunLen keys
-constexpr int kRunLen = 64;
-constexpr int kNS = kRuns * kRunLen;
-constexpr int kBins = 4096;
-constexpr int kPartLen = 4096;     // parallel filter: keys per part pass (kNT x 4)
+constexpr int kRunLen = 64;        // sample: runs of kRunLen consecutive keys
 constexpr int kPartRows = 256;     // rows below which long rows are filtered in parts
 constexpr int kMaxParts = 64;
 constexpr int kPartWGs = 512;      // target workgroups of the parallel filter
+
+// Sizes of one row workgroup.
+template <int NT_, int CAP_, int DIGIT_, int NC_, int NS_LONG_, int QF4_, int QA_>
+struct TopkCfg {
+  static constexpr int NT = NT_;        // threads
+  static constexpr int EPT = 16;        // row elements per thread per segment
+  static constexpr int SEG = NT * EPT;
+  static constexpr int CAP = CAP_;      // candidate capacity (LDS)
+  static constexpr int DIGIT = DIGIT_;  // radix digit bits
+  static constexpr int BINS = 1 << DIGIT;
+  // histogram copies: thread t adds to copy t % NC (bin b, copy c at
+  // b * NC + c), so the equal bins of one instruction's lanes fall on
+  // different banks (a row's bulk often shares one bin)
+  static constexpr int NC = NC_;
+  // sample keys: NS, or NS_LONG for rows longer than LONG_ROW (a larger
+  // sample keeps the survivor count's spread small when the expected sample
+  // rank of the K-th key is small)
+  static constexpr int NS = 4096;
+  static constexpr int NS_LONG = NS_LONG_;
+  static constexpr int LONG_ROW = 65536;
+  // sample rank of the threshold: QF4 / 4 x the expected sample rank of the
+  // K-th largest key, plus QA
+  static constexpr int QF4 = QF4_, QA = QA_;
+  // after the first digit, a selected bin of at most RANKLIST keys is ranked
+  // directly (one key per thread)
+  static constexpr uint32_t RANKLIST = NT < 512 ? NT : 512;
+  static constexpr int PART_LEN = NT * 4;  // parallel filter: keys per part pass
+  static_assert(NS <= NS_LONG && NS_LONG <= 2 * CAP && NS % NT == 0 && NS_LONG % NT == 0 && CAP % NT == 0 &&
+                    BINS % NT == 0 && NS % kRunLen == 0 && NS_LONG % kRunLen == 0,
+                "top-K sizes");
+};
+// few rows, and the decode-time parts: 12288 candidates, 12-bit digits,
+// threshold at twice the expected rank of a 4096-key sample plus 32
+using BigCfg = TopkCfg<1024, 12288, 12, 1, 4096, 8, 32>;
+// many rows: 4096 candidates (37 KB of LDS: four workgroups per CU), 8-bit
+// digits over four histogram copies, threshold at 1.5 times the expected
+// sample rank, no slack: for K = 2048 the survivors (about 3072) stay between
+// K and the capacity by more than four standard deviations of the sample's
+// rank statistics (relative spread 1 / sqrt(rank)) up to 64K keys per row
+// with 4096 sample keys and up to 128K with 8192
+using SmallCfg = TopkCfg<256, 4096, 8, 4, 8192, 6, 0>;
+constexpr int64_t kSmallRows = 384;  // rows from which SmallCfg is used (with K <= its capacity / 2)
 
 struct TopkArgs {
   const float* scores;
@@ -57,37 +95,46 @@ struct TopkArgs {
   ValidLen vl;
   int32_t k;
   int32_t* idx;
-  // parallel filter: part p of row r keeps its survivors in
-  // pkey/pidx[(r * nparts + p) * kCap ...] and their number in pcnt[r * nparts + p]
+  // parallel filter (BigCfg): part p of row r keeps its survivors in
+  // pkey/pidx[(r * nparts + p) * CAP ...] and their number in pcnt[r * nparts + p]
   int nparts;
-  int part_len;  // multiple of kPartLen
+  int part_len;  // multiple of PART_LEN
   uint32_t* pkey;
   int32_t* pidx;
   uint32_t* pcnt;
 };
 
-// LDS of a row workgroup: the candidate list and the radix histogram.
-struct TopkSmem {
-  uint32_t ckey[kCap];
-  int32_t cidx[kCap];
-  uint32_t hist[kBins];
-  uint32_t wsum[kNT / 64];
-  uint32_t wmin[kNT / 64];
-  uint32_t wmax[kNT / 64];
+// LDS of a row workgroup: the candidate list (or, before the filter, the
+// sample) and the radix histogram.
+template <class C>
+struct RowSmem {
+  union {
+    struct {
+      uint32_t ckey[C::CAP];
+      int32_t cidx[C::CAP];
+    };
+    uint32_t samp[2 * C::CAP];
+  };
+  uint32_t hist[C::BINS * C::NC];
+  uint32_t wsum[C::NT / 64];
+  uint32_t wmin[C::NT / 64];
+  uint32_t wmax[C::NT / 64];
   uint32_t sel[4];
 };
 // LDS of a part workgroup: the sample only (several fit on one CU).
+template <class C>
 struct SampleSmem {
-  uint32_t ckey[kNS];
-  uint32_t hist[kBins];
-  uint32_t wsum[kNT / 64];
-  uint32_t wmin[kNT / 64];
-  uint32_t wmax[kNT / 64];
+  uint32_t samp[C::NS_LONG];
+  uint32_t hist[C::BINS * C::NC];
+  uint32_t wsum[C::NT / 64];
+  uint32_t wmin[C::NT / 64];
+  uint32_t wmax[C::NT / 64];
   uint32_t sel[4];
 };
 
 // Exclusive block-wide scan of one value per thread; returns the exclusive
 // prefix and the total.  Two barriers.
+template <class C>
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t x = wave_inclusive_scan(v);
@@ -95,7 +142,7 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint3
   __syncthreads();
   uint32_t pre = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kNT / 64; ++w) {
+  for (int w = 0; w < C::NT / 64; ++w) {
     const uint32_t s = wsum[w];
     pre += (w < wave) ? s : 0u;
     tot += s;
@@ -106,7 +153,7 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint3
 }
 
 // Block-wide min and max of one pair per thread (two barriers).
-template <class SM>
+template <class C, class SM>
 __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SM& sm, uint32_t* mn_out,
                                              uint32_t* mx_out) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -118,7 +165,7 @@ __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SM& sm, u
   __syncthreads();
   uint32_t a = 0xFFFFFFFFu, b = 0u;
 #pragma unroll
-  for (int w = 0; w < kNT / 64; ++w) {
+  for (int w = 0; w < C::NT / 64; ++w) {
     a = min(a, sm.wmin[w]);
     b = max(b, sm.wmax[w]);
   }
@@ -130,14 +177,12 @@ __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SM& sm, u
 // Radix select: the k-th largest key T over the keys the visitor hands to its
 // callback (this thread's keys), and the number k_rem of keys equal to T that
 // belong to the top k.  Requires 1 <= k <= number of keys.  The digits are
-// taken from r = key - min over the keys' own range (12 bits at a time from
-// the top of max - min), so the histogram bins are spread over the values
-// actually present.  After the first digit the keys of the selected bin are
-// usually few: up to kRankList of them are ranked directly in LDS instead of
-// running the remaining digit passes.
-constexpr uint32_t kRankList = 512;
-
-template <class Visit, class SM>
+// taken from r = key - min over the keys' own range (C::DIGIT bits at a time
+// from the top of max - min), so the histogram bins are spread over the
+// values actually present.  After the first digit the keys of the selected
+// bin are usually few: up to C::RANKLIST of them are ranked directly in LDS
+// instead of running the remaining digit passes.
+template <class C, class Visit, class SM>
 __device__ __forceinline__ void radix_select(uint32_t k, Visit visit, SM& sm, uint32_t* T_out,
                                              uint32_t* krem_out) {
   const int t = threadIdx.x;
@@ -147,39 +192,42 @@ __device__ __forceinline__ void radix_select(uint32_t k, Visit visit, SM& sm, ui
     hi = max(hi, u);
   });
   uint32_t base, top;
-  block_minmax(lo, hi, sm, &base, &top);
+  block_minmax<C>(lo, hi, sm, &base, &top);
   const uint32_t range = top - base;
   int s_hi = range == 0u ? 0 : 32 - __clz(range);  // every r = key - base is < 2^s_hi
   uint32_t P = 0, krem = k;                         // selected value of r >> s_hi
   while (s_hi > 0) {
-    const int s_lo = s_hi > 12 ? s_hi - 12 : 0;
+    const int s_lo = s_hi > C::DIGIT ? s_hi - C::DIGIT : 0;
     const uint32_t dmask = (1u << (s_hi - s_lo)) - 1u;
+    constexpr int BPT = C::BINS / C::NT;  // bins per thread
 #pragma unroll
-    for (int e = 0; e < kBins / kNT; ++e) sm.hist[t * (kBins / kNT) + e] = 0u;
+    for (int e = 0; e < BPT * C::NC; ++e) sm.hist[t * (BPT * C::NC) + e] = 0u;
     if (t == 0) sm.sel[2] = 0u;
     __syncthreads();
     visit([&](uint32_t u) {
       const uint32_t r = u - base;
-      if ((uint32_t)((uint64_t)r >> s_hi) == P) atomicAdd(&sm.hist[(r >> s_lo) & dmask], 1u);
+      if ((uint32_t)((uint64_t)r >> s_hi) == P) atomicAdd(&sm.hist[((r >> s_lo) & dmask) * C::NC + (t % C::NC)], 1u);
     });
     __syncthreads();
-    // thread t owns bins [4t, 4t + 4); count keys in higher bins
-    uint32_t c[kBins / kNT];
+    // thread t owns bins [BPT t, BPT (t + 1)); count keys in higher bins
+    uint32_t c[BPT];
     uint32_t tot = 0;
 #pragma unroll
-    for (int e = 0; e < kBins / kNT; ++e) {
-      c[e] = sm.hist[t * (kBins / kNT) + e];
+    for (int e = 0; e < BPT; ++e) {
+      c[e] = 0u;
+#pragma unroll
+      for (int x = 0; x < C::NC; ++x) c[e] += sm.hist[(t * BPT + e) * C::NC + x];
       tot += c[e];
     }
     uint32_t all;
-    const uint32_t below = block_scan(tot, sm.wsum, &all);
+    const uint32_t below = block_scan<C>(tot, sm.wsum, &all);
     const uint32_t above = all - below - tot;
     if (above < krem && krem <= above + tot) {
       uint32_t cum = above;
 #pragma unroll
-      for (int e = kBins / kNT - 1; e >= 0; --e) {
+      for (int e = BPT - 1; e >= 0; --e) {
         if (cum < krem && krem <= cum + c[e]) {
-          sm.sel[0] = (P << (s_hi - s_lo)) | (uint32_t)(t * (kBins / kNT) + e);
+          sm.sel[0] = (P << (s_hi - s_lo)) | (uint32_t)(t * BPT + e);
           sm.sel[1] = krem - cum;
           sm.sel[3] = c[e];  // keys in the selected bin
         }
@@ -192,7 +240,7 @@ __device__ __forceinline__ void radix_select(uint32_t k, Visit visit, SM& sm, ui
     const uint32_t nbin = sm.sel[3];
     __syncthreads();
     s_hi = s_lo;
-    if (s_hi > 0 && nbin <= kRankList) {
+    if (s_hi > 0 && nbin <= C::RANKLIST) {
       // the selected bin's keys into a list (hist reused), then rank them
       visit([&](uint32_t u) {
         const uint32_t r = u - base;
@@ -223,44 +271,48 @@ __device__ __forceinline__ void radix_select(uint32_t k, Visit visit, SM& sm, ui
   *krem_out = krem;
 }
 
-// Threshold t0 from a sample of the row (n > kCap): keys >= t0 include, in
-// expectation, about twice the top K.  Every workgroup of a row computes the
-// same value (same sample, same arithmetic).
-template <class SM>
+// Threshold t0 from an NS-key sample of the row (n > C::CAP): keys >= t0
+// include, in expectation, C::QF4 / 4 times the top K (plus the slack C::QA).
+// Every workgroup of a row computes the same value (same sample, same
+// arithmetic).
+template <class C, int NS, class SM>
 __device__ __forceinline__ uint32_t sample_threshold(const float* srow, int n, uint32_t kk, SM& sm) {
   const int t = threadIdx.x;
+  constexpr int RUNS = NS / kRunLen;
   // run r covers keys [base_r, base_r + kRunLen); runs are evenly spread.
   // Fixed trip count: all of a thread's loads are in flight together.
-  float v[kNS / kNT];
+  constexpr int SPT = NS / C::NT;
+  float v[SPT];
 #pragma unroll
-  for (int e = 0; e < kNS / kNT; ++e) {
-    const int s = t + e * kNT, r = s / kRunLen, o = s - r * kRunLen;
-    const int base = (int)((int64_t)r * (n - kRunLen) / (kRuns - 1));
+  for (int e = 0; e < SPT; ++e) {
+    const int s = t + e * C::NT, r = s / kRunLen, o = s - r * kRunLen;
+    const int base = (int)((int64_t)r * (n - kRunLen) / (RUNS - 1));
     v[e] = srow[base + o];
   }
 #pragma unroll
-  for (int e = 0; e < kNS / kNT; ++e) sm.ckey[t + e * kNT] = order_key(v[e]);
+  for (int e = 0; e < SPT; ++e) sm.samp[t + e * C::NT] = order_key(v[e]);
   __syncthreads();
-  // rank in the sample: twice the expected count of top-K keys, plus slack
-  int64_t q = ((int64_t)kk * kNS + n - 1) / n * 2 + 32;
-  if (q > kNS) q = kNS;
+  // rank in the sample: a multiple of the expected count of top-K keys, plus slack
+  int64_t q = ((int64_t)kk * NS + n - 1) / n * C::QF4 / 4 + C::QA;
+  if (q > NS) q = NS;
   uint32_t T0, r0;
-  radix_select((uint32_t)q, [&](auto f) {
+  radix_select<C>((uint32_t)q, [&](auto f) {
 #pragma unroll
-    for (int e = 0; e < kNS / kNT; ++e) f(sm.ckey[t + e * kNT]);
+    for (int e = 0; e < SPT; ++e) f(sm.samp[t + e * C::NT]);
   }, sm, &T0, &r0);
   return T0;  // the q-th largest sample key: keys >= t0 include the top q of the sample
 }
 
 // Steps 2 and 3 over the C candidates in sm.ckey / sm.cidx (index order).
-__device__ __forceinline__ void select_candidates(uint32_t C, uint32_t kk, int32_t* out, TopkSmem& sm) {
+template <class C>
+__device__ __forceinline__ void select_candidates(uint32_t nc, uint32_t kk, int32_t* out, RowSmem<C>& sm) {
   const int t = threadIdx.x;
   // thread t owns a contiguous run of candidates; an odd run length keeps the
   // lanes' strided LDS reads on distinct banks
-  const uint32_t per = ((C + kNT - 1) / kNT) | 1u;
-  const uint32_t c0 = min(C, t * per), c1 = min(C, c0 + per);
+  const uint32_t per = ((nc + C::NT - 1) / C::NT) | 1u;
+  const uint32_t c0 = min(nc, t * per), c1 = min(nc, c0 + per);
   uint32_t T, krem;
-  radix_select(kk, [&](auto f) {
+  radix_select<C>(kk, [&](auto f) {
     for (uint32_t c = c0; c < c1; ++c) f(sm.ckey[c]);
   }, sm, &T, &krem);
   uint32_t gt = 0, eq = 0;
@@ -269,8 +321,8 @@ __device__ __forceinline__ void select_candidates(uint32_t C, uint32_t kk, int32
     eq += sm.ckey[c] == T;
   }
   uint32_t tg, te;
-  uint32_t gb = block_scan(gt, sm.wsum, &tg);
-  uint32_t eb = block_scan(eq, sm.wsum, &te);
+  uint32_t gb = block_scan<C>(gt, sm.wsum, &tg);
+  uint32_t eb = block_scan<C>(eq, sm.wsum, &te);
   for (uint32_t c = c0; c < c1; ++c) {
     const uint32_t u = sm.ckey[c];
     const bool is_gt = u > T, is_eq = u == T;
@@ -281,33 +333,35 @@ __device__ __forceinline__ void select_candidates(uint32_t C, uint32_t kk, int32
   }
 }
 
-// this thread's kEPT consecutive keys of segment sg (0 past the row end)
-// A row of at most kCap keys is its own candidate list: coalesced loads
-// (thread t takes keys t, t + kNT, ...; clamped indices, so all are in
-// flight together) stored at their index in LDS (consecutive lanes,
-// consecutive words: no bank conflicts), then select_candidates.
+// A row of at most C::CAP keys is its own candidate list: coalesced loads
+// (thread t takes keys t, t + NT, ...; clamped indices, so all are in flight
+// together) stored at their index in LDS (consecutive lanes, consecutive
+// words: no bank conflicts), then select_candidates.
+template <class C>
 __device__ __forceinline__ void select_short_row(const float* srow, int n, uint32_t kk, int32_t* out,
-                                                 TopkSmem& sm) {
+                                                 RowSmem<C>& sm) {
   const int t = threadIdx.x;
-  constexpr int kB = kCap / kNT;  // 12 loads per thread
+  constexpr int kB = C::CAP / C::NT;  // loads per thread
   float v[kB];
 #pragma unroll
-  for (int e = 0; e < kB; ++e) v[e] = srow[min(t + e * kNT, n - 1)];
+  for (int e = 0; e < kB; ++e) v[e] = srow[min(t + e * C::NT, n - 1)];
 #pragma unroll
   for (int e = 0; e < kB; ++e)
-    if (t + e * kNT < n) {
-      sm.ckey[t + e * kNT] = order_key(v[e]);
-      sm.cidx[t + e * kNT] = t + e * kNT;
+    if (t + e * C::NT < n) {
+      sm.ckey[t + e * C::NT] = order_key(v[e]);
+      sm.cidx[t + e * C::NT] = t + e * C::NT;
     }
   __syncthreads();
-  select_candidates((uint32_t)n, kk, out, sm);
+  select_candidates<C>((uint32_t)n, kk, out, sm);
 }
 
-__device__ __forceinline__ void load_seg(const float* srow, int n, bool vec, int sg, uint32_t (&keys)[kEPT]) {
-  const int j0 = sg * kSeg + threadIdx.x * kEPT;
-  if (vec && j0 + kEPT <= n) {
+// this thread's C::EPT consecutive keys of segment sg (0 past the row end)
+template <class C>
+__device__ __forceinline__ void load_seg(const float* srow, int n, bool vec, int sg, uint32_t (&keys)[C::EPT]) {
+  const int j0 = sg * C::SEG + threadIdx.x * C::EPT;
+  if (vec && j0 + C::EPT <= n) {
 #pragma unroll
-    for (int e = 0; e < kEPT; e += 4) {
+    for (int e = 0; e < C::EPT; e += 4) {
       const float4 x = *reinterpret_cast<const float4*>(srow + j0 + e);
       keys[e] = order_key(x.x);
       keys[e + 1] = order_key(x.y);
@@ -316,43 +370,44 @@ __device__ __forceinline__ void load_seg(const float* srow, int n, bool vec, int
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < kEPT; ++e) keys[e] = (j0 + e < n) ? order_key(srow[j0 + e]) : 0u;
+    for (int e = 0; e < C::EPT; ++e) keys[e] = (j0 + e < n) ? order_key(srow[j0 + e]) : 0u;
   }
 }
 
 // Fallback: radix select and compaction over the whole row.
+template <class C>
 __device__ __forceinline__ void select_whole_row(const float* srow, int n, bool vec, uint32_t kk, int32_t* out,
-                                                 TopkSmem& sm) {
+                                                 RowSmem<C>& sm) {
   const int t = threadIdx.x;
-  const int nseg = (n + kSeg - 1) / kSeg;
+  const int nseg = (n + C::SEG - 1) / C::SEG;
   uint32_t T, krem;
-  radix_select(kk, [&](auto f) {
+  radix_select<C>(kk, [&](auto f) {
     for (int sg = 0; sg < nseg; ++sg) {
-      uint32_t keys[kEPT];
-      load_seg(srow, n, vec, sg, keys);
-      const int j0 = sg * kSeg + t * kEPT;
+      uint32_t keys[C::EPT];
+      load_seg<C>(srow, n, vec, sg, keys);
+      const int j0 = sg * C::SEG + t * C::EPT;
 #pragma unroll
-      for (int e = 0; e < kEPT; ++e)
+      for (int e = 0; e < C::EPT; ++e)
         if (j0 + e < n) f(keys[e]);
     }
   }, sm, &T, &krem);
   uint32_t g_base = 0, e_base = 0;
   for (int sg = 0; sg < nseg; ++sg) {
-    uint32_t keys[kEPT];
-    load_seg(srow, n, vec, sg, keys);
-    const int j0 = sg * kSeg + t * kEPT;
+    uint32_t keys[C::EPT];
+    load_seg<C>(srow, n, vec, sg, keys);
+    const int j0 = sg * C::SEG + t * C::EPT;
     uint32_t gt = 0, eq = 0;
 #pragma unroll
-    for (int e = 0; e < kEPT; ++e) {
+    for (int e = 0; e < C::EPT; ++e) {
       const bool in = j0 + e < n;
       gt += (in && keys[e] > T);
       eq += (in && keys[e] == T);
     }
     uint32_t tg, te;
-    uint32_t gb = g_base + block_scan(gt, sm.wsum, &tg);
-    uint32_t eb = e_base + block_scan(eq, sm.wsum, &te);
+    uint32_t gb = g_base + block_scan<C>(gt, sm.wsum, &tg);
+    uint32_t eb = e_base + block_scan<C>(eq, sm.wsum, &te);
 #pragma unroll
-    for (int e = 0; e < kEPT; ++e) {
+    for (int e = 0; e < C::EPT; ++e) {
       const bool in = j0 + e < n;
       const bool is_gt = in && keys[e] > T;
       const bool is_eq = in && keys[e] == T;
@@ -366,89 +421,94 @@ __device__ __forceinline__ void select_whole_row(const float* srow, int n, bool 
   }
 }
 
-__global__ __launch_bounds__(kNT) void topk_row_kernel(TopkArgs a) {
-  __shared__ TopkSmem sm;
+template <class C>
+__global__ __launch_bounds__(C::NT) void topk_row_kernel(TopkArgs a) {
+  __shared__ RowSmem<C> sm;
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x;
   const int n = valid_len_of(a.vl, row);
   const uint32_t kk = (uint32_t)a.k;
   int32_t* out = a.idx + row * a.k;
   if (n <= a.k) {  // every candidate is selected
-    for (int x = t; x < a.k; x += kNT) out[x] = x < n ? x : -1;
+    for (int x = t; x < a.k; x += C::NT) out[x] = x < n ? x : -1;
     return;
   }
   const float* srow = a.scores + row * a.row_stride;
-  if (n <= kCap) {  // the whole row is the candidate list: no filter
-    select_short_row(srow, n, kk, out, sm);
+  if (n <= C::CAP) {  // the whole row is the candidate list: no filter
+    select_short_row<C>(srow, n, kk, out, sm);
     return;
   }
   const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
-  const int nseg = (n + kSeg - 1) / kSeg;
+  const int nseg = (n + C::SEG - 1) / C::SEG;
 
   // ---- 1. threshold from a sample (rows longer than the capacity)
-  const uint32_t t0 = n > kCap ? sample_threshold(srow, n, kk, sm) : 0u;
+  const uint32_t t0 = (C::NS_LONG > C::NS && n > C::LONG_ROW) ? sample_threshold<C, C::NS_LONG>(srow, n, kk, sm)
+                                                              : sample_threshold<C, C::NS>(srow, n, kk, sm);
+  __syncthreads();  // the sample's LDS becomes the candidate list
 
   // ---- filter: keys >= t0 into LDS, index order
-  uint32_t C = 0;  // candidates kept (block-uniform)
+  uint32_t nc = 0;  // candidates kept (block-uniform)
   bool fits = true;
   for (int sg = 0; sg < nseg; ++sg) {
-    uint32_t keys[kEPT];
-    load_seg(srow, n, vec, sg, keys);
-    const int j0 = sg * kSeg + t * kEPT;
+    uint32_t keys[C::EPT];
+    load_seg<C>(srow, n, vec, sg, keys);
+    const int j0 = sg * C::SEG + t * C::EPT;
     uint32_t cnt = 0;
 #pragma unroll
-    for (int e = 0; e < kEPT; ++e) cnt += (j0 + e < n && keys[e] >= t0);
+    for (int e = 0; e < C::EPT; ++e) cnt += (j0 + e < n && keys[e] >= t0);
     uint32_t tot;
-    uint32_t off = C + block_scan(cnt, sm.wsum, &tot);
+    uint32_t off = nc + block_scan<C>(cnt, sm.wsum, &tot);
 #pragma unroll
-    for (int e = 0; e < kEPT; ++e) {
+    for (int e = 0; e < C::EPT; ++e) {
       if (j0 + e < n && keys[e] >= t0) {
-        if (off < (uint32_t)kCap) {
+        if (off < (uint32_t)C::CAP) {
           sm.ckey[off] = keys[e];
           sm.cidx[off] = j0 + e;
         }
         ++off;
       }
     }
-    C += tot;
-    if (C > (uint32_t)kCap) {
+    nc += tot;
+    if (nc > (uint32_t)C::CAP) {
       fits = false;
       break;
     }
   }
   __syncthreads();
-  if (fits && C >= kk)
-    select_candidates(C, kk, out, sm);
+  if (fits && nc >= kk)
+    select_candidates<C>(nc, kk, out, sm);
   else
-    select_whole_row(srow, n, vec, kk, out, sm);
+    select_whole_row<C>(srow, n, vec, kk, out, sm);
 }
 
-// Parallel filter, workgroup (row, part): the survivors (keys >= t0) of keys
-// [p * part_len, (p + 1) * part_len) of a row longer than kCap, in index
-// order, and their number (which may exceed kCap; then only kCap are kept).
-__global__ __launch_bounds__(kNT) void topk_part_kernel(TopkArgs a) {
-  __shared__ SampleSmem sm;
+// Parallel filter (BigCfg), workgroup (row, part): the survivors (keys >= t0)
+// of keys [p * part_len, (p + 1) * part_len) of a row longer than the
+// capacity, in index order, and their number (which may exceed the capacity;
+// then only CAP are kept).
+__global__ __launch_bounds__(BigCfg::NT) void topk_part_kernel(TopkArgs a) {
+  using C = BigCfg;
+  __shared__ SampleSmem<C> sm;
   const int64_t row = blockIdx.x / a.nparts;
   const int p = blockIdx.x - (int)(row * a.nparts);
   const int t = threadIdx.x;
   const int n = valid_len_of(a.vl, row);
   const uint32_t kk = (uint32_t)a.k;
-  if (n <= a.k || n <= kCap) return;  // the select kernel takes the row whole
+  if (n <= a.k || n <= C::CAP) return;  // the select kernel takes the row whole
   const float* srow = a.scores + row * a.row_stride;
   const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
   const int pend = min(n, (p + 1) * a.part_len);
-  // the part's first kPartLen keys are loaded before the threshold is formed,
+  // the part's first PART_LEN keys are loaded before the threshold is formed,
   // so their round trip overlaps the sample's
   const int jf = p * a.part_len + 4 * t;
   const bool first_vec = vec && jf + 4 <= pend;
   float4 first = make_float4(0.f, 0.f, 0.f, 0.f);
   if (first_vec) first = *reinterpret_cast<const float4*>(srow + jf);
-  const uint32_t t0 = sample_threshold(srow, n, kk, sm);
+  const uint32_t t0 = sample_threshold<C, C::NS>(srow, n, kk, sm);
   const int64_t slot = row * a.nparts + p;
-  uint32_t* okey = a.pkey + slot * kCap;
-  int32_t* oidx = a.pidx + slot * kCap;
-  uint32_t C = 0;
-  for (int j0 = p * a.part_len + 4 * t, jb = p * a.part_len; jb < pend; j0 += kPartLen, jb += kPartLen) {
+  uint32_t* okey = a.pkey + slot * C::CAP;
+  int32_t* oidx = a.pidx + slot * C::CAP;
+  uint32_t nc = 0;
+  for (int j0 = p * a.part_len + 4 * t, jb = p * a.part_len; jb < pend; j0 += C::PART_LEN, jb += C::PART_LEN) {
     uint32_t keys[4];
     if (vec && j0 + 4 <= pend) {
       const float4 x = j0 == jf ? first : *reinterpret_cast<const float4*>(srow + j0);
@@ -464,26 +524,27 @@ __global__ __launch_bounds__(kNT) void topk_part_kernel(TopkArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) cnt += (j0 + e < pend && keys[e] >= t0);
     uint32_t tot;
-    uint32_t off = C + block_scan(cnt, sm.wsum, &tot);
+    uint32_t off = nc + block_scan<C>(cnt, sm.wsum, &tot);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (j0 + e < pend && keys[e] >= t0) {
-        if (off < (uint32_t)kCap) {
+        if (off < (uint32_t)C::CAP) {
           okey[off] = keys[e];
           oidx[off] = j0 + e;
         }
         ++off;
       }
     }
-    C += tot;
-    if (C > (uint32_t)kCap) break;  // the row will fall back to the whole-row select
+    nc += tot;
+    if (nc > (uint32_t)C::CAP) break;  // the row will fall back to the whole-row select
   }
-  if (t == 0) a.pcnt[slot] = C;
+  if (t == 0) a.pcnt[slot] = nc;
 }
 
-// Select after the parallel filter: one workgroup per row.
-__global__ __launch_bounds__(kNT) void topk_select_kernel(TopkArgs a) {
-  __shared__ TopkSmem sm;
+// Select after the parallel filter (BigCfg): one workgroup per row.
+__global__ __launch_bounds__(BigCfg::NT) void topk_select_kernel(TopkArgs a) {
+  using C = BigCfg;
+  __shared__ RowSmem<C> sm;
   __shared__ uint32_t pstart[kMaxParts + 1];
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x;
@@ -491,40 +552,40 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkArgs a) {
   const uint32_t kk = (uint32_t)a.k;
   int32_t* out = a.idx + row * a.k;
   if (n <= a.k) {
-    for (int x = t; x < a.k; x += kNT) out[x] = x < n ? x : -1;
+    for (int x = t; x < a.k; x += C::NT) out[x] = x < n ? x : -1;
     return;
   }
   const float* srow = a.scores + row * a.row_stride;
   const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
-  if (n <= kCap) {  // the whole row is the candidate list
-    select_short_row(srow, n, kk, out, sm);
+  if (n <= C::CAP) {  // the whole row is the candidate list
+    select_short_row<C>(srow, n, kk, out, sm);
     return;
   }
   // part-major copy below: tpp threads per part; its first kU rounds of
   // survivor loads are issued before the counts are known (indices clamped
   // to the part's workspace slot), so both round trips overlap
-  const int tpp = kNT / a.nparts;
+  const int tpp = C::NT / a.nparts;
   const int pp = t / tpp, r = t - pp * tpp;
-  const int64_t base = (row * a.nparts + (pp < a.nparts ? pp : 0)) * kCap;
+  const int64_t base = (row * a.nparts + (pp < a.nparts ? pp : 0)) * C::CAP;
   constexpr int kU = 8;
   uint32_t kv[kU];
   int32_t iv[kU];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
-    const int i = min(r + u * tpp, kCap - 1);
+    const int i = min(r + u * tpp, C::CAP - 1);
     kv[u] = a.pkey[base + i];
     iv[u] = a.pidx[base + i];
   }
   if (t < 64) {  // one lane per part (nparts <= 64): counts, then an exclusive scan
     const uint32_t c = t < a.nparts ? a.pcnt[row * a.nparts + t] : 0u;
     const uint32_t x = wave_inclusive_scan(c);
-    const bool ok = __builtin_amdgcn_ballot_w64(c > (uint32_t)kCap) == 0;
+    const bool ok = __builtin_amdgcn_ballot_w64(c > (uint32_t)C::CAP) == 0;
     if (t < a.nparts) pstart[t] = x - c;
     if (t == 63) pstart[a.nparts] = ok ? x : 0xFFFFFFFFu;
   }
   __syncthreads();
-  const uint32_t C = pstart[a.nparts];
-  if (C <= (uint32_t)kCap && C >= kk) {
+  const uint32_t nc = pstart[a.nparts];
+  if (nc <= (uint32_t)C::CAP && nc >= kk) {
     // part-major copy: each part's survivors to their place in the
     // concatenated list (part order); a part with more survivors than the
     // first kU rounds finishes in a loop
@@ -544,16 +605,16 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkArgs a) {
       }
     }
     __syncthreads();
-    select_candidates(C, kk, out, sm);
+    select_candidates<C>(nc, kk, out, sm);
   } else {
-    select_whole_row(srow, n, vec, kk, out, sm);
+    select_whole_row<C>(srow, n, vec, kk, out, sm);
   }
 }
 
 int topk_parts(int64_t n_rows, int32_t row_len) {
-  if (n_rows <= 0 || n_rows >= kPartRows || row_len <= kCap) return 1;
+  if (n_rows <= 0 || n_rows >= kPartRows || row_len <= BigCfg::CAP) return 1;
   int np = (int)((kPartWGs + n_rows - 1) / n_rows);
-  const int by_len = (row_len + kPartLen - 1) / kPartLen;
+  const int by_len = (row_len + BigCfg::PART_LEN - 1) / BigCfg::PART_LEN;
   if (np > by_len) np = by_len;
   if (np > kMaxParts) np = kMaxParts;
   return np < 2 ? 1 : np;
@@ -561,8 +622,11 @@ int topk_parts(int64_t n_rows, int32_t row_len) {
 
 int topk_part_len(int32_t row_len, int np) {
   const int per = (row_len + np - 1) / np;
-  return (per + kPartLen - 1) / kPartLen * kPartLen;
+  return (per + BigCfg::PART_LEN - 1) / BigCfg::PART_LEN * BigCfg::PART_LEN;
 }
+
+// Many rows with K within half the small capacity: small workgroups.
+bool topk_small(int64_t n_rows, int32_t k) { return n_rows >= kSmallRows && 2 * k <= SmallCfg::CAP; }
 
 }  // namespace
 
@@ -570,7 +634,7 @@ size_t topk_ws_bytes(int64_t n_rows, int32_t row_len, int32_t /*k*/) {
   const int np = topk_parts(n_rows, row_len);
   if (np == 1) return 0;
   const size_t slots = (size_t)n_rows * np;
-  return align_up(slots * kCap * sizeof(uint32_t)) * 2 + align_up(slots * sizeof(uint32_t));
+  return align_up(slots * BigCfg::CAP * sizeof(uint32_t)) * 2 + align_up(slots * sizeof(uint32_t));
 }
 
 hipError_t launch_topk(const float* scores, int64_t n_rows, int32_t row_len, int64_t row_stride,
@@ -585,18 +649,22 @@ hipError_t launch_topk(const float* scores, int64_t n_rows, int32_t row_len, int
   a.k = k;
   a.idx = idx;
   a.nparts = topk_parts(n_rows, row_len);
-  if (a.nparts == 1) return launch("topk", topk_row_kernel, dim3((unsigned)n_rows), dim3(kNT), 0, st, a);
+  if (a.nparts == 1) {
+    if (topk_small(n_rows, k))
+      return launch("topk", topk_row_kernel<SmallCfg>, dim3((unsigned)n_rows), dim3(SmallCfg::NT), 0, st, a);
+    return launch("topk", topk_row_kernel<BigCfg>, dim3((unsigned)n_rows), dim3(BigCfg::NT), 0, st, a);
+  }
   const size_t slots = (size_t)n_rows * a.nparts;
   unsigned char* c = static_cast<unsigned char*>(ws);
   a.pkey = reinterpret_cast<uint32_t*>(c);
-  c += align_up(slots * kCap * sizeof(uint32_t));
+  c += align_up(slots * BigCfg::CAP * sizeof(uint32_t));
   a.pidx = reinterpret_cast<int32_t*>(c);
-  c += align_up(slots * kCap * sizeof(uint32_t));
+  c += align_up(slots * BigCfg::CAP * sizeof(uint32_t));
   a.pcnt = reinterpret_cast<uint32_t*>(c);
   a.part_len = topk_part_len(row_len, a.nparts);
-  hipError_t e = launch("topk_part", topk_part_kernel, dim3((unsigned)slots), dim3(kNT), 0, st, a);
+  hipError_t e = launch("topk_part", topk_part_kernel, dim3((unsigned)slots), dim3(BigCfg::NT), 0, st, a);
   if (e != hipSuccess) return e;
-  return launch("topk_select", topk_select_kernel, dim3((unsigned)n_rows), dim3(kNT), 0, st, a);
+  return launch("topk_select", topk_select_kernel, dim3((unsigned)n_rows), dim3(BigCfg::NT), 0, st, a);
 }
 
 }  // namespace hys

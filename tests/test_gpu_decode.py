@@ -120,6 +120,51 @@ def test_topk_parts_strided_rows_and_fallback():
     np.testing.assert_array_equal(got2, orc.topk_rows(S2, 131072, 5000))
 
 
+@pytest.mark.parametrize("kind", ["probs", "ties", "signed"])
+@pytest.mark.parametrize("k", [1, 100, 2048])
+def test_topk_many_rows_small_workgroups(kind, k):
+    """Many rows (the prefill shape: one row per KV group and 64-query block)
+    run in the small row workgroups: valid lengths across the short-row path
+    (<= 4096 candidates), the sampled filter and, for tied rows (more
+    survivors than the capacity), the whole-row fallback."""
+    say(f"topk many rows kind={kind} k={k}")
+    R, L = 512, 9000
+    S = gen.random_scores(61 + k, R, L, kind)
+    vl = np.random.default_rng(200 + k).integers(0, L + 1, size=R).astype(np.int32)
+    vl[:8] = [0, L, min(k, L), 4096, 4097, min(2 * k, L), 8191, 8192]
+    ref = orc.topk_rows(S, vl, k)
+    got = hy.hysparse_topk(torch.from_numpy(S).cuda(), k, valid_len=torch.from_numpy(vl).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(got), ref)
+
+
+def test_topk_many_long_rows_small_workgroups():
+    """400 rows of up to 131072 scores with K = 2048 (the 128K prefill's row
+    lengths) in the small row workgroups: the 8192-key sample keeps the
+    survivors between K and the 4096-entry capacity."""
+    say("topk 400 rows x 131072")
+    R, L = 400, 131072
+    S = gen.random_scores(71, R, L, "probs")
+    vl = np.linspace(4097, L, R).astype(np.int32)
+    ref = orc.topk_rows(S, vl, 2048)
+    got = hy.hysparse_topk(torch.from_numpy(S).cuda(), 2048, valid_len=torch.from_numpy(vl).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(got), ref)
+
+
+def test_topk_many_rows_k_above_small_capacity():
+    """Many rows with K above half the small workgroups' capacity run in the
+    large ones."""
+    say("topk many rows k=2500")
+    R, L = 400, 7000
+    S = gen.random_scores(81, R, L, "signed")
+    vl = np.random.default_rng(300).integers(0, L + 1, size=R).astype(np.int32)
+    ref = orc.topk_rows(S, vl, 2500)
+    got = hy.hysparse_topk(torch.from_numpy(S).cuda(), 2500, valid_len=torch.from_numpy(vl).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(got), ref)
+
+
 def test_topk_row_stride_and_all_equal():
     say("topk strided rows, all-equal rows")
     base = np.full((5, 4100), 0.5, np.float32)
