@@ -25,10 +25,12 @@ DECODE_CASES = {
     "g16_window300": W["decode128k"].replace(batch=1, kv_len=2000, k_top=300, window=300, n_sparse=1,
                                              n_planted=8),
     "short_ctx": W["decode8k"].replace(batch=1, kv_len=20, k_top=64, window=128, n_sparse=1),
+    # one key in the cache: every attention is over key 0 (O = v0, S = G)
+    "single_key": W["decode8k"].replace(batch=2, kv_len=1, k_top=16, window=8, n_sparse=1),
     # logits with std 8 (Q, K std 2.83, V std 1): base-2 logits spread over
-    # about +-45, so most per-head probabilities fall below 2^-29 of their
-    # step's maximum, the range where the fp16 scratch of the decode full
-    # layer leaves the normal numbers (their absolute error stays below 2^-40)
+    # about +-45, so most per-head probabilities fall far below their step's
+    # maximum; the decode full layer's three-byte probability scratch keeps
+    # fp32's exponent range, so they keep their 2^-16 relative precision
     "wide_logits": W["decode128k"].replace(batch=1, kv_len=5000, k_top=256, n_sparse=1, n_planted=8,
                                            std=float(np.sqrt(8.0)), v_std=1.0),
     # kv_len on and one past the 1024-key score chunks and 32-key steps of
