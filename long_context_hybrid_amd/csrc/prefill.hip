@@ -57,12 +57,31 @@ constexpr int kIdxCh = 2048;                // sparse layer: selected indices st
 #define HYS_SC_DMA 1
 #endif
 constexpr int kDmaStages = 3;
+#ifndef HYS_FWD_STAGES
+#define HYS_FWD_STAGES 3
+#endif
+constexpr int kFwdStages = HYS_FWD_STAGES;  // forward sweep's ring: tiles it + 1 .. it + kFwdStages - 1 in flight
+static_assert(kFwdStages >= 2 && kFwdStages <= 4, "forward ring stages");
 
 // wait until at most N of this wave's vector-memory operations are
 // outstanding (they complete in issue order) and its LDS reads are done
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
+
+// wait until the DMA of the ring's current tile has landed, while the PER
+// instructions of each of the next min(N, rem) tiles may stay outstanding
+template <int PER, int N>
+__device__ __forceinline__ void wait_ring(int rem) {
+  if constexpr (N == 0) {
+    wait_vm_lgkm<0>();
+  } else {
+    if (rem >= N)
+      wait_vm_lgkm<N * PER>();
+    else
+      wait_ring<PER, N - 1>(rem);
+  }
 }
 
 struct PrefillArgs {
@@ -112,7 +131,7 @@ __global__ __launch_bounds__(kNW * 64, kWPE) void prefill_fwd_kernel(PrefillArgs
   using L = TileLayout<TR, D>;
   constexpr int KC = D / 32, DT = D / 16;
   static_assert(!DMA || (TR::kBytes == 2 && D == 128), "DMA staging is for bf16, head_dim 128");
-  __shared__ __align__(16) unsigned char sm[DMA ? kDmaStages * DmaTile::kBytes : L::kBytes];
+  __shared__ __align__(16) unsigned char sm[DMA ? kFwdStages * DmaTile::kBytes : L::kBytes];
   __shared__ int kj[DMA ? 1 : kTK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, quad = lane >> 4;
   const int per_qt = a.B * a.Hkv * a.NHC;
@@ -148,18 +167,21 @@ __global__ __launch_bounds__(kNW * 64, kWPE) void prefill_fwd_kernel(PrefillArgs
   RowState<kRTW, D> st;
   st.reset();
   if constexpr (DMA) {
-    // Ring of kDmaStages stages: at step it, tile it is used while tiles
-    // it + 1 and it + 2 are in flight.  Each wave waits for its own DMA of
-    // tile it (at most the 2 * 16 / kNW instructions of tile it + 1 may remain
-    // outstanding); the barrier then makes every wave's part visible and
-    // frees the stage of tile it - 1 for tile it + 2.  Keys past kv_len are
-    // loaded from row kv_len - 1 and masked (they lie after every position).
+    // Ring of S = kFwdStages stages: at step it, tile it is used while
+    // tiles it + 1 .. it + S - 1 are in flight.  Each wave waits for its own
+    // DMA of tile it (the 2 * 16 / kNW instructions of each later tile may
+    // remain outstanding); the barrier then makes every wave's part visible
+    // and frees the stage of tile it - 1 for tile it + S - 1.  Keys past
+    // kv_len are loaded from row kv_len - 1 and masked (they lie after every
+    // position).
+    constexpr int S = kFwdStages, P = S - 1;
     constexpr int kDmaPerTile = 2 * 16 / kNW;
     const uint16_t* kb = reinterpret_cast<const uint16_t*>(kbase);
     const uint16_t* vb = reinterpret_cast<const uint16_t*>(vbase);
     const int last = Tkv - 1;
-    dma_tile<kNW>(sm, kb, vb, a.ks_t, 0, last);
-    if (nkt > 1) dma_tile<kNW>(sm + DmaTile::kBytes, kb, vb, a.ks_t, kTK, last);
+#pragma unroll
+    for (int t = 0; t < P; ++t)
+      if (t < nkt) dma_tile<kNW>(sm + t * DmaTile::kBytes, kb, vb, a.ks_t, t * kTK, last);
     // The Q fragments must be resident before the loop: the compiler cannot
     // count the ring's loads across steps and would otherwise wait for all
     // of them (vmcnt 0) at the first MFMA of every step.
@@ -167,20 +189,17 @@ __global__ __launch_bounds__(kNW * 64, kWPE) void prefill_fwd_kernel(PrefillArgs
     for (int rt = 0; rt < kRTW; ++rt)
 #pragma unroll
       for (int c = 0; c < KC; ++c) asm volatile("" ::"v"(qf[rt][c]));
-    int cur = 0;  // stage of tile it; tile it + 2 goes to the stage of tile it - 1
+    int cur = 0;  // stage of tile it; tile it + P goes to the stage of tile it - 1
     for (int it = 0; it < nkt; ++it) {
-      if (it + 1 < nkt)
-        wait_vm_lgkm<kDmaPerTile>();
-      else
-        wait_vm_lgkm<0>();
+      wait_ring<kDmaPerTile, P - 1>(nkt - 1 - it);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      const int nxt = cur == 0 ? kDmaStages - 1 : cur - 1;
-      if (it + 2 < nkt) dma_tile<kNW>(sm + nxt * DmaTile::kBytes, kb, vb, a.ks_t, (it + 2) * kTK, last);
+      const int nxt = cur == 0 ? S - 1 : cur - 1;
+      if (it + P < nkt) dma_tile<kNW>(sm + nxt * DmaTile::kBytes, kb, vb, a.ks_t, (it + P) * kTK, last);
       const int j0 = it * kTK;
       attend_tile_dma<kRTW>(st, qf, sm + cur * DmaTile::kBytes, [j0](int e) { return j0 + e; }, a.sl2,
                             (it + 1) * kTK - 1 > pmin, [&](int rt, int j) { return j <= rpos[rt]; });
-      cur = cur == kDmaStages - 1 ? 0 : cur + 1;
+      cur = cur == S - 1 ? 0 : cur + 1;
     }
   } else {
     TileStage<TR, D, kNT, true> stg;
