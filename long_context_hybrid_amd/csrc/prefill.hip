@@ -48,20 +48,27 @@ constexpr int kFwdNW = kFwdShape[0], kFwdRTW = kFwdShape[1], kFwdWPE = kFwdShape
 constexpr int kScNW = kScShape[0], kScRTW = kScShape[1];
 constexpr int kSpNW = kSpShape[0], kSpRTW = kSpShape[1];
 constexpr int kIdxCh = 2048;                // sparse layer: selected indices staged in LDS per refill
-// Forward sweep, bf16 with head_dim 128: tiles staged by LDS DMA into a ring
-// of kDmaStages stages (the next two tiles in flight while one is used).
+// Both sweeps, bf16 with head_dim 128: tiles staged by LDS DMA into a ring
+// of stages (the next tiles in flight while one is used).
 #ifndef HYS_FWD_DMA
 #define HYS_FWD_DMA 1
 #endif
 #ifndef HYS_SC_DMA
 #define HYS_SC_DMA 1
 #endif
-constexpr int kDmaStages = 3;
+// Ring stages: at step it, tiles it + 1 .. it + stages - 1 are in flight.
+// Measured at 32K and 128K, two stages (one tile in flight, the DMA issued
+// a whole tile step ahead) beat three by 1-1.5% in both sweeps; four were
+// slower still.
 #ifndef HYS_FWD_STAGES
-#define HYS_FWD_STAGES 3
+#define HYS_FWD_STAGES 2
 #endif
-constexpr int kFwdStages = HYS_FWD_STAGES;  // forward sweep's ring: tiles it + 1 .. it + kFwdStages - 1 in flight
-static_assert(kFwdStages >= 2 && kFwdStages <= 4, "forward ring stages");
+#ifndef HYS_SC_STAGES
+#define HYS_SC_STAGES 2
+#endif
+constexpr int kFwdStages = HYS_FWD_STAGES;
+constexpr int kScStages = HYS_SC_STAGES;
+static_assert(kFwdStages >= 2 && kFwdStages <= 4 && kScStages >= 2 && kScStages <= 4, "ring stages");
 
 // wait until at most N of this wave's vector-memory operations are
 // outstanding (they complete in issue order) and its LDS reads are done
@@ -348,7 +355,7 @@ __device__ __forceinline__ void score_tile(const typename TR::frag (&qf)[RTW][D 
 // workgroup adds the wave sums in a fixed order and writes S (first pass) or
 // adds to it (later passes; the same thread owns the same key in every pass,
 // so the order of the additions is fixed).
-// DMA (bf16, head_dim 128): K tiles come into a ring of three LDS stages by
+// DMA (bf16, head_dim 128): K tiles come into a ring of LDS stages by
 // global_load_lds, one barrier per tile, the wave sums double-buffered; the
 // later passes add with a no-return atomic so that no load waits inside the
 // ring.  Otherwise: global -> registers -> one LDS tile.
@@ -360,7 +367,7 @@ __global__ __launch_bounds__(kNW * 64, DMA ? 2 : 1) void prefill_block_scores_ke
   constexpr int KC = D / 32;
   static_assert(!DMA || (TR::kBytes == 2 && D == 128), "DMA staging is for bf16, head_dim 128");
   static_assert(kRTW % 4 == 0, "a wave's row tiles cover whole groups of the block's 64 queries");
-  __shared__ __align__(16) unsigned char sm[DMA ? kDmaStages * DmaTile::kHalf : L::kKBytes];
+  __shared__ __align__(16) unsigned char sm[DMA ? kScStages * DmaTile::kHalf : L::kKBytes];
   __shared__ int kj[DMA ? 1 : kTK];
   __shared__ float red[DMA ? 2 : 1][kNW * kTK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, quad = lane >> 4;
@@ -422,13 +429,15 @@ __global__ __launch_bounds__(kNW * 64, DMA ? 2 : 1) void prefill_block_scores_ke
       }
     };
     if constexpr (DMA) {
+      constexpr int S = kScStages, P = S - 1;
       constexpr int kDmaPerTile = 16 / kNW;
       const uint16_t* kb = reinterpret_cast<const uint16_t*>(kbase);
       const int last = Tkv - 1;
       // every wave is done with the previous pass's stages and sums
       __syncthreads();
-      dma_tile_k<kNW>(sm, kb, a.ks_t, 0, last);
-      if (nkt > 1) dma_tile_k<kNW>(sm + DmaTile::kHalf, kb, a.ks_t, kTK, last);
+#pragma unroll
+      for (int t = 0; t < P; ++t)
+        if (t < nkt) dma_tile_k<kNW>(sm + t * DmaTile::kHalf, kb, a.ks_t, t * kTK, last);
       // resident Q / LSE before the ring (see the forward sweep)
 #pragma unroll
       for (int x = 0; x < kRTW; ++x) {
@@ -439,15 +448,12 @@ __global__ __launch_bounds__(kNW * 64, DMA ? 2 : 1) void prefill_block_scores_ke
       }
       int cur = 0;
       for (int it = 0; it < nkt; ++it) {
-        if (it + 1 < nkt)
-          wait_vm_lgkm<kDmaPerTile>();
-        else
-          wait_vm_lgkm<0>();
+        wait_ring<kDmaPerTile, P - 1>(nkt - 1 - it);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (it > 0 && tid < kTK) flush(it - 1, (it - 1) & 1);
-        const int nxt = cur == 0 ? kDmaStages - 1 : cur - 1;
-        if (it + 2 < nkt) dma_tile_k<kNW>(sm + nxt * DmaTile::kHalf, kb, a.ks_t, (it + 2) * kTK, last);
+        const int nxt = cur == 0 ? S - 1 : cur - 1;
+        if (it + P < nkt) dma_tile_k<kNW>(sm + nxt * DmaTile::kHalf, kb, a.ks_t, (it + P) * kTK, last);
         const unsigned char* stage = sm + cur * DmaTile::kHalf;
         const int j0 = it * kTK;
         auto kfrag = [&](int ct, int c) { return dma_k_frag(stage, ct, c, col, quad); };
@@ -457,7 +463,7 @@ __global__ __launch_bounds__(kNW * 64, DMA ? 2 : 1) void prefill_block_scores_ke
           block_score_tile<TR, D, kRTW, true>(qf, nl, pos0, kfrag, keys, a.sl2, wred);
         else
           block_score_tile<TR, D, kRTW, false>(qf, nl, pos0, kfrag, keys, a.sl2, wred);
-        cur = cur == kDmaStages - 1 ? 0 : cur + 1;
+        cur = cur == S - 1 ? 0 : cur + 1;
       }
       __syncthreads();
       if (tid < kTK) flush(nkt - 1, (nkt - 1) & 1);
