@@ -98,7 +98,6 @@ def check_hybrid(wl, inp, res, n_check_layers=None, blocks=None):
     say(f"  index rows differing from the oracle's own selection: {agree['rows_differing']}/{agree['rows']}, "
         f"mean IoU {agree['mean_iou']:.6f}")
     layers = range(len(inp.q_sparse)) if n_check_layers is None else range(n_check_layers)
-    layers = range(len(inp.q_sparse)) if n_check_layers is None else range(n_check_layers)
     for l in layers:
         ref = orc.sparse_layer(inp.q_sparse[l], inp.k, inp.v, idx_gpu, Sb, wl.window, inp.gate_logits[l],
                                blocks=blocks)

@@ -1,0 +1,68 @@
+"""GPU parity of the whole hybrid block on seeded random shapes.
+
+Each case draws its own combination of dtype, head_dim, KV heads, group size,
+batch, decode or (chunked) prefill, score block, K, window, layer count and
+gates (with an occasional +-inf gate logit, which selects one branch), then
+runs the block through the C ABI and checks it against the CPU oracle with
+the same criteria as the hand-picked cases: full-layer output and scores
+within tolerance, the index rows equal to the oracle's top-K of the GPU's
+scores and eps-valid against the oracle's, and every sparse layer's output
+equal to the oracle's on those indices.  Sizes keep the fp64 oracle to a few
+seconds per case.
+"""
+import numpy as np
+import pytest
+import torch
+
+from long_context_hybrid_amd import hysparse as hy
+from long_context_hybrid_amd import inputs as gen
+from tests.gpu_util import check_hybrid, dev_tensor, say
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 48
+
+
+def random_workload(seed: int):
+    r = np.random.default_rng(5000 + seed)
+    dtype = str(r.choice(["bf16", "f32"]))
+    D = int(r.choice([64, 128]))
+    Hkv = int(r.choice([1, 2, 4]))
+    G = int(r.choice([1, 2, 4, 8, 16]))
+    B = int(r.integers(1, 4))
+    if r.random() < 0.5:  # decode
+        Tq, Tkv, Sb = 1, int(r.integers(1, 2500)), 1
+    else:  # prefill, whole or chunked (queries at the end of a longer context)
+        Tkv = int(r.integers(2, 520))
+        Tq = Tkv if r.random() < 0.5 else int(r.integers(2, Tkv + 1))
+        Sb = int(r.choice([1, 64]))
+    K = int(r.integers(1, 400))
+    W = int(r.integers(1, 200))
+    N = int(r.integers(1, 3))
+    std = float(r.choice([1.0 / np.sqrt(D), 1.0]))
+    wl = gen.WORKLOADS["decode8k"].replace(
+        name=f"random{seed}", config_id=100 + seed, batch=B, q_len=Tq, kv_len=Tkv, n_q_heads=G * Hkv,
+        n_kv_heads=Hkv, head_dim=D, dtype=dtype, std=std, score_block=Sb, k_top=K, window=W, n_sparse=N,
+        n_planted=0)
+    # a few gate logits at +-inf (global branch only / window branch only)
+    inf_heads = [(int(r.integers(0, N)), int(r.integers(0, G * Hkv)), float(r.choice([np.inf, -np.inf])))
+                 for _ in range(int(r.integers(0, 3)))]
+    return wl, inf_heads
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_shape_hybrid_block(seed):
+    wl, inf_heads = random_workload(seed)
+    say(f"random case {seed}: {wl.dtype} D{wl.head_dim} B{wl.batch} Tq{wl.q_len} Tkv{wl.kv_len} "
+        f"Hq{wl.n_q_heads}/Hkv{wl.n_kv_heads} Sb{wl.score_block} K{wl.k_top} W{wl.window} N{wl.n_sparse} "
+        f"inf gates {inf_heads}")
+    inp = gen.make_inputs(wl)
+    for (layer, head, val) in inf_heads:
+        inp.gate_logits[layer, head] = val
+    dt = wl.dtype
+    qf, k, v = dev_tensor(inp.q_full, dt), dev_tensor(inp.k, dt), dev_tensor(inp.v, dt)
+    qs = [dev_tensor(q, dt) for q in inp.q_sparse]
+    gates = torch.from_numpy(inp.gate_logits).cuda()
+    res = hy.hysparse_hybrid_block(qf, k, v, qs, gates, wl.k_top, wl.score_block, wl.window)
+    torch.cuda.synchronize()
+    check_hybrid(wl, inp, res)
