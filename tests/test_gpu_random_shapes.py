@@ -16,7 +16,8 @@ import torch
 
 from long_context_hybrid_amd import hysparse as hy
 from long_context_hybrid_amd import inputs as gen
-from tests.gpu_util import check_hybrid, dev_tensor, say
+from oracle import hysparse_oracle as orc
+from tests.gpu_util import assert_attn_close, check_hybrid, dev_tensor, say
 
 pytestmark = pytest.mark.gpu
 
@@ -66,3 +67,52 @@ def test_random_shape_hybrid_block(seed):
     res = hy.hysparse_hybrid_block(qf, k, v, qs, gates, wl.k_top, wl.score_block, wl.window)
     torch.cuda.synchronize()
     check_hybrid(wl, inp, res)
+
+
+def _ring(x: np.ndarray, ring: int, dt: str) -> torch.Tensor:
+    """The last `ring` positions of a [B, T, H, D] array in a ring: row p % ring."""
+    B, T, H, D = x.shape
+    r = np.zeros((B, ring, H, D), np.float32)
+    for p in range(max(0, T - ring), T):
+        r[:, p % ring] = x[:, p]
+    return dev_tensor(r, dt)
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_shape_sparse_layer_general(seed):
+    """The general sparse layer on the oracle's own indices: the window branch
+    on the shared cache or on the layer's own window keys/values (a
+    position-indexed buffer or a ring of the shortest allowed length or
+    longer), gates per head or per (token, head), some at +-inf."""
+    wl, _ = random_workload(1000 + seed)
+    wl = wl.replace(n_sparse=1)
+    r = np.random.default_rng(9000 + seed)
+    own = r.random() < 0.7
+    ring = 0
+    if own and r.random() < 0.6:
+        ring = (wl.window if wl.q_len == 1 else wl.window + wl.q_len - 1) + int(r.integers(0, 64))
+    token_gate = r.random() < 0.5
+    say(f"general sparse layer {seed}: {wl.dtype} D{wl.head_dim} B{wl.batch} Tq{wl.q_len} Tkv{wl.kv_len} "
+        f"Hq{wl.n_q_heads}/Hkv{wl.n_kv_heads} Sb{wl.score_block} K{wl.k_top} W{wl.window} own={own} ring={ring} "
+        f"token_gate={token_gate}")
+    inp = gen.make_inputs(wl)
+    _, _, S = orc.full_layer(inp.q_full, inp.k, inp.v, wl.score_block)
+    idx = orc.select_indices(S, wl.q_len, wl.kv_len, wl.score_block, wl.k_top)
+    if token_gate:
+        gl = r.standard_normal((wl.batch, wl.q_len, wl.n_q_heads)).astype(np.float32)
+        gl[r.random(gl.shape) < 0.05] = np.inf
+        gl[r.random(gl.shape) < 0.05] = -np.inf
+    else:
+        gl = inp.gate_logits[0].copy()
+    dt = wl.dtype
+    k, v, qs = dev_tensor(inp.k, dt), dev_tensor(inp.v, dt), dev_tensor(inp.q_sparse[0], dt)
+    kw = vw = own_k = own_v = None
+    if own:
+        kw, vw = gen.own_window_kv(wl)
+        own_k = _ring(kw, ring, dt) if ring else dev_tensor(kw, dt)
+        own_v = _ring(vw, ring, dt) if ring else dev_tensor(vw, dt)
+    out = hy.hysparse_sparse_attn_ex(qs, k, v, torch.from_numpy(idx).cuda(), wl.k_top, wl.score_block, wl.window,
+                                     torch.from_numpy(gl).cuda(), own_k=own_k, own_v=own_v, ring=ring)
+    torch.cuda.synchronize()
+    ref = orc.sparse_layer(inp.q_sparse[0], inp.k, inp.v, idx, wl.score_block, wl.window, gl, k_win=kw, v_win=vw)
+    assert_attn_close(out, ref, dt, f"general sparse layer {seed}")
