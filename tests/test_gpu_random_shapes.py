@@ -116,3 +116,26 @@ def test_random_shape_sparse_layer_general(seed):
     torch.cuda.synchronize()
     ref = orc.sparse_layer(inp.q_sparse[0], inp.k, inp.v, idx, wl.score_block, wl.window, gl, k_win=kw, v_win=vw)
     assert_attn_close(out, ref, dt, f"general sparse layer {seed}")
+
+
+@pytest.mark.parametrize("seed", range(N_CASES // 2))
+def test_random_shape_hier_select(seed):
+    """Hierarchical selection (decode) on random shapes: block sizes that do
+    and do not divide the context, more blocks kept than exist, K above the
+    kept blocks' token count."""
+    from tests.test_gpu_hier import _check, _run
+    r = np.random.default_rng(7000 + seed)
+    Tkv = int(r.integers(1, 3000))
+    block = int(r.choice([16, 32, 64, 100, 128, 256]))
+    nb = -(-Tkv // block)
+    n_keep = int(r.integers(1, nb + 4))
+    D = int(r.choice([64, 128]))
+    Hkv, G = int(r.choice([1, 2, 4])), int(r.choice([1, 2, 4, 8, 16]))
+    wl = gen.WORKLOADS["hier128k"].replace(
+        name=f"hier_random{seed}", config_id=200 + seed, batch=int(r.integers(1, 4)), kv_len=Tkv,
+        n_q_heads=G * Hkv, n_kv_heads=Hkv, head_dim=D, dtype=str(r.choice(["bf16", "f32"])),
+        std=float(r.choice([1.0 / np.sqrt(D), 1.0])), k_top=int(r.integers(1, 600)), n_sparse=1, n_planted=0)
+    say(f"hier random {seed}: {wl.dtype} D{D} B{wl.batch} Tkv{Tkv} Hq{wl.n_q_heads}/Hkv{Hkv} block{block} "
+        f"keep{n_keep} K{wl.k_top}")
+    inp, _, S, idx, bs, blk = _run(wl, block, n_keep)
+    _check(wl, inp, S, idx, bs, blk, block, n_keep)
