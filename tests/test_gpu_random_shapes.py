@@ -139,3 +139,27 @@ def test_random_shape_hier_select(seed):
         f"keep{n_keep} K{wl.k_top}")
     inp, _, S, idx, bs, blk = _run(wl, block, n_keep)
     _check(wl, inp, S, idx, bs, blk, block, n_keep)
+
+
+@pytest.mark.parametrize("seed", range(N_CASES // 2))
+def test_random_shape_topk(seed):
+    """Top-K alone on random row counts (either side of the thresholds that
+    pick the many-row workgroups and the split filter), lengths, K, score
+    kinds, valid lengths and row strides (the row length rounded up to a
+    multiple of 4, plus 0, 4 or 8): bit-exact against the oracle."""
+    r = np.random.default_rng(8000 + seed)
+    R = int(r.choice([int(r.integers(1, 40)), int(r.integers(200, 300)), int(r.integers(380, 900))]))
+    L = int(r.integers(1, max(2, min(140000, 20_000_000 // R))))
+    K = int(r.integers(1, 3000))
+    kind = str(r.choice(["probs", "ties", "signed"]))
+    pad = int(r.choice([0, 4, 8]))
+    vl = r.integers(0, L + 1, size=R).astype(np.int32)
+    if r.random() < 0.5:
+        vl[:] = L
+    stride = -(-L // 4) * 4 + pad  # the row stride must be a multiple of 4 elements
+    say(f"topk random {seed}: R{R} L{L} K{K} {kind} stride{stride}")
+    S = gen.random_scores(900 + seed, R, stride, kind)
+    ref = orc.topk_rows(S[:, :L], vl, K)
+    got = hy.hysparse_topk(torch.from_numpy(S).cuda()[:, :L], K, valid_len=torch.from_numpy(vl).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), ref)
