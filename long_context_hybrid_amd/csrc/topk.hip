@@ -174,25 +174,43 @@ __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SM& sm, u
   *mx_out = b;
 }
 
+// The bounds of a key set held in registers while the keys are being stored
+// to LDS: each wave's minimum and maximum go to LDS with the keys, so the
+// barrier that publishes the keys publishes the bounds too (range_read after
+// it), instead of a separate min/max pass with two barriers of its own.
+template <class SM>
+__device__ __forceinline__ void range_publish(uint32_t mn, uint32_t mx, SM& sm) {
+  wave_min_max(mn, mx);
+  if ((threadIdx.x & 63) == 0) {
+    sm.wmin[threadIdx.x >> 6] = mn;
+    sm.wmax[threadIdx.x >> 6] = mx;
+  }
+}
+template <class C, class SM>
+__device__ __forceinline__ void range_read(SM& sm, uint32_t* base, uint32_t* top) {
+  uint32_t a = 0xFFFFFFFFu, b = 0u;
+#pragma unroll
+  for (int w = 0; w < C::NT / 64; ++w) {
+    a = min(a, sm.wmin[w]);
+    b = max(b, sm.wmax[w]);
+  }
+  *base = a;
+  *top = b;
+}
+
 // Radix select: the k-th largest key T over the keys the visitor hands to its
 // callback (this thread's keys), and the number k_rem of keys equal to T that
-// belong to the top k.  Requires 1 <= k <= number of keys.  The digits are
-// taken from r = key - min over the keys' own range (C::DIGIT bits at a time
-// from the top of max - min), so the histogram bins are spread over the
-// values actually present.  After the first digit the keys of the selected
-// bin are usually few: up to C::RANKLIST of them are ranked directly in LDS
-// instead of running the remaining digit passes.
+// belong to the top k.  Requires 1 <= k <= number of keys and base <= every
+// key <= top.  The digits are taken from r = key - base over the keys' own
+// range (C::DIGIT bits at a time from the top of top - base), so the
+// histogram bins are spread over the values actually present.  After the
+// first digit the keys of the selected bin are usually few: up to
+// C::RANKLIST of them are ranked directly in LDS instead of running the
+// remaining digit passes.
 template <class C, class Visit, class SM>
-__device__ __forceinline__ void radix_select(uint32_t k, Visit visit, SM& sm, uint32_t* T_out,
-                                             uint32_t* krem_out) {
+__device__ __forceinline__ void radix_select_in(uint32_t k, uint32_t base, uint32_t top, Visit visit, SM& sm,
+                                                uint32_t* T_out, uint32_t* krem_out) {
   const int t = threadIdx.x;
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  visit([&](uint32_t u) {
-    lo = min(lo, u);
-    hi = max(hi, u);
-  });
-  uint32_t base, top;
-  block_minmax<C>(lo, hi, sm, &base, &top);
   const uint32_t range = top - base;
   int s_hi = range == 0u ? 0 : 32 - __clz(range);  // every r = key - base is < 2^s_hi
   uint32_t P = 0, krem = k;                         // selected value of r >> s_hi
@@ -271,6 +289,20 @@ __device__ __forceinline__ void radix_select(uint32_t k, Visit visit, SM& sm, ui
   *krem_out = krem;
 }
 
+// Radix select over keys whose bounds are not known yet: a min/max pass first.
+template <class C, class Visit, class SM>
+__device__ __forceinline__ void radix_select(uint32_t k, Visit visit, SM& sm, uint32_t* T_out,
+                                             uint32_t* krem_out) {
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  visit([&](uint32_t u) {
+    lo = min(lo, u);
+    hi = max(hi, u);
+  });
+  uint32_t base, top;
+  block_minmax<C>(lo, hi, sm, &base, &top);
+  radix_select_in<C>(k, base, top, visit, sm, T_out, krem_out);
+}
+
 // Threshold t0 from an NS-key sample of the row (n > C::CAP): keys >= t0
 // include, in expectation, C::QF4 / 4 times the top K (plus the slack C::QA).
 // Every workgroup of a row computes the same value (same sample, same
@@ -289,30 +321,41 @@ __device__ __forceinline__ uint32_t sample_threshold(const float* srow, int n, u
     const int base = (int)((int64_t)r * (n - kRunLen) / (RUNS - 1));
     v[e] = srow[base + o];
   }
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
-  for (int e = 0; e < SPT; ++e) sm.samp[t + e * C::NT] = order_key(v[e]);
+  for (int e = 0; e < SPT; ++e) {
+    const uint32_t u = order_key(v[e]);
+    sm.samp[t + e * C::NT] = u;
+    mn = min(mn, u);
+    mx = max(mx, u);
+  }
+  range_publish(mn, mx, sm);
   __syncthreads();
+  uint32_t base, top;
+  range_read<C>(sm, &base, &top);
   // rank in the sample: a multiple of the expected count of top-K keys, plus slack
   int64_t q = ((int64_t)kk * NS + n - 1) / n * C::QF4 / 4 + C::QA;
   if (q > NS) q = NS;
   uint32_t T0, r0;
-  radix_select<C>((uint32_t)q, [&](auto f) {
+  radix_select_in<C>((uint32_t)q, base, top, [&](auto f) {
 #pragma unroll
     for (int e = 0; e < SPT; ++e) f(sm.samp[t + e * C::NT]);
   }, sm, &T0, &r0);
   return T0;  // the q-th largest sample key: keys >= t0 include the top q of the sample
 }
 
-// Steps 2 and 3 over the C candidates in sm.ckey / sm.cidx (index order).
+// Steps 2 and 3 over the nc candidates in sm.ckey / sm.cidx (index order),
+// whose keys lie in [base, top].
 template <class C>
-__device__ __forceinline__ void select_candidates(uint32_t nc, uint32_t kk, int32_t* out, RowSmem<C>& sm) {
+__device__ __forceinline__ void select_candidates(uint32_t nc, uint32_t kk, uint32_t base, uint32_t top, int32_t* out,
+                                                  RowSmem<C>& sm) {
   const int t = threadIdx.x;
   // thread t owns a contiguous run of candidates; an odd run length keeps the
   // lanes' strided LDS reads on distinct banks
   const uint32_t per = ((nc + C::NT - 1) / C::NT) | 1u;
   const uint32_t c0 = min(nc, t * per), c1 = min(nc, c0 + per);
   uint32_t T, krem;
-  radix_select<C>(kk, [&](auto f) {
+  radix_select_in<C>(kk, base, top, [&](auto f) {
     for (uint32_t c = c0; c < c1; ++c) f(sm.ckey[c]);
   }, sm, &T, &krem);
   uint32_t gt = 0, eq = 0;
@@ -320,9 +363,10 @@ __device__ __forceinline__ void select_candidates(uint32_t nc, uint32_t kk, int3
     gt += sm.ckey[c] > T;
     eq += sm.ckey[c] == T;
   }
-  uint32_t tg, te;
-  uint32_t gb = block_scan<C>(gt, sm.wsum, &tg);
-  uint32_t eb = block_scan<C>(eq, sm.wsum, &te);
+  // both counts in one scan: (greater << 16) | equal (at most C::CAP < 2^16 each)
+  uint32_t tot;
+  const uint32_t pre = block_scan<C>((gt << 16) | eq, sm.wsum, &tot);
+  uint32_t gb = pre >> 16, eb = pre & 0xFFFFu;
   for (uint32_t c = c0; c < c1; ++c) {
     const uint32_t u = sm.ckey[c];
     const bool is_gt = u > T, is_eq = u == T;
@@ -345,14 +389,21 @@ __device__ __forceinline__ void select_short_row(const float* srow, int n, uint3
   float v[kB];
 #pragma unroll
   for (int e = 0; e < kB; ++e) v[e] = srow[min(t + e * C::NT, n - 1)];
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
   for (int e = 0; e < kB; ++e)
     if (t + e * C::NT < n) {
-      sm.ckey[t + e * C::NT] = order_key(v[e]);
+      const uint32_t u = order_key(v[e]);
+      sm.ckey[t + e * C::NT] = u;
       sm.cidx[t + e * C::NT] = t + e * C::NT;
+      mn = min(mn, u);
+      mx = max(mx, u);
     }
+  range_publish(mn, mx, sm);
   __syncthreads();
-  select_candidates<C>((uint32_t)n, kk, out, sm);
+  uint32_t base, top;
+  range_read<C>(sm, &base, &top);
+  select_candidates<C>((uint32_t)n, kk, base, top, out, sm);
 }
 
 // this thread's C::EPT consecutive keys of segment sg (0 past the row end)
@@ -403,9 +454,10 @@ __device__ __forceinline__ void select_whole_row(const float* srow, int n, bool 
       gt += (in && keys[e] > T);
       eq += (in && keys[e] == T);
     }
-    uint32_t tg, te;
-    uint32_t gb = g_base + block_scan<C>(gt, sm.wsum, &tg);
-    uint32_t eb = e_base + block_scan<C>(eq, sm.wsum, &te);
+    // both counts in one scan (at most C::SEG < 2^16 each per segment)
+    uint32_t tot;
+    const uint32_t pre = block_scan<C>((gt << 16) | eq, sm.wsum, &tot);
+    uint32_t gb = g_base + (pre >> 16), eb = e_base + (pre & 0xFFFFu);
 #pragma unroll
     for (int e = 0; e < C::EPT; ++e) {
       const bool in = j0 + e < n;
@@ -416,8 +468,8 @@ __device__ __forceinline__ void select_whole_row(const float* srow, int n, bool 
       gb += is_gt;
       eb += is_eq;
     }
-    g_base += tg;
-    e_base += te;
+    g_base += tot >> 16;
+    e_base += tot & 0xFFFFu;
   }
 }
 
@@ -449,6 +501,7 @@ __global__ __launch_bounds__(C::NT) void topk_row_kernel(TopkArgs a) {
   // ---- filter: keys >= t0 into LDS, index order
   uint32_t nc = 0;  // candidates kept (block-uniform)
   bool fits = true;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;  // bounds of this thread's kept keys
   for (int sg = 0; sg < nseg; ++sg) {
     uint32_t keys[C::EPT];
     load_seg<C>(srow, n, vec, sg, keys);
@@ -466,6 +519,8 @@ __global__ __launch_bounds__(C::NT) void topk_row_kernel(TopkArgs a) {
           sm.cidx[off] = j0 + e;
         }
         ++off;
+        mn = min(mn, keys[e]);
+        mx = max(mx, keys[e]);
       }
     }
     nc += tot;
@@ -474,10 +529,13 @@ __global__ __launch_bounds__(C::NT) void topk_row_kernel(TopkArgs a) {
       break;
     }
   }
+  range_publish(mn, mx, sm);
   __syncthreads();
-  if (fits && nc >= kk)
-    select_candidates<C>(nc, kk, out, sm);
-  else
+  if (fits && nc >= kk) {
+    uint32_t base, top;
+    range_read<C>(sm, &base, &top);
+    select_candidates<C>(nc, kk, base, top, out, sm);
+  } else
     select_whole_row<C>(srow, n, vec, kk, out, sm);
 }
 
@@ -589,6 +647,7 @@ __global__ __launch_bounds__(BigCfg::NT) void topk_select_kernel(TopkArgs a) {
     // part-major copy: each part's survivors to their place in the
     // concatenated list (part order); a part with more survivors than the
     // first kU rounds finishes in a loop
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
     if (pp < a.nparts) {
       const uint32_t c0 = pstart[pp], cnt = pstart[pp + 1] - c0;
 #pragma unroll
@@ -597,15 +656,23 @@ __global__ __launch_bounds__(BigCfg::NT) void topk_select_kernel(TopkArgs a) {
         if (i < cnt) {
           sm.ckey[c0 + i] = kv[u];
           sm.cidx[c0 + i] = iv[u];
+          mn = min(mn, kv[u]);
+          mx = max(mx, kv[u]);
         }
       }
       for (uint32_t i = r + kU * tpp; i < cnt; i += tpp) {
-        sm.ckey[c0 + i] = a.pkey[base + i];
+        const uint32_t u = a.pkey[base + i];
+        sm.ckey[c0 + i] = u;
         sm.cidx[c0 + i] = a.pidx[base + i];
+        mn = min(mn, u);
+        mx = max(mx, u);
       }
     }
+    range_publish(mn, mx, sm);
     __syncthreads();
-    select_candidates<C>(nc, kk, out, sm);
+    uint32_t lo, hi;
+    range_read<C>(sm, &lo, &hi);
+    select_candidates<C>(nc, kk, lo, hi, out, sm);
   } else {
     select_whole_row<C>(srow, n, vec, kk, out, sm);
   }
