@@ -116,7 +116,7 @@ struct RowSmem {
     uint32_t samp[2 * C::CAP];
   };
   uint32_t hist[C::BINS * C::NC];
-  uint32_t wsum[C::NT / 64];
+  uint32_t wsum[2 * (C::NT / 64)];  // two scan buffers, used alternately by loops of scans
   uint32_t wmin[C::NT / 64];
   uint32_t wmax[C::NT / 64];
   uint32_t sel[4];
@@ -126,14 +126,16 @@ template <class C>
 struct SampleSmem {
   uint32_t samp[C::NS_LONG];
   uint32_t hist[C::BINS * C::NC];
-  uint32_t wsum[C::NT / 64];
+  uint32_t wsum[2 * (C::NT / 64)];
   uint32_t wmin[C::NT / 64];
   uint32_t wmax[C::NT / 64];
   uint32_t sel[4];
 };
 
 // Exclusive block-wide scan of one value per thread; returns the exclusive
-// prefix and the total.  Two barriers.
+// prefix and the total.  One barrier: the C::NT / 64 words at wsum may be
+// written again only after another barrier (loops of scans alternate
+// between two buffers, so the next scan's own barrier is that barrier).
 template <class C>
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -147,9 +149,18 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint3
     pre += (w < wave) ? s : 0u;
     tot += s;
   }
-  __syncthreads();
   *total = tot;
   return pre + x - v;
+}
+
+// Clears the radix histogram (and the rank-list counter) ahead of a radix
+// select; the caller's next barrier publishes it.
+template <class C, class SM>
+__device__ __forceinline__ void hist_clear(SM& sm) {
+  constexpr int E = C::BINS * C::NC / C::NT;
+#pragma unroll
+  for (int e = 0; e < E; ++e) sm.hist[threadIdx.x * E + e] = 0u;
+  if (threadIdx.x == 0) sm.sel[2] = 0u;
 }
 
 // Block-wide min and max of one pair per thread (two barriers).
@@ -206,10 +217,15 @@ __device__ __forceinline__ void range_read(SM& sm, uint32_t* base, uint32_t* top
 // histogram bins are spread over the values actually present.  After the
 // first digit the keys of the selected bin are usually few: up to
 // C::RANKLIST of them are ranked directly in LDS instead of running the
-// remaining digit passes.
+// remaining digit passes.  With `cleared`, the caller has cleared the
+// histogram (hist_clear) before the barrier that published the keys.
+// Barriers: three per digit (histogram, scan, selected bin) plus one to
+// clear the histogram for every digit after the first; two for the rank
+// list.  No barrier follows the last LDS read, so the caller must pass one
+// before writing sm.hist or sm.sel[0], sm.sel[1] again.
 template <class C, class Visit, class SM>
 __device__ __forceinline__ void radix_select_in(uint32_t k, uint32_t base, uint32_t top, Visit visit, SM& sm,
-                                                uint32_t* T_out, uint32_t* krem_out) {
+                                                uint32_t* T_out, uint32_t* krem_out, bool cleared) {
   const int t = threadIdx.x;
   const uint32_t range = top - base;
   int s_hi = range == 0u ? 0 : 32 - __clz(range);  // every r = key - base is < 2^s_hi
@@ -218,10 +234,13 @@ __device__ __forceinline__ void radix_select_in(uint32_t k, uint32_t base, uint3
     const int s_lo = s_hi > C::DIGIT ? s_hi - C::DIGIT : 0;
     const uint32_t dmask = (1u << (s_hi - s_lo)) - 1u;
     constexpr int BPT = C::BINS / C::NT;  // bins per thread
-#pragma unroll
-    for (int e = 0; e < BPT * C::NC; ++e) sm.hist[t * (BPT * C::NC) + e] = 0u;
-    if (t == 0) sm.sel[2] = 0u;
-    __syncthreads();
+    if (!cleared) {
+      // the previous digit's histogram reads and rank-list counter use all
+      // ended before its scan barrier
+      hist_clear<C>(sm);
+      __syncthreads();
+    }
+    cleared = false;
     visit([&](uint32_t u) {
       const uint32_t r = u - base;
       if ((uint32_t)((uint64_t)r >> s_hi) == P) atomicAdd(&sm.hist[((r >> s_lo) & dmask) * C::NC + (t % C::NC)], 1u);
@@ -253,10 +272,12 @@ __device__ __forceinline__ void radix_select_in(uint32_t k, uint32_t base, uint3
       }
     }
     __syncthreads();
+    // no barrier after these reads: the next writes of sel[0], sel[1] and
+    // sel[3] come after further barriers, and sel[2] and the histogram (read
+    // before the scan's barrier) are other words
     P = sm.sel[0];
     krem = sm.sel[1];
     const uint32_t nbin = sm.sel[3];
-    __syncthreads();
     s_hi = s_lo;
     if (s_hi > 0 && nbin <= C::RANKLIST) {
       // the selected bin's keys into a list (hist reused), then rank them
@@ -281,7 +302,6 @@ __device__ __forceinline__ void radix_select_in(uint32_t k, uint32_t base, uint3
       __syncthreads();
       *T_out = sm.sel[0];
       *krem_out = sm.sel[1];
-      __syncthreads();
       return;
     }
   }
@@ -300,7 +320,7 @@ __device__ __forceinline__ void radix_select(uint32_t k, Visit visit, SM& sm, ui
   });
   uint32_t base, top;
   block_minmax<C>(lo, hi, sm, &base, &top);
-  radix_select_in<C>(k, base, top, visit, sm, T_out, krem_out);
+  radix_select_in<C>(k, base, top, visit, sm, T_out, krem_out, false);
 }
 
 // Threshold t0 from an NS-key sample of the row (n > C::CAP): keys >= t0
@@ -330,6 +350,7 @@ __device__ __forceinline__ uint32_t sample_threshold(const float* srow, int n, u
     mx = max(mx, u);
   }
   range_publish(mn, mx, sm);
+  hist_clear<C>(sm);
   __syncthreads();
   uint32_t base, top;
   range_read<C>(sm, &base, &top);
@@ -340,12 +361,13 @@ __device__ __forceinline__ uint32_t sample_threshold(const float* srow, int n, u
   radix_select_in<C>((uint32_t)q, base, top, [&](auto f) {
 #pragma unroll
     for (int e = 0; e < SPT; ++e) f(sm.samp[t + e * C::NT]);
-  }, sm, &T0, &r0);
+  }, sm, &T0, &r0, true);
   return T0;  // the q-th largest sample key: keys >= t0 include the top q of the sample
 }
 
 // Steps 2 and 3 over the nc candidates in sm.ckey / sm.cidx (index order),
-// whose keys lie in [base, top].
+// whose keys lie in [base, top]; the histogram was cleared before the
+// barrier that published the candidates.
 template <class C>
 __device__ __forceinline__ void select_candidates(uint32_t nc, uint32_t kk, uint32_t base, uint32_t top, int32_t* out,
                                                   RowSmem<C>& sm) {
@@ -357,7 +379,7 @@ __device__ __forceinline__ void select_candidates(uint32_t nc, uint32_t kk, uint
   uint32_t T, krem;
   radix_select_in<C>(kk, base, top, [&](auto f) {
     for (uint32_t c = c0; c < c1; ++c) f(sm.ckey[c]);
-  }, sm, &T, &krem);
+  }, sm, &T, &krem, true);
   uint32_t gt = 0, eq = 0;
   for (uint32_t c = c0; c < c1; ++c) {
     gt += sm.ckey[c] > T;
@@ -365,7 +387,8 @@ __device__ __forceinline__ void select_candidates(uint32_t nc, uint32_t kk, uint
   }
   // both counts in one scan: (greater << 16) | equal (at most C::CAP < 2^16 each)
   uint32_t tot;
-  const uint32_t pre = block_scan<C>((gt << 16) | eq, sm.wsum, &tot);
+  // (the radix select's last scan used buffer 0, with barriers since)
+  const uint32_t pre = block_scan<C>((gt << 16) | eq, sm.wsum + C::NT / 64, &tot);
   uint32_t gb = pre >> 16, eb = pre & 0xFFFFu;
   for (uint32_t c = c0; c < c1; ++c) {
     const uint32_t u = sm.ckey[c];
@@ -400,6 +423,7 @@ __device__ __forceinline__ void select_short_row(const float* srow, int n, uint3
       mx = max(mx, u);
     }
   range_publish(mn, mx, sm);
+  hist_clear<C>(sm);
   __syncthreads();
   uint32_t base, top;
   range_read<C>(sm, &base, &top);
@@ -456,7 +480,7 @@ __device__ __forceinline__ void select_whole_row(const float* srow, int n, bool 
     }
     // both counts in one scan (at most C::SEG < 2^16 each per segment)
     uint32_t tot;
-    const uint32_t pre = block_scan<C>((gt << 16) | eq, sm.wsum, &tot);
+    const uint32_t pre = block_scan<C>((gt << 16) | eq, sm.wsum + (sg & 1) * (C::NT / 64), &tot);
     uint32_t gb = g_base + (pre >> 16), eb = e_base + (pre & 0xFFFFu);
 #pragma unroll
     for (int e = 0; e < C::EPT; ++e) {
@@ -510,7 +534,7 @@ __global__ __launch_bounds__(C::NT) void topk_row_kernel(TopkArgs a) {
 #pragma unroll
     for (int e = 0; e < C::EPT; ++e) cnt += (j0 + e < n && keys[e] >= t0);
     uint32_t tot;
-    uint32_t off = nc + block_scan<C>(cnt, sm.wsum, &tot);
+    uint32_t off = nc + block_scan<C>(cnt, sm.wsum + (sg & 1) * (C::NT / 64), &tot);
 #pragma unroll
     for (int e = 0; e < C::EPT; ++e) {
       if (j0 + e < n && keys[e] >= t0) {
@@ -530,6 +554,7 @@ __global__ __launch_bounds__(C::NT) void topk_row_kernel(TopkArgs a) {
     }
   }
   range_publish(mn, mx, sm);
+  hist_clear<C>(sm);  // the threshold's radix select ended before the barrier after it
   __syncthreads();
   if (fits && nc >= kk) {
     uint32_t base, top;
@@ -566,7 +591,8 @@ __global__ __launch_bounds__(BigCfg::NT) void topk_part_kernel(TopkArgs a) {
   uint32_t* okey = a.pkey + slot * C::CAP;
   int32_t* oidx = a.pidx + slot * C::CAP;
   uint32_t nc = 0;
-  for (int j0 = p * a.part_len + 4 * t, jb = p * a.part_len; jb < pend; j0 += C::PART_LEN, jb += C::PART_LEN) {
+  for (int j0 = p * a.part_len + 4 * t, jb = p * a.part_len, ps = 0; jb < pend;
+       j0 += C::PART_LEN, jb += C::PART_LEN, ++ps) {
     uint32_t keys[4];
     if (vec && j0 + 4 <= pend) {
       const float4 x = j0 == jf ? first : *reinterpret_cast<const float4*>(srow + j0);
@@ -582,7 +608,7 @@ __global__ __launch_bounds__(BigCfg::NT) void topk_part_kernel(TopkArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) cnt += (j0 + e < pend && keys[e] >= t0);
     uint32_t tot;
-    uint32_t off = nc + block_scan<C>(cnt, sm.wsum, &tot);
+    uint32_t off = nc + block_scan<C>(cnt, sm.wsum + (ps & 1) * (C::NT / 64), &tot);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (j0 + e < pend && keys[e] >= t0) {
@@ -669,6 +695,7 @@ __global__ __launch_bounds__(BigCfg::NT) void topk_select_kernel(TopkArgs a) {
       }
     }
     range_publish(mn, mx, sm);
+    hist_clear<C>(sm);
     __syncthreads();
     uint32_t lo, hi;
     range_read<C>(sm, &lo, &hi);
