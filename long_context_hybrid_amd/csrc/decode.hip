@@ -816,9 +816,9 @@ DecodePlan plan_sparse_rows(const Geom& g, int k_top, int window) {
 }
 
 // Full-decode probability scratch: per unit (b, g), key-major rows of lgp
-// slots (the group's G heads, padded to 4, 8 or 16) of 2 bytes (bf16 inputs)
-// or 4, for kv_len rounded up to whole score chunks; and the running maxima,
-// lgp floats per 32-key step.
+// slots (the group's G heads, padded to 4, 8 or 16) of 3 bytes (bf16 inputs,
+// see ProbFmt) or 4, for kv_len rounded up to whole score chunks; and the
+// running maxima, lgp floats per 32-key step.
 static int prob_slots(const Geom& g) { return g.G <= 4 ? 4 : (g.G <= 8 ? 8 : 16); }
 static int64_t score_keys(const Geom& g) { return (int64_t)(g.Tkv + kScoreChunk - 1) / kScoreChunk * kScoreChunk; }
 static int64_t prob_unit_elems(const Geom& g) { return score_keys(g) * prob_slots(g); }
