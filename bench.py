@@ -4,14 +4,17 @@
 Default workload: decode at 128K context (B 4, Hq 64 / Hkv 4, D 128, bf16,
 K 2048, window 128, 9 sparse layers).  ``value`` is the sparse layer's decode
 tokens per second (batch / time of one sparse layer), measured cold: a 1 GiB
-write evicts the caches before each timed layer, and HIP events on the
-library's stream bracket the layer (its split and merge kernels).  The line
-also carries the same layer warm (layers back to back, rows partly served
-from the last-level cache), its per-kernel cold durations, the bandwidth a
-launch of the same size reaches with nothing else to do (a streaming read of
-the layer's bytes, a gather of its rows), the whole hybrid block (full layer
-+ top-K + all sparse layers: the K timed steps), and the 128K prefill full
-layer (both sweeps) against the bf16 MFMA peak.
+write evicts the caches before each timed layer, and the layer's time is the
+sum of its split and merge kernels' durations, each bracketed by HIP events
+that the library records on its launch stream.  The line also carries the
+same layer warm (layers back to back, rows partly served from the last-level
+cache), its per-kernel cold durations, the bandwidth a launch of the same
+size reaches with nothing else to do (a streaming read of the layer's bytes,
+a gather of its rows), the roofline of the step's dominant kernel (the full
+layer's split kernel) with a streaming read of the same K and V bytes beside
+it, the whole hybrid block (full layer + top-K + all sparse layers: the K
+timed steps), and the 128K prefill full layer (both sweeps) against the bf16
+MFMA peak.
 
 Inputs are resident in HBM before any timed region.  Per-kernel durations
 come from HIP events that the library records around each kernel on its
@@ -318,6 +321,30 @@ def decode_layer_measurements(args, wl, hy, torch, k, v, qs, gates, idx, sb_byte
                         "cold_frac_of_gather_ceiling": ga_r["us_median"] / cold_r["us_median"]}}
 
 
+def full_split_ceiling(hy, torch, k, v, dev, reps=5):
+    """What one launch that only streams the full decode layer's K and V
+    reaches on this GPU (the streaming-read ceiling kernel, non-temporal
+    16-byte loads, nothing computed; one launch for K, one for V): the
+    attainable rate beside the 8 TB/s peak for the full layer's split
+    kernel, which reads the same bytes."""
+    kflat, vflat = k.reshape(-1), v.reshape(-1)
+    nbytes = kflat.numel() * kflat.element_size()
+    cws = torch.empty(hy.hysparse_ceiling_workspace_bytes(nbytes, 0), dtype=torch.uint8, device=dev)
+
+    def run(r):
+        hy.hysparse_ceiling_stream_read(kflat, nbytes, workspace=cws)
+        hy.hysparse_ceiling_stream_read(vflat, nbytes, workspace=cws)
+
+    run(0)
+    per, _ = traced(hy, torch, run, reps)
+    pair_us = np.array(per["ceiling_stream"]).reshape(reps, 2).sum(axis=1)
+    us = float(np.median(pair_us))
+    gbs = 2 * nbytes / (us * 1e-6) / 1e9
+    return {"GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "us_median": us, "bytes": 2 * nbytes,
+            "what": "K and V of the cache read once as two contiguous streams (one launch each, non-temporal "
+                    "16-byte loads, nothing computed), kernel durations"}
+
+
 def prefill128k_full_layer(hy, torch, gen, dev, reps=2):
     """The 128K prefill full layer (both sweeps), inputs drawn on the GPU,
     against the bf16 MFMA peak."""
@@ -510,6 +537,10 @@ def main():
     if Tq == 1:
         sb = sparse_layer_bytes(wl, idx_np)
         rf = roof("full_decode_split", full_split_bytes(wl))
+        if rf:
+            c = full_split_ceiling(hy, torch, k, v, dev)
+            rf["ceiling"] = c
+            rf["frac_of_ceiling"] = rf["achieved"] / c["GB_per_s"]
         result["roofline"] = rf
         result["hybrid_block"] = {"tokens_per_s": block_tps, "ms_per_step": ms,
                                   "what": "full layer + top-K + all sparse layers, the timed steps"}
