@@ -198,7 +198,13 @@ def random_scores(seed: int, n_rows: int, row_len: int, kind: str = "probs") -> 
 
     ``kind``: "probs" - positive, softmax-like magnitudes with many near-ties;
     "ties"  - values from a set of 7 levels, so equal keys cross the K boundary;
-    "signed" - normal values of both signs, including -0.0 and +0.0.
+    "signed" - normal values of both signs, including -0.0 and +0.0;
+    "cluster" - a small background, a few large outliers at the start of the
+    row (indices 0..4) and a dense cluster of ``min(3000, row_len // 3)``
+    keys at random positions taking 64 adjacent float32 values just above
+    0.5 (many ties, and a key range so stretched by the outliers that the
+    cluster shares one bin of any coarse radix digit);
+    "cluster_wide" - the same with 16384 adjacent values (few ties).
     """
     rng = _rng(1000 + seed, 0)
     if kind == "probs":
@@ -210,6 +216,14 @@ def random_scores(seed: int, n_rows: int, row_len: int, kind: str = "probs") -> 
         z = rng.random((n_rows, row_len))
         x[z < 0.02] = 0.0
         x[(z >= 0.02) & (z < 0.04)] = -0.0
+    elif kind in ("cluster", "cluster_wide"):
+        x = rng.random((n_rows, row_len)) * 1e-3
+        c = min(3000, row_len // 3)
+        levels = 64 if kind == "cluster" else 16384
+        for r in range(n_rows):
+            pos = 5 + rng.choice(row_len - 5, size=c, replace=False)
+            x[r, pos] = 0.5 + rng.integers(0, levels, size=c) * 2.0 ** -24
+        x[:, :5] = np.array([1e4, 1e3, 1e2, 10.0, 2.0])[: min(5, row_len)]
     else:
         raise ValueError(kind)
     return x.astype(np.float32)

@@ -106,6 +106,28 @@ def test_topk_few_long_rows_in_parts(kind, k):
     np.testing.assert_array_equal(host(got), ref)
 
 
+@pytest.mark.parametrize("kind", ["cluster", "cluster_wide"])
+@pytest.mark.parametrize("R,L", [(8, 20000), (300, 10000), (300, 30000), (400, 3000), (400, 20000)])
+def test_topk_clustered_rows_multi_digit(kind, R, L):
+    """A dense cluster of near-tied keys, with outliers stretching the key
+    range, holds the K-th key, so the radix select's selected bin still has
+    more keys than the rank list takes after the first digit: later digit
+    passes run (their histogram cleared under their own barrier), ending in
+    the last digit ("cluster", 64 values) or in the rank list
+    ("cluster_wide").  Rows cover the part-and-select path (8 x 20000), the
+    large row workgroups with the whole row as candidates (300 x 10000) and
+    with the sampled filter (300 x 30000), and the small row workgroups
+    without (400 x 3000) and with (400 x 20000) the filter."""
+    c = min(3000, L // 3)
+    k = 5 + c // 2
+    say(f"topk {kind} R{R} L{L} k{k}")
+    S = gen.random_scores(77 + R + L, R, L, kind)
+    ref = orc.topk_rows(S, L, k)
+    got = hy.hysparse_topk(torch.from_numpy(S).cuda(), k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(got), ref)
+
+
 def test_topk_parts_strided_rows_and_fallback():
     """Parts with a row stride wider than the row, and a K above the sample's
     reach (the filter keeps too many candidates and the whole-row select
