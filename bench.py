@@ -390,7 +390,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU; multi-GPU runs are not part of it (use --gpus 1)",
+        print("bench.py: the library and this benchmark run on one GPU; --gpus above 1 is not supported (use --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
     import torch

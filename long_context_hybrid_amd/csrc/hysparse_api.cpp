@@ -113,7 +113,7 @@ hys_status check_ws(void* ws, size_t ws_bytes, size_t need) {
 
 hys_status from_hip(hipError_t e) {
   if (e == hipSuccess) return ok();
-  if (e == hipErrorNotSupported) return fail(HYS_ERR_UNSUPPORTED, "this path is not available in this build");
+  if (e == hipErrorNotSupported) return fail(HYS_ERR_UNSUPPORTED, "this path is not compiled into the library");
   return fail(HYS_ERR_HIP, std::string("HIP error: ") + hipGetErrorString(e));
 }
 
