@@ -21,7 +21,7 @@ from tests.gpu_util import assert_attn_close, check_hybrid, dev_tensor, say
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 96
 
 
 def random_workload(seed: int):
