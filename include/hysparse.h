@@ -124,7 +124,7 @@ hys_status hysparse_full_attn_scores(const hys_attn_desc* desc, const void* q, c
  *                fewer than 256 rows longer than 12288 keys: such rows are
  *                filtered in parts by several workgroups each, whose
  *                candidates go to the workspace (16 rows of 131072 keys:
- *                about 12.6 MB).  A NULL or smaller ws then returns
+ *                about 50 MB).  A NULL or smaller ws then returns
  *                HYS_ERR_WORKSPACE.
  * Results are bit-exact functions of the input bits (no atomics-order effects).
  */
