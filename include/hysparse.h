@@ -123,8 +123,9 @@ hys_status hysparse_full_attn_scores(const hys_attn_desc* desc, const void* q, c
  *                bytes.  That size is 0 (ws may be NULL) unless there are
  *                fewer than 256 rows longer than 12288 keys: such rows are
  *                filtered in parts by several workgroups each, whose
- *                candidates go to the workspace (16 rows of 131072 keys:
- *                about 50 MB).  A NULL or smaller ws then returns
+ *                candidates go to the workspace, a slot of min(part length,
+ *                12288) keys and indices per part (16 rows of 131072 keys:
+ *                32 parts of 4096, about 17 MB).  A NULL or smaller ws then returns
  *                HYS_ERR_WORKSPACE.
  * Results are bit-exact functions of the input bits (no atomics-order effects).
  */

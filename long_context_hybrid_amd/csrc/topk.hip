@@ -96,9 +96,11 @@ struct TopkArgs {
   int32_t k;
   int32_t* idx;
   // parallel filter (BigCfg): part p of row r keeps its survivors in
-  // pkey/pidx[(r * nparts + p) * CAP ...] and their number in pcnt[r * nparts + p]
+  // pkey/pidx[(r * nparts + p) * slot_cap ...] and their number in
+  // pcnt[r * nparts + p]
   int nparts;
   int part_len;  // multiple of PART_LEN
+  int slot_cap;  // min(CAP, part_len): a part never has more survivors than keys
   uint32_t* pkey;
   int32_t* pidx;
   uint32_t* pcnt;
@@ -588,8 +590,8 @@ __global__ __launch_bounds__(BigCfg::NT) void topk_part_kernel(TopkArgs a) {
   if (first_vec) first = *reinterpret_cast<const float4*>(srow + jf);
   const uint32_t t0 = sample_threshold<C, C::NS>(srow, n, kk, sm);
   const int64_t slot = row * a.nparts + p;
-  uint32_t* okey = a.pkey + slot * C::CAP;
-  int32_t* oidx = a.pidx + slot * C::CAP;
+  uint32_t* okey = a.pkey + slot * a.slot_cap;
+  int32_t* oidx = a.pidx + slot * a.slot_cap;
   uint32_t nc = 0;
   for (int j0 = p * a.part_len + 4 * t, jb = p * a.part_len, ps = 0; jb < pend;
        j0 += C::PART_LEN, jb += C::PART_LEN, ++ps) {
@@ -612,7 +614,7 @@ __global__ __launch_bounds__(BigCfg::NT) void topk_part_kernel(TopkArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (j0 + e < pend && keys[e] >= t0) {
-        if (off < (uint32_t)C::CAP) {
+        if (off < (uint32_t)a.slot_cap) {
           okey[off] = keys[e];
           oidx[off] = j0 + e;
         }
@@ -620,7 +622,7 @@ __global__ __launch_bounds__(BigCfg::NT) void topk_part_kernel(TopkArgs a) {
       }
     }
     nc += tot;
-    if (nc > (uint32_t)C::CAP) break;  // the row will fall back to the whole-row select
+    if (nc > (uint32_t)a.slot_cap) break;  // the row will fall back to the whole-row select
   }
   if (t == 0) a.pcnt[slot] = nc;
 }
@@ -650,20 +652,20 @@ __global__ __launch_bounds__(BigCfg::NT) void topk_select_kernel(TopkArgs a) {
   // to the part's workspace slot), so both round trips overlap
   const int tpp = C::NT / a.nparts;
   const int pp = t / tpp, r = t - pp * tpp;
-  const int64_t base = (row * a.nparts + (pp < a.nparts ? pp : 0)) * C::CAP;
+  const int64_t base = (row * a.nparts + (pp < a.nparts ? pp : 0)) * a.slot_cap;
   constexpr int kU = 8;
   uint32_t kv[kU];
   int32_t iv[kU];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
-    const int i = min(r + u * tpp, C::CAP - 1);
+    const int i = min(r + u * tpp, a.slot_cap - 1);
     kv[u] = a.pkey[base + i];
     iv[u] = a.pidx[base + i];
   }
   if (t < 64) {  // one lane per part (nparts <= 64): counts, then an exclusive scan
     const uint32_t c = t < a.nparts ? a.pcnt[row * a.nparts + t] : 0u;
     const uint32_t x = wave_inclusive_scan(c);
-    const bool ok = __builtin_amdgcn_ballot_w64(c > (uint32_t)C::CAP) == 0;
+    const bool ok = __builtin_amdgcn_ballot_w64(c > (uint32_t)a.slot_cap) == 0;
     if (t < a.nparts) pstart[t] = x - c;
     if (t == 63) pstart[a.nparts] = ok ? x : 0xFFFFFFFFu;
   }
@@ -714,6 +716,13 @@ int topk_parts(int64_t n_rows, int32_t row_len) {
   return np < 2 ? 1 : np;
 }
 
+int topk_part_len(int32_t row_len, int np);
+// survivors one part's workspace slot holds
+int topk_slot_cap(int32_t row_len, int np) {
+  const int pl = topk_part_len(row_len, np);
+  return pl < BigCfg::CAP ? pl : BigCfg::CAP;
+}
+
 int topk_part_len(int32_t row_len, int np) {
   const int per = (row_len + np - 1) / np;
   return (per + BigCfg::PART_LEN - 1) / BigCfg::PART_LEN * BigCfg::PART_LEN;
@@ -728,7 +737,8 @@ size_t topk_ws_bytes(int64_t n_rows, int32_t row_len, int32_t /*k*/) {
   const int np = topk_parts(n_rows, row_len);
   if (np == 1) return 0;
   const size_t slots = (size_t)n_rows * np;
-  return align_up(slots * BigCfg::CAP * sizeof(uint32_t)) * 2 + align_up(slots * sizeof(uint32_t));
+  const size_t cap = (size_t)topk_slot_cap(row_len, np);
+  return align_up(slots * cap * sizeof(uint32_t)) * 2 + align_up(slots * sizeof(uint32_t));
 }
 
 hipError_t launch_topk(const float* scores, int64_t n_rows, int32_t row_len, int64_t row_stride,
@@ -749,13 +759,14 @@ hipError_t launch_topk(const float* scores, int64_t n_rows, int32_t row_len, int
     return launch("topk", topk_row_kernel<BigCfg>, dim3((unsigned)n_rows), dim3(BigCfg::NT), 0, st, a);
   }
   const size_t slots = (size_t)n_rows * a.nparts;
+  a.part_len = topk_part_len(row_len, a.nparts);
+  a.slot_cap = topk_slot_cap(row_len, a.nparts);
   unsigned char* c = static_cast<unsigned char*>(ws);
   a.pkey = reinterpret_cast<uint32_t*>(c);
-  c += align_up(slots * BigCfg::CAP * sizeof(uint32_t));
+  c += align_up(slots * a.slot_cap * sizeof(uint32_t));
   a.pidx = reinterpret_cast<int32_t*>(c);
-  c += align_up(slots * BigCfg::CAP * sizeof(uint32_t));
+  c += align_up(slots * a.slot_cap * sizeof(uint32_t));
   a.pcnt = reinterpret_cast<uint32_t*>(c);
-  a.part_len = topk_part_len(row_len, a.nparts);
   hipError_t e = launch("topk_part", topk_part_kernel, dim3((unsigned)slots), dim3(BigCfg::NT), 0, st, a);
   if (e != hipSuccess) return e;
   return launch("topk_select", topk_select_kernel, dim3((unsigned)n_rows), dim3(BigCfg::NT), 0, st, a);

@@ -95,8 +95,11 @@ def test_topk_validation():
     assert L.hysparse_topk(FAKE, 4, 100, 102, None, 8, FAKE, FAKE, 1 << 30, None) == 4   # stride % 4
     assert L.hysparse_topk(None, 4, 100, 100, None, 8, FAKE, FAKE, 1 << 30, None) == 1
     assert L.hysparse_topk(FAKE, 0, 100, 100, None, 8, FAKE, None, 0, None) == 0        # empty: no-op
-    # few long rows: the candidate filter runs in parts and needs a workspace
-    assert L.hysparse_topk_workspace_bytes(16, 131072, 2048) >= 16 * 32 * 12288 * 8
+    # few long rows: the candidate filter runs in parts and needs a workspace,
+    # a slot per part of min(part length, 12288) keys and indices
+    assert L.hysparse_topk_workspace_bytes(16, 131072, 2048) >= 16 * 32 * 4096 * 8          # 32 parts of 4096
+    assert L.hysparse_topk_workspace_bytes(16, 131072, 2048) < 16 * 32 * 12288 * 8
+    assert L.hysparse_topk_workspace_bytes(255, 131072, 2048) >= 255 * 3 * 12288 * 8        # 3 parts of 45056
     assert L.hysparse_topk_workspace_bytes(4096, 32768, 2048) == 0                        # one workgroup per row
     assert L.hysparse_topk_workspace_bytes(16, 12288, 2048) == 0                          # rows fit the LDS
     assert L.hysparse_topk_workspace_bytes(-1, 131072, 2048) == 0
