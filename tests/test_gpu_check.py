@@ -70,3 +70,18 @@ def test_check_indices_on_hybrid_block_indices():
     st = host(hy.hysparse_check_indices(res["idx"], wl.kv_len))
     torch.cuda.synchronize()
     assert (st == 0).all()
+
+
+def test_check_indices_at_the_maximum_row_length():
+    """Rows of the largest supported length (a 64 KiB LDS bitmap), with entries
+    at both ends of the row and a duplicate of the last position."""
+    L, K = 524288, 64
+    rng = np.random.default_rng(9)
+    rows = np.stack([np.sort(rng.choice(L, size=K, replace=False)) for _ in range(3)]).astype(np.int32)
+    rows[0, 0], rows[0, -1] = 0, L - 1
+    rows[1, -2], rows[1, -1] = L - 1, L - 1   # duplicate of the last position
+    got = host(hy.hysparse_check_indices(torch.from_numpy(rows).cuda(), L))
+    torch.cuda.synchronize()
+    want = np.array([expected_status(rows[r], L, L) for r in range(3)])
+    np.testing.assert_array_equal(got, want)
+    assert want[0] == 0 and want[1] & hy.HYS_IDX_DUPLICATE
