@@ -106,6 +106,20 @@ def test_topk_few_long_rows_in_parts(kind, k):
     np.testing.assert_array_equal(host(got), ref)
 
 
+@pytest.mark.parametrize("R,L,k", [(3, 40000, 15000), (16, 131072, 13000), (2, 20000, 19999), (2, 13000, 13000)])
+def test_topk_k_above_the_candidate_capacity(R, L, k):
+    """K above the 12,288 candidates a row workgroup holds: the filtered
+    candidates cannot hold the top K, so every path (one workgroup per row,
+    and the part filter with its select) selects over the whole row; K one
+    below and equal to the row length."""
+    say(f"topk R{R} L{L} k{k}")
+    S = gen.random_scores(61 + k, R, L, "probs")
+    ref = orc.topk_rows(S, L, k)
+    got = hy.hysparse_topk(torch.from_numpy(S).cuda(), k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(got), ref)
+
+
 @pytest.mark.parametrize("kind", ["cluster", "cluster_wide"])
 @pytest.mark.parametrize("R,L", [(8, 20000), (300, 10000), (300, 30000), (400, 3000), (400, 20000)])
 def test_topk_clustered_rows_multi_digit(kind, R, L):
