@@ -42,6 +42,9 @@ DECODE_CASES = {
     # splits so that the split workgroups fit one resident round (3 splits of
     # 384 entries here), with a K that is not a multiple of the split
     "capped_splits_128_units": W["decode128k"].replace(batch=32, kv_len=3000, k_top=777, n_sparse=1, n_planted=4),
+    # one query with score block 64: a block of one query (NB 1, last(0) = the
+    # query's own position), the same rows as score block 1
+    "one_query_block64": W["decode8k"].replace(batch=2, kv_len=900, k_top=100, n_sparse=1, score_block=64),
     # fp32 with head_dim 128 (no other case covers this instantiation)
     "f32_d128_g4": W["tiny"].replace(batch=2, q_len=1, kv_len=1300, n_q_heads=8, n_kv_heads=2, head_dim=128,
                                      std=1.0 / np.sqrt(128.0), k_top=200, window=64, n_sparse=2),
